@@ -1,0 +1,186 @@
+/*
+ * pagedattn.h — C ABI of the gfx950 paged decode-attention library.
+ *
+ * What it computes.  Single-token decode attention over a paged KV cache
+ * (PagedAttention).  For every sequence b and query head h, with
+ * L = seq_lens[b] and KV head g = h / (num_q_heads / num_kv_heads):
+ *
+ *     s_t   = scale * <q[b][h], K_b[t]>                  t = 0 .. L-1
+ *     w_t   = exp(s_t - max_u s_u) / sum_u exp(s_u - max_u s_u)
+ *     out[b][h] = sum_t w_t * V_b[t]
+ *
+ * where K_b[t] / V_b[t] is the key / value row of logical token t, found by
+ * following the block table: physical block block_tables[b][t / B], slot
+ * t % B, KV head g.  This is ordinary exact attention with only the
+ * addressing changed ("39 · PagedAttention", §1 "What attention needs",
+ * §2 "The paged version" and the IMPORTANT box; the softmax(QK^T/sqrt(d))V
+ * definition is in "FlashAttention vs PagedAttention", section "What does
+ * FlashAttention optimize?").  Query heads are grouped onto KV heads
+ * consecutively (grouped-query attention, "PagedAttention: The Cache Was
+ * Storing Nothing", §3.1 "Sharing the keys and values"; the pages fix no
+ * index convention, this library fixes g = h / G).
+ *
+ * Device memory layouts (row-major, dense, element = one value of `dtype`):
+ *
+ *   q            [num_seqs][num_q_heads][head_dim]              dtype
+ *   out          [num_seqs][num_q_heads][head_dim]              out_dtype
+ *   k_pool       [num_blocks][num_kv_heads][block_size][head_dim]   token-major
+ *   v_pool       [num_blocks][num_kv_heads][head_dim][block_size]   dim-major
+ *   block_tables int32 [num_seqs][max_blocks_per_seq]
+ *   seq_lens     int32 [num_seqs]
+ *
+ * One (physical block, KV head) tile of either pool is one contiguous
+ * block_size*head_dim*esize-byte range (4 KiB for bf16/fp16 with 16-token
+ * blocks), so a block is read as a single coalesced burst.  K is stored
+ * token-major (a token's key row is contiguous, the reduction axis of q.k);
+ * V is stored dim-major inside the tile (the block's tokens for one value
+ * dimension are contiguous, the reduction axis of w.V).  Both choices put
+ * each product's reduction axis innermost, which is the operand layout the
+ * gfx950 matrix cores consume directly.
+ *
+ * Table semantics.  Sequence b has n_b = ceil(L / block_size) logical
+ * blocks; entries j >= n_b of its table row are never read (they may hold
+ * -1).  Slots of the last block at or beyond L - (n_b-1)*block_size are
+ * never part of the result, whatever they hold.  Physical blocks may be
+ * shared by several sequences (prefix sharing: "PagedAttention: The Cache
+ * Was Storing Nothing", §2.3).  L = 0 gives out = 0.
+ *
+ * Ownership and threading.  The caller allocates every buffer (including
+ * the workspace) and owns the stream.  The library allocates nothing, keeps
+ * no pointer after a call returns and holds no state between calls.  Calls
+ * are asynchronous on `stream` (a hipStream_t; NULL = the null stream).
+ * Calls that share a workspace must be ordered on one stream.  `out` must
+ * not alias any input.
+ *
+ * Errors.  Every function that can fail returns a pa_status; no exception
+ * crosses the ABI.  Descriptor and pointer errors are detected on the host
+ * before anything is launched.  Data-dependent preconditions (every used
+ * table id in [0, num_blocks), 0 <= seq_lens[b] <= max_blocks_per_seq *
+ * block_size) are NOT checked on the device; pa_validate_host checks them
+ * on host copies.  A launch failure returns PA_ERR_LAUNCH.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,       /* a size is <= 0, or num_q_heads % num_kv_heads != 0 */
+  PA_ERR_DTYPE = 3,       /* unknown dtype, or out_dtype neither PA_F32 nor dtype */
+  PA_ERR_UNSUPPORTED = 4, /* valid but not built: head_dim, block_size, group size, kernel/dtype pair */
+  PA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than pa_workspace_bytes() */
+  PA_ERR_ALIGN = 6,       /* q, pools or out not 16-byte aligned */
+  PA_ERR_LAUNCH = 7,      /* the HIP launch reported an error */
+  PA_ERR_TABLE = 8,       /* pa_validate_host: table id out of range or bad seq_len */
+  PA_ERR_DEVICE = 9       /* device query failed or the device is not gfx950 */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0,
+  PA_F16 = 1, /* IEEE binary16 */
+  PA_BF16 = 2 /* bfloat16: the upper 16 bits of an IEEE binary32 */
+} pa_dtype;
+
+/* Which decode kernel runs.  AUTO picks the matrix-core kernel for fp16/bf16
+ * and the vector-ALU kernel for fp32.  Forcing a kernel is for tests and
+ * measurement; MFMA with PA_F32 returns PA_ERR_UNSUPPORTED. */
+typedef enum pa_kernel {
+  PA_KERNEL_AUTO = 0,
+  PA_KERNEL_VALU = 1, /* vector ALU, DPP row reductions; any dtype */
+  PA_KERNEL_MFMA = 2  /* gfx950 matrix cores for the query-group products */
+} pa_kernel;
+
+typedef struct pa_desc {
+  int32_t num_seqs;           /* >= 1 */
+  int32_t num_q_heads;        /* Hq, multiple of num_kv_heads */
+  int32_t num_kv_heads;       /* Hkv >= 1; group size G = Hq / Hkv in {1, 2, 4, 8, 16} */
+  int32_t head_dim;           /* D; built: 128 */
+  int32_t block_size;         /* B tokens per block; built: 16, 32 */
+  int32_t num_blocks;         /* physical blocks in each pool */
+  int32_t max_blocks_per_seq; /* row stride of block_tables */
+  int32_t dtype;              /* pa_dtype of q, k_pool, v_pool */
+  int32_t out_dtype;          /* PA_F32, or equal to dtype (round to nearest even) */
+  int32_t kernel;             /* pa_kernel */
+} pa_desc;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* pa_status_str(int32_t status);
+
+/* Bytes of one element of `dtype`, 0 if unknown. */
+size_t pa_dtype_size(int32_t dtype);
+
+/* Logical blocks a sequence of `len` tokens occupies: ceil(len / block_size),
+ * 0 when len <= 0 or block_size <= 0.  The last block holds
+ * len - (n-1)*block_size tokens ("FlashAttention vs PagedAttention", the
+ * sizing example's block rounding). */
+int64_t pa_blocks_for_len(int64_t len, int32_t block_size);
+
+/* Bytes of ONE pool (k_pool and v_pool have the same size):
+ * num_blocks * num_kv_heads * block_size * head_dim * esize. 0 on a bad desc. */
+size_t pa_pool_bytes(const pa_desc* desc);
+
+/* Element offset of K[block][kv_head][slot][dim] inside k_pool, and of the
+ * same logical element of V inside v_pool.  -1 if an index is out of range
+ * or the descriptor is invalid. */
+int64_t pa_k_elem_offset(const pa_desc* desc, int32_t block, int32_t kv_head,
+                         int32_t slot, int32_t dim);
+int64_t pa_v_elem_offset(const pa_desc* desc, int32_t block, int32_t kv_head,
+                         int32_t slot, int32_t dim);
+
+/* Bytes of device workspace that paged_attn_decode needs for this
+ * descriptor (holds the partition partials of split sequences); 0 on a bad
+ * descriptor.  The content needs no initialisation. */
+size_t pa_workspace_bytes(const pa_desc* desc);
+
+/* Checks the descriptor, then the data-dependent preconditions on HOST
+ * copies of the block table and lengths: 0 <= seq_lens[b] <=
+ * max_blocks_per_seq*block_size and block_tables[b][j] in [0, num_blocks)
+ * for every j < n_b.  PA_OK, a descriptor error, or PA_ERR_TABLE. */
+int32_t pa_validate_host(const pa_desc* desc, const int32_t* block_tables_host,
+                         const int32_t* seq_lens_host);
+
+/* Checks a descriptor alone (what every launching entry point checks). */
+int32_t pa_check_desc(const pa_desc* desc);
+
+/* Paged decode attention, whole operation: the decode kernel then, on the
+ * same stream, the partition-merge kernel.  All pointers are device
+ * pointers in the layouts above; `scale` multiplies q.k (1/sqrt(head_dim)
+ * for standard attention).  workspace: device buffer of at least
+ * pa_workspace_bytes(desc) bytes. */
+int32_t paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_tables, const int32_t* seq_lens,
+                          float scale, void* out, const pa_desc* desc,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two launches of paged_attn_decode, exposed separately so that each
+ * kernel can be timed on its own.  pa_decode_partitions walks the block
+ * tables, writes `out` for sequences processed whole by one workgroup and
+ * (max, sum-of-exp, weighted-V) partials for the rest into the workspace;
+ * pa_merge_partitions folds those partials with
+ *   m = max(m1, m2),  l = l1*e^(m1-m) + l2*e^(m2-m),  o = o1*e^(m1-m) + o2*e^(m2-m)
+ * ("39 · PagedAttention", §3 "On the GPU", merge equation) and writes
+ * out = o / l.  Calling pa_decode_partitions then pa_merge_partitions with
+ * the same arguments on one stream equals paged_attn_decode. */
+int32_t pa_decode_partitions(const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* block_tables, const int32_t* seq_lens,
+                             float scale, void* out, const pa_desc* desc,
+                             void* workspace, size_t workspace_bytes, void* stream);
+int32_t pa_merge_partitions(const int32_t* seq_lens, void* out, const pa_desc* desc,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Number of decode workgroups a launch uses for this descriptor on the
+ * current device (the split-K granularity), or -1 on error. */
+int32_t pa_decode_grid(const pa_desc* desc);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,446 @@
+"""Pins that tie the fp64 oracle to the pages and to mathematics.
+
+Each pin takes a loaded oracle build (oracle.Oracle) and raises
+AssertionError when that build disagrees with something fixed outside the
+oracle: a worked example on the pages, a closed form, an invariant of
+exact attention, a library routine (torch / numpy), or an independent
+brute-force evaluation written here.  test_oracle.py runs every pin on the
+real build; test_oracle_mutants.py runs them on builds with planted
+mistakes and requires each mistake to be caught by at least one pin.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- helpers
+# Written independently of the oracle: numpy fancy indexing instead of the
+# oracle's per-token loops.
+
+def scatter(Klog, Vlog, tables, lens, num_blocks, B, fill=np.nan):
+    """Place logical fp64 K/V [S][Hkv][Lmax][D] into pools of the library
+    layout: K [NB][Hkv][B][D], V [NB][Hkv][D][B]; untouched slots = fill."""
+    S, H, _, D = Klog.shape
+    kp = np.full((num_blocks, H, B, D), fill)
+    vp = np.full((num_blocks, H, D, B), fill)
+    for b in range(S):
+        t = np.arange(int(lens[b]))
+        phys = np.asarray(tables[b])[t // B]
+        slot = t % B
+        for g in range(H):
+            kp[phys, g, slot, :] = Klog[b, g, : t.size]
+            vp[phys, g, :, slot] = Vlog[b, g, : t.size]
+    return kp, vp
+
+
+def random_tables(rng, lens, B, num_blocks, max_blocks):
+    ids = rng.permutation(num_blocks)
+    bt = np.full((len(lens), max_blocks), -1, np.int32)
+    k = 0
+    for b, L in enumerate(lens):
+        n = -(-int(L) // B)
+        bt[b, :n] = ids[k: k + n]
+        k += n
+    return bt
+
+
+def numpy_reference(q, kp, vp, bt, lens, scale, Hkv, B):
+    """Second, independent evaluation of the formula (fp64 numpy)."""
+    S, Hq, D = q.shape
+    G = Hq // Hkv
+    out = np.zeros((S, Hq, D))
+    for b in range(S):
+        L = int(lens[b])
+        if L == 0:
+            continue
+        t = np.arange(L)
+        phys, slot = bt[b, t // B], t % B
+        for h in range(Hq):
+            K = kp[phys, h // G, slot, :]
+            V = vp[phys, h // G, :, slot]
+            s = scale * (K @ q[b, h])
+            w = np.exp(s - s.max())
+            out[b, h] = (w / w.sum()) @ V
+    return out
+
+
+def sdpa(q, K, V, scale):
+    """torch's scaled_dot_product_attention on CPU in fp64, one query."""
+    qt = torch.from_numpy(np.asarray(q, np.float64)).reshape(1, 1, 1, -1)
+    Kt = torch.from_numpy(np.asarray(K, np.float64))[None, None]
+    Vt = torch.from_numpy(np.asarray(V, np.float64))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, scale=scale)[0, 0, 0].numpy()
+
+
+def decode_f64(O, q, kp, vp, bt, lens, scale, Hkv, B):
+    """Oracle on fp64 data stored as float32 (values chosen exactly
+    representable in float32 by the callers)."""
+    return O.paged_decode(np.asarray(q, np.float32), np.asarray(kp, np.float32),
+                          np.asarray(vp, np.float32), bt, np.asarray(lens, np.int32), scale,
+                          num_kv_heads=Hkv, block_size=B, dtype="f32")
+
+
+def f32_normal(rng, shape, grid=None):
+    """N(0,1) draws; with grid, rounded to multiples of 2**-grid."""
+    x = rng.standard_normal(shape)
+    if grid is not None:
+        x = np.round(x * 2.0 ** grid) / 2.0 ** grid
+    return x.astype(np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------------ conversions
+
+def pin_f16_decode_all_patterns(O):
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = O.to_f64(bits, "f16")
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def pin_bf16_decode_all_patterns(O):
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = O.to_f64(bits, "bf16")
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def pin_dtype_paths_agree(O):
+    """f16 / bf16 storage gives the same result as f32 storage of the same
+    (exactly representable) values."""
+    rng = np.random.default_rng(11)
+    S, Hq, Hkv, D, B = 3, 4, 2, 16, 4
+    lens = [7, 1, 12]
+    NB = 12
+    bt = random_tables(rng, lens, B, NB, 4)
+    Kl = rng.standard_normal((S, Hkv, 12, D))
+    Vl = rng.standard_normal((S, Hkv, 12, D))
+    q = rng.standard_normal((S, Hq, D))
+    for dt, npdt in (("f16", np.float16), ("bf16", None)):
+        def rnd(x):
+            if npdt is not None:
+                return x.astype(npdt)
+            return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+        def bits(x):
+            r = rnd(x)
+            return r if npdt is not None else r.view(torch.int16).numpy().view(np.uint16)
+        def wide(x):
+            r = rnd(x)
+            return r.astype(np.float64) if npdt is not None else r.double().numpy()
+        kp, vp = scatter(wide(Kl), wide(Vl), bt, lens, NB, B, fill=0.0)
+        a = O.paged_decode(bits(q), bits(kp), bits(vp), bt, np.array(lens, np.int32), 0.25,
+                           num_kv_heads=Hkv, block_size=B, dtype=dt)
+        c = decode_f64(O, wide(q), kp, vp, bt, lens, 0.25, Hkv, B)
+        assert np.array_equal(a, c), dt
+
+
+# ------------------------------------------------ the pages' worked example
+
+def pin_worked_example_walk(O):
+    """Gather follows the block table exactly as the worked example walks it."""
+    fx = _golden("worked_example_60tok.json")
+    B, L, table = fx["block_size"], fx["num_tokens"], fx["block_table"]
+    NB, D = 16, 2
+    kp = np.full((NB, 1, B, D), np.nan, np.float32)
+    vp = np.full((NB, 1, D, B), np.nan, np.float32)
+    for p in range(NB):
+        for s in range(B):
+            kp[p, 0, s] = [p, s]          # K row encodes (physical block, slot)
+            vp[p, 0, :, s] = [-p, -s]
+    bt = np.array([table], np.int32)
+    K, V = O.gather(kp, vp, bt, 0, 0, L, num_kv_heads=1, head_dim=D, block_size=B, dtype="f32")
+    t = 0
+    for step in fx["walk"]:
+        for s in range(step["tokens"]):
+            assert K[t, 0] == step["physical"] and K[t, 1] == s, (t, K[t])
+            assert V[t, 0] == -step["physical"] and V[t, 1] == -s, (t, V[t])
+            t += 1
+    assert t == L == K.shape[0]
+
+
+def pin_worked_example_paged_equals_contiguous(O):
+    """Paged result == contiguous attention on the same logical K/V
+    (bitwise, same summation order) and == torch SDPA (1e-12)."""
+    fx = _golden("worked_example_60tok.json")
+    B, L, table = fx["block_size"], fx["num_tokens"], fx["block_table"]
+    rng = np.random.default_rng(60)
+    D, NB = 128, 16
+    Kl = f32_normal(rng, (1, 1, L, D))
+    Vl = f32_normal(rng, (1, 1, L, D))
+    q = f32_normal(rng, (1, 1, D))
+    scale = float(np.float32(1 / math.sqrt(D)))
+    kp, vp = scatter(Kl, Vl, [table], [L], NB, B)
+    bt = np.array([table], np.int32)
+    paged = decode_f64(O, q, kp, vp, bt, [L], scale, 1, B)[0, 0]
+    contig = O.attention(q[0, 0], Kl[0, 0], Vl[0, 0], scale)
+    assert np.array_equal(paged, contig)
+    assert np.max(np.abs(paged - sdpa(q[0, 0], Kl[0, 0], Vl[0, 0], scale))) < 1e-12
+    assert np.all(np.isfinite(paged))  # NaN in slots 12..15 of block 4 and unused blocks
+
+
+# ------------------------------------------------------------ closed forms
+
+def pin_single_token_returns_value_row(O):
+    rng = np.random.default_rng(1)
+    D, B, NB = 8, 4, 5
+    Kl = f32_normal(rng, (1, 1, 1, D))
+    Vl = f32_normal(rng, (1, 1, 1, D))
+    q = f32_normal(rng, (1, 1, D))
+    kp, vp = scatter(Kl, Vl, [[3]], [1], NB, B)
+    out = decode_f64(O, q, kp, vp, np.array([[3]], np.int32), [1], 0.7, 1, B)
+    assert np.array_equal(out[0, 0], Vl[0, 0, 0])
+
+
+def pin_zero_query_gives_mean_of_exactly_L_values(O):
+    """q = 0 -> every score 0 -> weights 1/L: the mean over exactly the
+    attended tokens (a slack slot of the partial last block would shift it;
+    here the slack holds NaN)."""
+    rng = np.random.default_rng(2)
+    D, B, NB, L = 16, 16, 9, 37
+    bt = random_tables(rng, [L], B, NB, 3)
+    Kl = f32_normal(rng, (1, 1, L, D))
+    Vl = f32_normal(rng, (1, 1, L, D), grid=8)
+    kp, vp = scatter(Kl, Vl, bt, [L], NB, B)
+    out = decode_f64(O, np.zeros((1, 1, D)), kp, vp, bt, [L], 0.3, 1, B)[0, 0]
+    assert np.max(np.abs(out - Vl[0, 0].mean(axis=0))) < 1e-13
+
+
+def pin_dominant_score_selects_value_row(O):
+    rng = np.random.default_rng(3)
+    D, B, NB, L = 8, 4, 6, 19
+    bt = random_tables(rng, [L], B, NB, 5)
+    Kl = f32_normal(rng, (1, 1, L, D))
+    Vl = f32_normal(rng, (1, 1, L, D))
+    q = f32_normal(rng, (1, 1, D))
+    s = Kl[0, 0] @ q[0, 0]
+    kp, vp = scatter(Kl, Vl, bt, [L], NB, B)
+    out = decode_f64(O, q, kp, vp, bt, [L], 1e6, 1, B)[0, 0]
+    assert np.max(np.abs(out - Vl[0, 0, int(np.argmax(s))])) < 1e-12
+
+
+def pin_two_tokens_by_hand(O):
+    """D = 1, L = 2: out = (v0 e^s0 + v1 e^s1) / (e^s0 + e^s1), s_i = c q k_i."""
+    q, k0, k1, v0, v1, c = 1.5, 0.25, -2.0, 3.0, -1.0, 0.5
+    s0, s1 = c * q * k0, c * q * k1
+    want = (v0 * math.exp(s0) + v1 * math.exp(s1)) / (math.exp(s0) + math.exp(s1))
+    kp = np.full((3, 1, 2, 1), np.nan)
+    vp = np.full((3, 1, 1, 2), np.nan)
+    kp[2, 0, 0, 0], kp[2, 0, 1, 0] = k0, k1
+    vp[2, 0, 0, 0], vp[2, 0, 0, 1] = v0, v1
+    out = decode_f64(O, [[[q]]], kp, vp, np.array([[2]], np.int32), [2], c, 1, 2)
+    assert abs(out[0, 0, 0] - want) < 1e-15
+
+
+def pin_empty_sequence_is_zero(O):
+    kp = np.full((2, 1, 4, 3), np.nan)
+    vp = np.full((2, 1, 3, 4), np.nan)
+    out = decode_f64(O, np.ones((1, 1, 3)), kp, vp, np.array([[-1]], np.int32), [0], 1.0, 1, 4)
+    assert np.array_equal(out, np.zeros((1, 1, 3)))
+
+
+def pin_table_out_of_range_is_an_error(O):
+    kp = np.zeros((2, 1, 4, 3))
+    vp = np.zeros((2, 1, 3, 4))
+    try:
+        decode_f64(O, np.ones((1, 1, 3)), kp, vp, np.array([[2]], np.int32), [3], 1.0, 1, 4)
+    except ValueError:
+        return
+    raise AssertionError("out-of-range table entry accepted")
+
+
+# ------------------------------------------------------------- invariants
+
+def _case(seed, S=3, Hq=4, Hkv=2, D=16, B=4, lens=(9, 16, 3), grid=None):
+    rng = np.random.default_rng(seed)
+    Lmax = max(lens)
+    Kl = f32_normal(rng, (S, Hkv, Lmax, D), grid)
+    Vl = f32_normal(rng, (S, Hkv, Lmax, D), grid)
+    q = f32_normal(rng, (S, Hq, D), grid)
+    return rng, Kl, Vl, q, list(lens)
+
+
+def pin_block_permutation_invariance(O):
+    rng, Kl, Vl, q, lens = _case(4)
+    B, NB = 4, 14
+    outs = []
+    for _ in range(3):
+        bt = random_tables(rng, lens, B, NB, 4)
+        kp, vp = scatter(Kl, Vl, bt, lens, NB, B)
+        outs.append(decode_f64(O, q, kp, vp, bt, lens, 0.25, 2, B))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def pin_block_size_invariance(O):
+    rng, Kl, Vl, q, lens = _case(5, lens=(13, 32, 5))
+    ref = None
+    for B in (1, 2, 16, 32, 13):
+        nbl = [-(-L // B) for L in lens]
+        NB = sum(nbl) + 3
+        bt = random_tables(rng, lens, B, NB, max(nbl))
+        kp, vp = scatter(Kl, Vl, bt, lens, NB, B)
+        out = decode_f64(O, q, kp, vp, bt, lens, 0.25, 2, B)
+        if ref is None:
+            ref = out
+        assert np.array_equal(out, ref), B
+
+
+def pin_key_shift_invariance(O):
+    """Adding the same vector u to every key shifts every score by
+    scale * q.u = 800 and must not change the output; e^800 overflows fp64,
+    so skipping the max subtraction fails here."""
+    rng = np.random.default_rng(6)
+    D, B, NB, L = 8, 4, 7, 21
+    bt = random_tables(rng, [L], B, NB, 6)
+    Kl = f32_normal(rng, (1, 1, L, D), grid=10)
+    Vl = f32_normal(rng, (1, 1, L, D))
+    q = np.zeros((1, 1, D))
+    q[0, 0, 3] = 2.0
+    scale = 0.125
+    Ks = Kl.copy()
+    Ks[..., 3] += 800.0 / (scale * 2.0)  # exact in float32 on the 2**-10 grid
+    kp, vp = scatter(Kl, Vl, bt, [L], NB, B)
+    kps, _ = scatter(Ks, Vl, bt, [L], NB, B)
+    a = decode_f64(O, q, kp, vp, bt, [L], scale, 1, B)
+    b = decode_f64(O, q, kps, vp, bt, [L], scale, 1, B)
+    assert np.all(np.isfinite(b))
+    assert np.max(np.abs(a - b)) < 1e-12
+
+
+def pin_output_in_convex_hull_of_values(O):
+    rng, Kl, Vl, q, lens = _case(7)
+    B, NB = 4, 12
+    bt = random_tables(rng, lens, B, NB, 4)
+    kp, vp = scatter(Kl, Vl, bt, lens, NB, B)
+    out = decode_f64(O, q, kp, vp, bt, lens, 2.0, 2, B)
+    for b, L in enumerate(lens):
+        for h in range(4):
+            V = Vl[b, h // 2, :L]
+            assert np.all(out[b, h] >= V.min(axis=0) - 1e-14)
+            assert np.all(out[b, h] <= V.max(axis=0) + 1e-14)
+
+
+def pin_grouped_query_mapping(O):
+    """Query head h reads KV head h // G (consecutive grouping); compared
+    with torch SDPA on K/V repeated G times along the head axis."""
+    rng = np.random.default_rng(8)
+    S, Hq, Hkv, D, B = 2, 8, 2, 16, 4
+    lens = [11, 6]
+    NB = 10
+    Kl = f32_normal(rng, (S, Hkv, 11, D))
+    Vl = f32_normal(rng, (S, Hkv, 11, D))
+    q = f32_normal(rng, (S, Hq, D))
+    bt = random_tables(rng, lens, B, NB, 3)
+    kp, vp = scatter(Kl, Vl, bt, lens, NB, B)
+    out = decode_f64(O, q, kp, vp, bt, lens, 0.3, Hkv, B)
+    for b, L in enumerate(lens):
+        Kt = torch.from_numpy(Kl[b, :, :L]).repeat_interleave(Hq // Hkv, dim=0)
+        Vt = torch.from_numpy(Vl[b, :, :L]).repeat_interleave(Hq // Hkv, dim=0)
+        qt = torch.from_numpy(q[b])[:, None, :]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, scale=0.3)[:, 0]
+        assert np.max(np.abs(out[b] - ref.numpy())) < 1e-12
+
+
+def pin_attention_matches_library_sdpa(O):
+    rng = np.random.default_rng(9)
+    for L, D in ((1, 4), (5, 128), (300, 64), (64, 1)):
+        q = rng.standard_normal(D)
+        K = rng.standard_normal((L, D))
+        V = rng.standard_normal((L, D))
+        a = O.attention(q, K, V, 0.37)
+        assert np.max(np.abs(a - sdpa(q, K, V, 0.37))) < 1e-12, (L, D)
+
+
+def pin_bruteforce_small_shapes(O):
+    """Many tiny random shapes against the independent numpy evaluation."""
+    rng = np.random.default_rng(10)
+    for trial in range(60):
+        B = int(rng.choice([1, 2, 4, 16]))
+        D = int(rng.choice([1, 2, 8]))
+        Hkv = int(rng.choice([1, 2]))
+        G = int(rng.choice([1, 2, 4]))
+        S = int(rng.integers(1, 4))
+        lens = rng.integers(0, 41, size=S)
+        lens[0] = max(lens[0], 1)
+        nbl = [-(-int(L) // B) for L in lens]
+        NB = sum(nbl) + int(rng.integers(0, 4))
+        mbs = max(max(nbl), 1) + int(rng.integers(0, 2))
+        bt = random_tables(rng, lens, B, NB, mbs)
+        Lmax = max(int(lens.max()), 1)
+        Kl = f32_normal(rng, (S, Hkv, Lmax, D))
+        Vl = f32_normal(rng, (S, Hkv, Lmax, D))
+        q = f32_normal(rng, (S, Hkv * G, D))
+        scale = float(rng.uniform(0.05, 1.5))
+        kp, vp = scatter(Kl, Vl, bt, lens, NB, B)
+        got = decode_f64(O, q, kp, vp, bt, lens, scale, Hkv, B)
+        want = numpy_reference(q, kp, vp, bt, lens, scale, Hkv, B)
+        assert np.max(np.abs(got - want)) < 1e-12, trial
+
+
+# ------------------------------------------------------------------ merge
+
+def _rows(seed, L=45, D=16):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal(D), rng.standard_normal((L, D)), rng.standard_normal((L, D))
+
+
+def pin_merge_of_block_partials_equals_one_softmax(O):
+    """Split the sequence at every block boundary, fold the partials with
+    the merge equation, normalise: equals the one-softmax result."""
+    q, K, V = _rows(12)
+    B, L, scale = 16, K.shape[0], 0.4
+    acc = (-math.inf, 0.0, np.zeros(K.shape[1]))
+    for t0 in range(0, L, B):
+        acc = O.merge(acc, O.partial(q, K, V, t0, min(t0 + B, L), scale))
+    m, l, o = acc
+    ref = O.attention(q, K, V, scale)
+    assert np.max(np.abs(o / l - ref)) < 1e-12
+    full = O.partial(q, K, V, 0, L, scale)
+    assert abs(m - full[0]) < 1e-15 and abs(l - full[1]) < 1e-12 * full[1]
+
+
+def pin_merge_order_does_not_matter(O):
+    q, K, V = _rows(13, L=64)
+    scale, rng = 0.6, np.random.default_rng(14)
+    parts = [O.partial(q, K, V, t0, t0 + 4, scale) for t0 in range(0, 64, 4)]
+    ref = O.attention(q, K, V, scale)
+    for _ in range(3):
+        order = rng.permutation(len(parts))
+        acc = (-math.inf, 0.0, np.zeros(K.shape[1]))
+        for i in order:
+            acc = O.merge(acc, parts[i])
+        assert np.max(np.abs(acc[2] / acc[1] - ref)) < 1e-12
+    # tree order
+    level = parts
+    while len(level) > 1:
+        level = [O.merge(level[i], level[i + 1]) for i in range(0, len(level), 2)]
+    assert np.max(np.abs(level[0][2] / level[0][1] - ref)) < 1e-12
+
+
+def pin_empty_partial_is_merge_identity(O):
+    q, K, V = _rows(15)
+    p = O.partial(q, K, V, 3, 20, 0.5)
+    e = O.partial(q, K, V, 7, 7, 0.5)
+    assert e[0] == -math.inf and e[1] == 0.0 and not np.any(e[2])
+    for r in (O.merge(e, p), O.merge(p, e)):
+        assert r[0] == p[0] and r[1] == p[1] and np.array_equal(r[2], p[2])
+    ee = O.merge(e, e)
+    assert ee[0] == -math.inf and ee[1] == 0.0 and not np.any(ee[2])
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
