@@ -1,0 +1,33 @@
+"""gfx950 paged decode attention: a C-ABI library (libpagedattn.so) and its
+thin Python binding.
+
+``_lib`` mirrors the C ABI (include/pagedattn.h) name for name; ``api``
+adds torch-tensor conveniences (descriptor from shapes, workspace and
+output allocation through torch, the current HIP stream)."""
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    PA_BF16,
+    PA_F16,
+    PA_F32,
+    PA_KERNEL_AUTO,
+    PA_KERNEL_MFMA,
+    PA_KERNEL_VALU,
+    LIB_PATH,
+    PaDesc,
+    PagedAttnError,
+    load,
+    pa_blocks_for_len,
+    pa_check_desc,
+    pa_decode_grid,
+    pa_decode_partitions,
+    pa_dtype_size,
+    pa_k_elem_offset,
+    pa_merge_partitions,
+    pa_pool_bytes,
+    pa_v_elem_offset,
+    pa_validate_host,
+    pa_workspace_bytes,
+    paged_attn_decode,
+    status_str,
+)
+from .api import decode, make_desc, ensure_built  # noqa: F401

@@ -1,0 +1,78 @@
+"""torch conveniences over the C ABI: a descriptor built from tensor
+shapes, output / workspace allocation through torch's caching allocator
+and the current HIP stream.  Marshalling only; the computation is the
+library's."""
+from __future__ import annotations
+
+import os
+
+import torch
+
+from . import _lib
+
+_TORCH_DTYPES = {torch.float32: _lib.PA_F32, torch.float16: _lib.PA_F16,
+                 torch.bfloat16: _lib.PA_BF16}
+
+
+def ensure_built() -> str:
+    """Build libpagedattn.so if it is not there yet; return its path."""
+    if not os.path.exists(_lib.LIB_PATH):
+        from . import build
+        build.build()
+    return _lib.LIB_PATH
+
+
+def pa_dtype_of(t: torch.dtype) -> int:
+    try:
+        return _TORCH_DTYPES[t]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t}") from None
+
+
+def make_desc(q: torch.Tensor, k_pool: torch.Tensor, block_tables: torch.Tensor, *,
+              out_dtype: torch.dtype | None = torch.float32, kernel: int = _lib.PA_KERNEL_AUTO
+              ) -> _lib.PaDesc:
+    """q [S][Hq][D]; k_pool [NB][Hkv][B][D]; block_tables int32 [S][max_blocks]."""
+    S, Hq, D = q.shape
+    NB, Hkv, B, Dk = k_pool.shape
+    if Dk != D:
+        raise ValueError("q and k_pool head_dim differ")
+    dt = pa_dtype_of(q.dtype)
+    odt = dt if out_dtype is None else pa_dtype_of(out_dtype)
+    return _lib.PaDesc(S, Hq, Hkv, D, B, NB, block_tables.shape[1], dt, odt, kernel)
+
+
+def decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, *,
+           out: torch.Tensor | None = None, out_dtype: torch.dtype | None = torch.float32,
+           kernel: int = _lib.PA_KERNEL_AUTO, workspace: torch.Tensor | None = None,
+           stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """Paged decode attention on device tensors; returns out [S][Hq][D].
+
+    k_pool [NB][Hkv][B][D] (token-major), v_pool [NB][Hkv][D][B]
+    (dim-major), block_tables / seq_lens int32, all on one GPU."""
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool),
+                    ("block_tables", block_tables), ("seq_lens", seq_lens)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_tables and seq_lens must be int32")
+    if k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+        raise TypeError("q, k_pool and v_pool must share a dtype")
+    NB, Hkv, B, D = k_pool.shape
+    if tuple(v_pool.shape) != (NB, Hkv, D, B):
+        raise ValueError("v_pool must be [num_blocks][num_kv_heads][head_dim][block_size]")
+    desc = make_desc(q, k_pool, block_tables, out_dtype=out_dtype, kernel=kernel)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    nbytes = _lib.pa_workspace_bytes(desc)
+    if nbytes == 0:
+        raise _lib.PagedAttnError(_lib.pa_check_desc(desc), "decode")
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    _lib.paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out, desc,
+                           workspace, workspace.numel() * workspace.element_size(),
+                           st.cuda_stream)
+    return out

@@ -1,0 +1,193 @@
+// decode_mfma.h — decode engine on the gfx950 matrix cores (fp16 / bf16).
+//
+// One workgroup piece = logical blocks [j0, j1) of one (sequence b, KV head).
+// Its tokens are streamed in 16-token sub-tiles; wave w of the workgroup
+// takes sub-tiles w, w+4, w+8, ... and keeps its own online-softmax state.
+//
+// Per sub-tile the query group of the KV head (G heads, padded to 16 MFMA
+// columns) meets the 16 keys as a dense tile:
+//   S^T[16 tok][16 heads]  = K[16 tok][128] . Q^T[128][16 heads]
+//       4 x v_mfma_f32_16x16x32_{bf16,f16}; A = K rows straight from the
+//       token-major K tile, B = the query group (loaded once per piece).
+//   O^T[128 dims][16 heads] += V^T[128][16 tok] . P^T[16 tok][16 heads]
+//       8 dim tiles x v_mfma_f32_16x16x16_{bf16,f16}; A = the dim-major V
+//       tile read as-is, B = P^T, which is exactly the C-layout of S^T, so
+//       the probabilities never leave their registers.
+// P is fed as hi + lo halves (p = hi + lo, both in the input type), so
+// the weighted sum keeps ~16 mantissa bits instead of the 8 (bf16) or 11
+// (fp16) one rounding would leave; this keeps the result within the fp32
+// accumulation budget.
+//
+// MFMA operand layouts used (wave64, 16x16 tiles; lane = 16*grp + col):
+//   A (16 x K): lane holds row `col`, K elements grp*k..grp*k+k-1 (k = K/4)
+//   B (K x 16): lane holds column `col`, the same K elements
+//   C/D (16 x 16): lane holds column `col`, rows 4*grp .. 4*grp+3
+// Only the pairing of A and B K-elements matters for a product, and both
+// operands are built with the same (grp, element) -> (dim or token) map.
+//
+// Softmax statistics follow "39 · PagedAttention", §2 (one softmax over all
+// scores) in its online form: a running max m per head, the running sum l
+// and the accumulator rescaled by 2^(m_old - m_new) when the max grows.
+#pragma once
+
+#include "pa_device.h"
+
+namespace pa {
+
+template <class T, int B, int G>
+struct MfmaEngine {
+  static_assert(T::kEsize == 2, "matrix-core path takes fp16 / bf16");
+  static_assert(G >= 1 && G <= 16, "query group padded to 16 MFMA columns");
+  static_assert(B % kSub == 0, "block size must be a multiple of 16");
+
+  using Smem = MergeSmem<G>;
+  using Op8 = typename std::conditional<T::kCode == BF16::kCode, bf16x8, f16x8>::type;
+  using Op4 = typename std::conditional<T::kCode == BF16::kCode, bf16x4, f16x4>::type;
+  using Elem = typename std::conditional<T::kCode == BF16::kCode, __bf16, _Float16>::type;
+
+  struct Tile {
+    uint4 k[4];  // K rows: token `col`, dims 32x + 8grp .. +8   (x = 0..3)
+    uint2 v[8];  // V^T: dim 16x + col, tokens 4grp .. 4grp+3   (x = 0..7)
+  };
+
+  static __device__ __forceinline__ f32x4 mma_qk(const uint4& k, const uint4& q, f32x4 c) {
+    const Op8 a = __builtin_bit_cast(Op8, k);
+    const Op8 b = __builtin_bit_cast(Op8, q);
+    if constexpr (T::kCode == BF16::kCode)
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+
+  static __device__ __forceinline__ f32x4 mma_pv(const uint2& v, const Op4& p, f32x4 c) {
+    const Op4 a = __builtin_bit_cast(Op4, v);
+    if constexpr (T::kCode == BF16::kCode)
+      return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, p, c, 0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_16x16x16f16(a, p, c, 0, 0, 0);
+  }
+
+  static __device__ void piece(const Args& a, Smem& sm, int b, int kvh, int j0, int j1,
+                               int L, bool complete, int slot) {
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+    const int col = lane & 15;
+    const int grp = lane >> 4;
+
+    // Query group as the B operand of the score product (zero columns >= G).
+    uint4 qop[4];
+    {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                           ((int64_t)b * a.Hq + (int64_t)kvh * G + col) * kD + 8 * grp;
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        qop[x] = col < G ? *reinterpret_cast<const uint4*>(qp + 32 * x) : make_uint4(0, 0, 0, 0);
+    }
+
+    const int tok_begin = j0 * B;
+    const int tok_end = min(j1 * B, L);
+    const int nsub = (tok_end - tok_begin + kSub - 1) / kSub;
+    const int32_t* __restrict__ row = a.bt + (int64_t)b * a.mbs;
+    const uint16_t* __restrict__ kbase = static_cast<const uint16_t*>(a.kp);
+    const uint16_t* __restrict__ vbase = static_cast<const uint16_t*>(a.vp);
+
+    auto load = [&](int i, Tile& t) {
+      const int tok = tok_begin + kSub * i;
+      const int j = tok / B;
+      const int s16 = tok - j * B;
+      const int phys = uniform(row[j]);
+      const int64_t tile = ((int64_t)phys * a.Hkv + kvh) * (int64_t)(B * kD);
+      const uint16_t* kp = kbase + tile + (s16 + col) * kD + 8 * grp;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) t.k[x] = *reinterpret_cast<const uint4*>(kp + 32 * x);
+      const uint16_t* vp = vbase + tile + col * B + s16 + 4 * grp;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) t.v[x] = *reinterpret_cast<const uint2*>(vp + 16 * x * B);
+    };
+
+    f32x4 acc[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) acc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY;  // running max of head `col` (base-2 units)
+    float lsum = 0.f;     // this lane's share of the running sum of 2^(s - m)
+
+    auto compute = [&](Tile& t, int i) {
+      const int valid = tok_end - (tok_begin + kSub * i);  // >= 1
+      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int x = 0; x < 4; ++x) s = mma_qk(t.k[x], qop[x], s);
+      float xr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) xr[r] = (4 * grp + r < valid) ? s[r] * a.scale_log2 : -INFINITY;
+      float bm = fmaxf(fmaxf(xr[0], xr[1]), fmaxf(xr[2], xr[3]));
+      bm = fmaxf(bm, xor_lanes(bm, 16));
+      bm = fmaxf(bm, xor_lanes(bm, 32));
+      const float mn = fmaxf(m, bm);
+      const float alpha = fast_exp2(m - mn);
+      m = mn;
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(xr[r] - mn);
+      lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+#pragma unroll
+      for (int x = 0; x < 8; ++x) acc[x] *= alpha;
+      Op4 phi, plo;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        phi[r] = (Elem)p[r];
+        plo[r] = (Elem)(p[r] - (float)phi[r]);
+      }
+      if (valid < kSub) {
+        // Slots past the sequence end may hold anything (NaN included):
+        // zero them so that 0 * slot cannot poison the product.
+        const int nv = valid - 4 * grp;  // valid tokens among this lane's 4
+        const uint32_t lo_keep = nv >= 1 ? 0x0000ffffu : 0u;
+        const uint32_t lo_mask = lo_keep | (nv >= 2 ? 0xffff0000u : 0u);
+        const uint32_t hi_mask = (nv >= 3 ? 0x0000ffffu : 0u) | (nv >= 4 ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          t.v[x].x &= lo_mask;
+          t.v[x].y &= hi_mask;
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        acc[x] = mma_pv(t.v[x], phi, acc[x]);
+        acc[x] = mma_pv(t.v[x], plo, acc[x]);
+      }
+    };
+
+    // Two sub-tiles in flight per wave: while one is consumed the next is loading.
+    Tile ta, tb;
+    int i = wave;
+    if (i < nsub) load(i, ta);
+    if (i + kWaves < nsub) load(i + kWaves, tb);
+    while (i < nsub) {
+      compute(ta, i);
+      if (i + 2 * kWaves < nsub) load(i + 2 * kWaves, ta);
+      i += kWaves;
+      if (i >= nsub) break;
+      compute(tb, i);
+      if (i + 2 * kWaves < nsub) load(i + 2 * kWaves, tb);
+      i += kWaves;
+    }
+
+    // Wave partial -> LDS: lsum summed over the 4 row groups of each column.
+    lsum += xor_lanes(lsum, 16);
+    lsum += xor_lanes(lsum, 32);
+    if (col < G) {
+#pragma unroll
+      for (int x = 0; x < 8; ++x)
+        *reinterpret_cast<f32x4*>(&sm.o[wave][col][16 * x + 4 * grp]) = acc[x];
+      if (grp == 0) {
+        sm.m[wave][col] = m;
+        sm.l[wave][col] = lsum;
+      }
+    }
+    __syncthreads();
+    emit_piece<T, G>(a, sm, b, kvh, complete, slot);
+    __syncthreads();
+  }
+};
+
+}  // namespace pa

@@ -1,0 +1,225 @@
+// decode_valu.h — decode engine on the vector ALU (fp32 / fp16 / bf16).
+//
+// Same work split as the matrix-core engine: a piece is logical blocks
+// [j0, j1) of one (sequence b, KV head), streamed in 16-token sub-tiles,
+// wave w taking sub-tiles w, w+4, ...  Products are fp32 FMAs.
+//
+// Scores.  The K sub-tile (16 token rows, token-major) is read as 16-byte
+// chunks, one per lane per load: a token row spans RL lanes (RL = 16 for
+// 16-bit types, 32 for fp32), so one load covers 64/RL tokens.  Each lane
+// dots its chunk with the matching slice of every query head of the group;
+// the RL partial sums of a row are then summed by DPP row moves (and one
+// cross-row exchange for fp32), leaving the token's score in all RL lanes.
+//
+// Weighted values.  The V sub-tile is dim-major (tokens of one value
+// dimension contiguous): each 16-byte chunk holds E consecutive tokens of
+// one dimension.  The probabilities of the sub-tile go through a 16-float
+// per-wave LDS line so every lane can read the E it needs; each lane then
+// accumulates o[dim] += sum_e p_e v_e for its dimensions, and the RV lanes
+// sharing a dimension are summed once at the end of the piece.
+//
+// Online softmax as in the matrix-core engine ("39 · PagedAttention", §2,
+// one softmax over all scores, kept as a running max and rescaled sums).
+#pragma once
+
+#include "pa_device.h"
+
+namespace pa {
+
+template <class T, int B, int G>
+struct ValuEngine {
+  static_assert(G >= 1 && G <= 8, "vector path holds the whole group in registers");
+  static_assert(B % kSub == 0, "block size must be a multiple of 16");
+  static constexpr int E = 16 / T::kEsize;  // elements per 16-byte chunk
+  static constexpr int RL = kD / E;         // lanes per K row
+  static constexpr int NK = kSub * RL / 64; // K loads per lane per sub-tile
+  static constexpr int TPL = 64 / RL;       // tokens per K load
+  static constexpr int RV = kSub / E;       // lanes per V dimension row
+  static constexpr int NV = kD * RV / 64;   // V loads per lane per sub-tile
+  static constexpr int DPL = 64 / RV;       // dimensions per V load
+
+  struct Smem : MergeSmem<G> {
+    float p[kWaves][G][kSub];
+  };
+
+  struct Tile {
+    uint4 k[NK];
+    uint4 v[NV];
+  };
+
+  static __device__ __forceinline__ float row_sum(float x) {
+    x = row16_sum(x);
+    if constexpr (RL == 32) x += xor_lanes(x, 16);
+    return x;
+  }
+
+  static __device__ void piece(const Args& a, Smem& sm, int b, int kvh, int j0, int j1, int L,
+                               bool complete, int slot) {
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+    const int rlane = lane % RL;  // position inside a K row
+    const int vlane = lane % RV;  // position inside a V dimension row
+
+    // This lane's slice of every query head of the group.
+    float qf[G][E];
+    {
+      const char* qb = static_cast<const char*>(a.q);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int64_t off = (((int64_t)b * a.Hq + (int64_t)kvh * G + g) * kD + rlane * E) * T::kEsize;
+        const uint4 c = *reinterpret_cast<const uint4*>(qb + off);
+        chunk_to_float<T>(c, qf[g]);
+      }
+    }
+
+    const int tok_begin = j0 * B;
+    const int tok_end = min(j1 * B, L);
+    const int nsub = (tok_end - tok_begin + kSub - 1) / kSub;
+    const int32_t* __restrict__ row = a.bt + (int64_t)b * a.mbs;
+    const char* __restrict__ kbase = static_cast<const char*>(a.kp);
+    const char* __restrict__ vbase = static_cast<const char*>(a.vp);
+
+    auto load = [&](int i, Tile& t) {
+      const int tok = tok_begin + kSub * i;
+      const int j = tok / B;
+      const int s16 = tok - j * B;
+      const int phys = uniform(row[j]);
+      const int64_t tile = ((int64_t)phys * a.Hkv + kvh) * (int64_t)(B * kD) * T::kEsize;
+      const char* kp = kbase + tile + ((int64_t)s16 * kD + lane / RL * kD + rlane * E) * T::kEsize;
+#pragma unroll
+      for (int n = 0; n < NK; ++n)
+        t.k[n] = *reinterpret_cast<const uint4*>(kp + (int64_t)n * TPL * kD * T::kEsize);
+      const char* vp = vbase + tile + ((int64_t)(lane / RV) * B + s16 + vlane * E) * T::kEsize;
+#pragma unroll
+      for (int n = 0; n < NV; ++n)
+        t.v[n] = *reinterpret_cast<const uint4*>(vp + (int64_t)n * DPL * B * T::kEsize);
+    };
+
+    float acc[NV][G];
+#pragma unroll
+    for (int n = 0; n < NV; ++n)
+#pragma unroll
+      for (int g = 0; g < G; ++g) acc[n][g] = 0.f;
+    float m[G], lsum[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = -INFINITY;
+      lsum[g] = 0.f;
+    }
+
+    auto compute = [&](Tile& t, int i) {
+      const int valid = tok_end - (tok_begin + kSub * i);  // >= 1
+      float x[NK][G];
+#pragma unroll
+      for (int n = 0; n < NK; ++n) {
+        float kf[E];
+        chunk_to_float<T>(t.k[n], kf);
+        const bool ok = n * TPL + lane / RL < valid;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float d = 0.f;
+#pragma unroll
+          for (int e = 0; e < E; ++e) d = fmaf(qf[g][e], kf[e], d);
+          d = row_sum(d);
+          x[n][g] = ok ? d * a.scale_log2 : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float bm = x[0][g];
+#pragma unroll
+        for (int n = 1; n < NK; ++n) bm = fmaxf(bm, x[n][g]);
+#pragma unroll
+        for (int msk = RL; msk < 64; msk <<= 1) bm = fmaxf(bm, xor_lanes(bm, msk));
+        const float mn = fmaxf(m[g], bm);
+        const float alpha = fast_exp2(m[g] - mn);
+        m[g] = mn;
+        float ps = 0.f;
+#pragma unroll
+        for (int n = 0; n < NK; ++n) {
+          x[n][g] = fast_exp2(x[n][g] - mn);
+          ps += x[n][g];
+        }
+        lsum[g] = lsum[g] * alpha + ps;
+#pragma unroll
+        for (int n = 0; n < NV; ++n) acc[n][g] *= alpha;
+      }
+      // Probabilities to the wave's LDS line: one lane per token row writes.
+      if (rlane == 0) {
+#pragma unroll
+        for (int n = 0; n < NK; ++n)
+#pragma unroll
+          for (int g = 0; g < G; ++g) sm.p[wave][g][n * TPL + lane / RL] = x[n][g];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      float pw[G][E];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < E; ++e) pw[g][e] = sm.p[wave][g][vlane * E + e];
+      const bool tail = valid < kSub;
+#pragma unroll
+      for (int n = 0; n < NV; ++n) {
+        float vf[E];
+        chunk_to_float<T>(t.v[n], vf);
+        if (tail) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) vf[e] = (vlane * E + e < valid) ? vf[e] : 0.f;
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[n][g] = fmaf(pw[g][e], vf[e], acc[n][g]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    Tile ta, tb;
+    int i = wave;
+    if (i < nsub) load(i, ta);
+    if (i + kWaves < nsub) load(i + kWaves, tb);
+    while (i < nsub) {
+      compute(ta, i);
+      if (i + 2 * kWaves < nsub) load(i + 2 * kWaves, ta);
+      i += kWaves;
+      if (i >= nsub) break;
+      compute(tb, i);
+      if (i + 2 * kWaves < nsub) load(i + 2 * kWaves, tb);
+      i += kWaves;
+    }
+
+    // Sum over the RV lanes of a dimension row and over the token rows.
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int n = 0; n < NV; ++n) {
+        acc[n][g] += dpp<kQuadXor1>(acc[n][g]);
+        if constexpr (RV == 4) acc[n][g] += dpp<kQuadXor2>(acc[n][g]);
+      }
+#pragma unroll
+      for (int msk = RL; msk < 64; msk <<= 1) lsum[g] += xor_lanes(lsum[g], msk);
+    }
+    if (vlane == 0) {
+#pragma unroll
+      for (int n = 0; n < NV; ++n)
+#pragma unroll
+        for (int g = 0; g < G; ++g) sm.o[wave][g][n * DPL + lane / RV] = acc[n][g];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        sm.m[wave][g] = m[g];
+        sm.l[wave][g] = lsum[g];
+      }
+    }
+    __syncthreads();
+    emit_piece<T, G>(a, sm, b, kvh, complete, slot);
+    __syncthreads();
+  }
+};
+
+}  // namespace pa

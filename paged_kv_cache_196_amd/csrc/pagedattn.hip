@@ -1,0 +1,381 @@
+// pagedattn.hip — gfx950 paged decode attention: kernels instantiation and
+// the C ABI declared in include/pagedattn.h.
+//
+// Launch structure of one call (all on the caller's stream):
+//   1. decode kernel (matrix-core or vector-ALU engine), grid = one
+//      resident wave of workgroups; each workgroup rebuilds the block-count
+//      prefix in LDS and walks its equal share of the flattened
+//      (sequence, KV head, logical block) units;
+//   2. merge kernel, one workgroup per chunk boundary; a boundary that cuts
+//      a (sequence, KV head) for the first time folds all its partials.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string.h>
+
+#include "pagedattn.h"
+#include "pa_device.h"
+#include "decode_mfma.h"
+#include "decode_valu.h"
+
+namespace pa {
+
+template <class T, int B, int G, bool kMfma>
+__global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
+  if constexpr (kMfma)
+    run_decode<T, B, G, MfmaEngine<T, B, G>>(a);
+  else
+    run_decode<T, B, G, ValuEngine<T, B, G>>(a);
+}
+
+// Folds the partials of every (sequence, KV head) that chunk boundaries cut
+// (merge equation of "39 · PagedAttention", §3) and writes out = o / l.
+template <class T, int G>
+__global__ __launch_bounds__(kThreads) void merge_kernel(Args a, int B) {
+  extern __shared__ int cum[];
+  __shared__ int wsum[kWaves];
+  build_prefix(a.lens, a.S, B, cum, wsum);
+  const int W = cum[a.S] * a.Hkv;
+  if (W == 0) return;
+  const int c = (W + a.nwg - 1) / a.nwg;
+  const int k = blockIdx.x + 1;  // boundary between chunks k-1 and k
+  const int f = k * c;
+  if (f >= W) return;
+  const int b = find_seq(cum, a.S, a.Hkv, f);
+  const int nb = cum[b + 1] - cum[b];
+  const int base = cum[b] * a.Hkv;
+  const int kvh = (f - base) / nb;
+  const int j = (f - base) - kvh * nb;
+  if (j == 0) return;  // a (sequence, KV head) starts here: nothing cut
+  const int ustart = base + kvh * nb;
+  const int kfirst = ustart / c;
+  if (k != kfirst + 1) return;  // handled at the first boundary inside it
+  const int klast = (ustart + nb - 1) / c;
+  const int first_slot = 2 * kfirst + (ustart != kfirst * c ? 1 : 0);
+  for (int idx = threadIdx.x; idx < G * kD; idx += kThreads) {
+    const int g = idx / kD, d = idx % kD;
+    float M = -INFINITY;
+    for (int kk = kfirst; kk <= klast; ++kk) {
+      const int slot = kk == kfirst ? first_slot : 2 * kk;
+      M = fmaxf(M, a.ws_ml[((int64_t)slot * G + g) * 2]);
+    }
+    float o = 0.f, l = 0.f;
+    for (int kk = kfirst; kk <= klast; ++kk) {
+      const int slot = kk == kfirst ? first_slot : 2 * kk;
+      const float f2 = rescale(a.ws_ml[((int64_t)slot * G + g) * 2], M);
+      o += f2 * a.ws_o[((int64_t)slot * G + g) * kD + d];
+      l += f2 * a.ws_ml[((int64_t)slot * G + g) * 2 + 1];
+    }
+    store_out<T>(a.out, ((int64_t)b * a.Hq + kvh * G + g) * kD + d, o / l, a.out_f32);
+  }
+}
+
+// ------------------------------------------------------------ dispatch
+
+using LaunchFn = hipError_t (*)(const Args&, int grid, size_t lds, hipStream_t);
+using OccFn = int (*)(size_t lds);
+using MergeFn = hipError_t (*)(const Args&, int B, int grid, size_t lds, hipStream_t);
+
+template <class T, int B, int G, bool M>
+hipError_t launch_decode(const Args& a, int grid, size_t lds, hipStream_t st) {
+  hipLaunchKernelGGL((decode_kernel<T, B, G, M>), dim3(grid), dim3(kThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+template <class T, int B, int G, bool M>
+int occupancy(size_t lds) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<T, B, G, M>, kThreads, lds) !=
+      hipSuccess)
+    return 0;
+  return n;
+}
+
+template <class T, int G>
+hipError_t launch_merge(const Args& a, int B, int grid, size_t lds, hipStream_t st) {
+  hipLaunchKernelGGL((merge_kernel<T, G>), dim3(grid), dim3(kThreads), lds, st, a, B);
+  return hipGetLastError();
+}
+
+struct Variant {
+  LaunchFn launch = nullptr;
+  OccFn occ = nullptr;
+  MergeFn merge = nullptr;
+};
+
+template <class T, int B, int G, bool M>
+Variant make_variant() {
+  Variant v;
+  v.launch = &launch_decode<T, B, G, M>;
+  v.occ = &occupancy<T, B, G, M>;
+  v.merge = &launch_merge<T, G>;
+  return v;
+}
+
+template <class T, int B, bool M>
+Variant pick_group(int G) {
+  switch (G) {
+    case 1: return make_variant<T, B, 1, M>();
+    case 2: return make_variant<T, B, 2, M>();
+    case 4: return make_variant<T, B, 4, M>();
+    case 8: return make_variant<T, B, 8, M>();
+    case 16:
+      if constexpr (M) return make_variant<T, B, 16, M>();
+      return Variant{};
+    default: return Variant{};
+  }
+}
+
+template <class T, bool M>
+Variant pick_block(int B, int G) {
+  if (B == 16) return pick_group<T, 16, M>(G);
+  if (B == 32) return pick_group<T, 32, M>(G);
+  return Variant{};
+}
+
+inline bool use_mfma(const pa_desc* d) {
+  if (d->kernel == PA_KERNEL_MFMA) return true;
+  if (d->kernel == PA_KERNEL_VALU) return false;
+  return d->dtype != PA_F32;
+}
+
+Variant pick(const pa_desc* d) {
+  const int G = d->num_q_heads / d->num_kv_heads;
+  const bool mf = use_mfma(d);
+  switch (d->dtype) {
+    case PA_F32: return mf ? Variant{} : pick_block<F32, false>(d->block_size, G);
+    case PA_F16: return mf ? pick_block<F16, true>(d->block_size, G) : pick_block<F16, false>(d->block_size, G);
+    case PA_BF16: return mf ? pick_block<BF16, true>(d->block_size, G) : pick_block<BF16, false>(d->block_size, G);
+    default: return Variant{};
+  }
+}
+
+// Per-device facts queried once.
+struct DeviceInfo {
+  bool ok = false;
+  int cus = 0;
+};
+
+DeviceInfo device_info() {
+  static std::mutex mu;
+  static DeviceInfo cache[64];
+  static bool known[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DeviceInfo{};
+  std::lock_guard<std::mutex> lk(mu);
+  if (!known[dev]) {
+    hipDeviceProp_t p;
+    DeviceInfo info;
+    if (hipGetDeviceProperties(&p, dev) == hipSuccess && strncmp(p.gcnArchName, "gfx950", 6) == 0) {
+      info.ok = true;
+      info.cus = p.multiProcessorCount;
+    }
+    cache[dev] = info;
+    known[dev] = true;
+  }
+  return cache[dev];
+}
+
+size_t prefix_lds(int S) { return (size_t)(S + 1) * sizeof(int); }
+
+size_t ws_floats(const pa_desc* d) {
+  const int64_t G = d->num_q_heads / d->num_kv_heads;
+  return (size_t)(2 * kMaxGrid) * G * (kD + 2);
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+const char* pa_status_str(int32_t s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: invalid size or num_q_heads % num_kv_heads != 0";
+    case PA_ERR_DTYPE: return "PA_ERR_DTYPE: unknown dtype or unsupported out_dtype";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: configuration not built (head_dim, block_size, group, kernel)";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_ALIGN: return "PA_ERR_ALIGN: q, pools and out must be 16-byte aligned";
+    case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: kernel launch failed";
+    case PA_ERR_TABLE: return "PA_ERR_TABLE: block table entry or sequence length out of range";
+    case PA_ERR_DEVICE: return "PA_ERR_DEVICE: no gfx950 device current";
+    default: return "unknown pa_status";
+  }
+}
+
+size_t pa_dtype_size(int32_t dt) {
+  switch (dt) {
+    case PA_F32: return 4;
+    case PA_F16:
+    case PA_BF16: return 2;
+    default: return 0;
+  }
+}
+
+int64_t pa_blocks_for_len(int64_t len, int32_t block_size) {
+  if (len <= 0 || block_size <= 0) return 0;
+  return (len + block_size - 1) / block_size;
+}
+
+int32_t pa_check_desc(const pa_desc* d) {
+  if (!d) return PA_ERR_NULL;
+  if (d->num_seqs < 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0 ||
+      d->block_size <= 0 || d->num_blocks <= 0 || d->max_blocks_per_seq <= 0)
+    return PA_ERR_SHAPE;
+  if (d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (pa_dtype_size(d->dtype) == 0) return PA_ERR_DTYPE;
+  if (d->out_dtype != PA_F32 && d->out_dtype != d->dtype) return PA_ERR_DTYPE;
+  if (d->head_dim != kD) return PA_ERR_UNSUPPORTED;
+  if (d->block_size != 16 && d->block_size != 32) return PA_ERR_UNSUPPORTED;
+  if (d->kernel < PA_KERNEL_AUTO || d->kernel > PA_KERNEL_MFMA) return PA_ERR_UNSUPPORTED;
+  if (d->kernel == PA_KERNEL_MFMA && d->dtype == PA_F32) return PA_ERR_UNSUPPORTED;
+  if (d->num_seqs > kMaxSeqs) return PA_ERR_UNSUPPORTED;
+  // flat unit indices are int32
+  if ((int64_t)d->num_seqs * d->max_blocks_per_seq * d->num_kv_heads >= ((int64_t)1 << 31))
+    return PA_ERR_UNSUPPORTED;
+  if (!pick(d).launch) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+size_t pa_pool_bytes(const pa_desc* d) {
+  if (pa_check_desc(d) != PA_OK) return 0;
+  return (size_t)d->num_blocks * d->num_kv_heads * d->block_size * d->head_dim *
+         pa_dtype_size(d->dtype);
+}
+
+int64_t pa_k_elem_offset(const pa_desc* d, int32_t block, int32_t kv_head, int32_t slot, int32_t dim) {
+  if (pa_check_desc(d) != PA_OK) return -1;
+  if (block < 0 || block >= d->num_blocks || kv_head < 0 || kv_head >= d->num_kv_heads || slot < 0 ||
+      slot >= d->block_size || dim < 0 || dim >= d->head_dim)
+    return -1;
+  return (((int64_t)block * d->num_kv_heads + kv_head) * d->block_size + slot) * d->head_dim + dim;
+}
+
+int64_t pa_v_elem_offset(const pa_desc* d, int32_t block, int32_t kv_head, int32_t slot, int32_t dim) {
+  if (pa_check_desc(d) != PA_OK) return -1;
+  if (block < 0 || block >= d->num_blocks || kv_head < 0 || kv_head >= d->num_kv_heads || slot < 0 ||
+      slot >= d->block_size || dim < 0 || dim >= d->head_dim)
+    return -1;
+  return (((int64_t)block * d->num_kv_heads + kv_head) * d->head_dim + dim) * d->block_size + slot;
+}
+
+size_t pa_workspace_bytes(const pa_desc* d) {
+  if (pa_check_desc(d) != PA_OK) return 0;
+  return ws_floats(d) * sizeof(float);
+}
+
+int32_t pa_validate_host(const pa_desc* d, const int32_t* bt, const int32_t* lens) {
+  const int32_t st = pa_check_desc(d);
+  if (st != PA_OK) return st;
+  if (d->num_seqs > 0 && (!bt || !lens)) return PA_ERR_NULL;
+  const int64_t cap = (int64_t)d->max_blocks_per_seq * d->block_size;
+  for (int32_t b = 0; b < d->num_seqs; ++b) {
+    if (lens[b] < 0 || lens[b] > cap) return PA_ERR_TABLE;
+    const int64_t n = pa_blocks_for_len(lens[b], d->block_size);
+    for (int64_t j = 0; j < n; ++j) {
+      const int32_t id = bt[(int64_t)b * d->max_blocks_per_seq + j];
+      if (id < 0 || id >= d->num_blocks) return PA_ERR_TABLE;
+    }
+  }
+  return PA_OK;
+}
+
+int32_t pa_decode_grid(const pa_desc* d) {
+  if (pa_check_desc(d) != PA_OK) return -1;
+  const DeviceInfo info = device_info();
+  if (!info.ok) return -1;
+  const Variant v = pick(d);
+  const int per_cu = v.occ(prefix_lds(d->num_seqs));
+  int grid = info.cus * (per_cu > 0 ? per_cu : 1);
+  if (grid > kMaxGrid) grid = kMaxGrid;
+  return grid;
+}
+
+static int32_t prepare(const void* q, const void* k_pool, const void* v_pool, const int32_t* bt,
+                       const int32_t* lens, float scale, void* out, const pa_desc* d,
+                       void* ws, size_t ws_bytes, Args* a, int* grid) {
+  const int32_t st = pa_check_desc(d);
+  if (st != PA_OK) return st;
+  if (d->num_seqs == 0) {
+    *grid = 0;
+    return PA_OK;
+  }
+  if (!q || !k_pool || !v_pool || !bt || !lens || !out) return PA_ERR_NULL;
+  if (((uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool | (uintptr_t)out) & 15u) return PA_ERR_ALIGN;
+  if (!ws || ws_bytes < pa_workspace_bytes(d) || ((uintptr_t)ws & 15u)) return PA_ERR_WORKSPACE;
+  const int g = pa_decode_grid(d);
+  if (g <= 0) return PA_ERR_DEVICE;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  a->q = q;
+  a->kp = k_pool;
+  a->vp = v_pool;
+  a->bt = bt;
+  a->lens = lens;
+  a->out = out;
+  a->ws_o = static_cast<float*>(ws);
+  a->ws_ml = static_cast<float*>(ws) + (size_t)(2 * kMaxGrid) * G * kD;
+  a->scale_log2 = scale * kLog2e;
+  a->S = d->num_seqs;
+  a->Hq = d->num_q_heads;
+  a->Hkv = d->num_kv_heads;
+  a->mbs = d->max_blocks_per_seq;
+  a->nwg = g;
+  a->out_f32 = d->out_dtype == PA_F32 ? 1 : 0;
+  *grid = g;
+  return PA_OK;
+}
+
+int32_t pa_decode_partitions(const void* q, const void* k_pool, const void* v_pool,
+                             const int32_t* bt, const int32_t* lens, float scale, void* out,
+                             const pa_desc* d, void* ws, size_t ws_bytes, void* stream) {
+  Args a;
+  int grid = 0;
+  const int32_t st = prepare(q, k_pool, v_pool, bt, lens, scale, out, d, ws, ws_bytes, &a, &grid);
+  if (st != PA_OK || grid == 0) return st;
+  const Variant v = pick(d);
+  if (v.launch(a, grid, prefix_lds(a.S), static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+int32_t pa_merge_partitions(const int32_t* lens, void* out, const pa_desc* d, void* ws,
+                            size_t ws_bytes, void* stream) {
+  const int32_t st = pa_check_desc(d);
+  if (st != PA_OK) return st;
+  if (d->num_seqs == 0) return PA_OK;
+  if (!lens || !out) return PA_ERR_NULL;
+  if ((uintptr_t)out & 15u) return PA_ERR_ALIGN;
+  if (!ws || ws_bytes < pa_workspace_bytes(d) || ((uintptr_t)ws & 15u)) return PA_ERR_WORKSPACE;
+  const int g = pa_decode_grid(d);
+  if (g <= 0) return PA_ERR_DEVICE;
+  if (g < 2) return PA_OK;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  Args a;
+  memset(&a, 0, sizeof a);
+  a.lens = lens;
+  a.out = out;
+  a.ws_o = static_cast<float*>(ws);
+  a.ws_ml = static_cast<float*>(ws) + (size_t)(2 * kMaxGrid) * G * kD;
+  a.S = d->num_seqs;
+  a.Hq = d->num_q_heads;
+  a.Hkv = d->num_kv_heads;
+  a.mbs = d->max_blocks_per_seq;
+  a.nwg = g;
+  a.out_f32 = d->out_dtype == PA_F32 ? 1 : 0;
+  const Variant v = pick(d);
+  if (v.merge(a, d->block_size, g - 1, prefix_lds(a.S), static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+int32_t paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* bt, const int32_t* lens, float scale, void* out,
+                          const pa_desc* d, void* ws, size_t ws_bytes, void* stream) {
+  const int32_t st = pa_decode_partitions(q, k_pool, v_pool, bt, lens, scale, out, d, ws, ws_bytes, stream);
+  if (st != PA_OK) return st;
+  return pa_merge_partitions(lens, out, d, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,163 @@
+"""GPU parity: the gfx950 library through its C ABI against the fp64
+oracle on the same seeded inputs.  Bar: max |out - oracle| <= 2e-3 for
+fp16/bf16 inputs (fp32 accumulation, fp32 output) and <= 1e-5 for fp32."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload
+from tests.gpu_util import TOL, Uploaded, kernels_for, max_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def O():
+    oracle.build(force=False)
+    return oracle.load()
+
+
+_cache = {}
+
+
+def _full(cfg, O):
+    if cfg not in _cache:
+        _cache.clear()
+        w = workload.make(cfg)
+        _cache[cfg] = (Uploaded(w), O.run_workload(w))
+    return _cache[cfg]
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_named_workload_full_size(O, cfg):
+    """Every output of the full-size workload, in the launch configuration
+    the benchmark times (automatic kernel choice), then each kernel."""
+    up, ref = _full(cfg, O)
+    for kern in ["auto"] + kernels_for(up.w.dtype):
+        _log(f"[parity] cfg {cfg} {up.w.name} kernel={kern}")
+        err = max_err(up.run(kern), ref)
+        _log(f"[parity] cfg {cfg} kernel={kern} max_abs_err={err:.3e}")
+        assert err <= TOL[up.w.dtype], (cfg, kern, err)
+
+
+@pytest.mark.parametrize("seed", [101, 102, 103])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_named_workload_reduced(O, cfg, seed):
+    w = workload.make(cfg, seed, batch={2: 3, 3: 5, 4: 2, 5: 24}[cfg],
+                      max_len={2: None, 3: 3000, 4: 5000, 5: None}[cfg])
+    ref = O.run_workload(w)
+    up = Uploaded(w)
+    for kern in kernels_for(w.dtype):
+        _log(f"[parity] reduced cfg {cfg} seed {seed} kernel={kern}")
+        err = max_err(up.run(kern), ref)
+        assert err <= TOL[w.dtype], (cfg, seed, kern, err)
+
+
+EDGE_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 47, 48, 63, 64, 65, 127, 129, 255, 300, 511, 1000]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("B", [16, 32])
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+def test_ragged_edges(O, dtype, B, G):
+    """Lengths around block and sub-tile boundaries, empty sequences and a
+    sequence filling its whole table row, for each group size."""
+    if dtype == "f32" and G == 16:
+        pytest.skip("group 16 is built for the matrix-core kernel only")
+    rng = np.random.default_rng(1000 + B + G)
+    lens = list(EDGE_LENS) + [0, 0]
+    rng.shuffle(lens)
+    mbs = -(-max(lens) // B) + 1
+    lens.append(mbs * B)  # exactly fills max_blocks_per_seq
+    Hkv = 2
+    w = workload.build(name="edges", dtype=dtype, seq_lens=lens, num_q_heads=Hkv * G,
+                       num_kv_heads=Hkv, head_dim=128, block_size=B, seed=int(rng.integers(1 << 30)),
+                       max_blocks_per_seq=mbs)
+    ref = O.run_workload(w)
+    up = Uploaded(w)
+    for kern in kernels_for(dtype):
+        if kern == "valu" and G == 16:
+            continue
+        err = max_err(up.run(kern), ref)
+        assert err <= TOL[dtype], (dtype, B, G, kern, err)
+
+
+def test_single_sequence_single_token(O):
+    w = workload.build(name="one", dtype="bf16", seq_lens=[1], num_q_heads=4, num_kv_heads=1,
+                       head_dim=128, block_size=16, seed=5)
+    ref = O.run_workload(w)
+    up = Uploaded(w)
+    for kern in ("valu", "mfma"):
+        assert max_err(up.run(kern), ref) <= 2e-3
+
+
+def test_all_sequences_empty():
+    w = workload.build(name="empty", dtype="bf16", seq_lens=[0, 0, 0], num_q_heads=8,
+                       num_kv_heads=2, head_dim=128, block_size=16, seed=6, num_blocks=4,
+                       max_blocks_per_seq=2)
+    up = Uploaded(w)
+    for kern in ("valu", "mfma"):
+        out = up.run(kern)
+        assert torch.count_nonzero(out).item() == 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_output_in_input_dtype(O, dtype):
+    """out_dtype = input dtype: the fp32 result rounded once (RNE), so the
+    bound is 2e-3 plus half an ulp of the output type at |ref|."""
+    w = workload.make(5, 7, batch=16) if dtype == "bf16" else workload.make(2, 7, batch=2)
+    ref = O.run_workload(w)
+    up = Uploaded(w)
+    mant = 8 if dtype == "bf16" else 11
+    half_ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - mant)
+    for kern in kernels_for(dtype):
+        got = up.run(kern, out_dtype=up.q.dtype).double().cpu().numpy()
+        assert np.all(np.abs(got - ref) <= 2e-3 + half_ulp), kern
+
+
+def test_block_permutation_gives_bitwise_equal_output(O):
+    """Same logical K/V behind a different physical placement: identical
+    work schedule, identical arithmetic, identical bits."""
+    w = workload.make(3, 11, batch=6, max_len=2000)
+    rng = np.random.default_rng(12)
+    perm = rng.permutation(w.num_blocks)
+    k2 = np.empty_like(w.k_pool)
+    v2 = np.empty_like(w.v_pool)
+    k2[perm] = w.k_pool
+    v2[perm] = w.v_pool
+    bt2 = np.where(w.block_tables >= 0, perm[np.maximum(w.block_tables, 0)], -1).astype(np.int32)
+    w2 = workload.Workload(**{**w.__dict__, "k_pool": k2, "v_pool": v2, "block_tables": bt2})
+    a, b = Uploaded(w), Uploaded(w2)
+    for kern in ("valu", "mfma"):
+        assert torch.equal(a.run(kern), b.run(kern)), kern
+
+
+def test_repeat_runs_are_bitwise_identical():
+    w = workload.make(4, 13, batch=2, max_len=8192)
+    up = Uploaded(w)
+    for kern in ("valu", "mfma"):
+        r1, r2 = up.run(kern), up.run(kern)
+        assert torch.equal(r1, r2), kern
+
+
+def test_split_entry_points_equal_whole_call():
+    import paged_kv_cache_196_amd as pa
+    w = workload.make(4, 14, batch=2, max_len=4096)
+    up = Uploaded(w)
+    whole = up.run("mfma")
+    desc = pa.make_desc(up.q, up.k, up.bt, kernel=pa.PA_KERNEL_MFMA)
+    nbytes = pa.pa_workspace_bytes(desc)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(whole)
+    st = torch.cuda.current_stream().cuda_stream
+    pa.pa_decode_partitions(up.q, up.k, up.v, up.bt, up.lens, float(w.scale), out, desc, ws, nbytes, st)
+    pa.pa_merge_partitions(up.lens, out, desc, ws, nbytes, st)
+    torch.cuda.synchronize()
+    assert torch.equal(out, whole)
