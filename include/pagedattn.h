@@ -25,18 +25,20 @@
  *   q            [num_seqs][num_q_heads][head_dim]              dtype
  *   out          [num_seqs][num_q_heads][head_dim]              out_dtype
  *   k_pool       [num_blocks][num_kv_heads][block_size][head_dim]   token-major
- *   v_pool       [num_blocks][num_kv_heads][head_dim][block_size]   dim-major
+ *   v_pool       [num_blocks][num_kv_heads][block_size/16][head_dim][16]
  *   block_tables int32 [num_seqs][max_blocks_per_seq]
  *   seq_lens     int32 [num_seqs]
  *
  * One (physical block, KV head) tile of either pool is one contiguous
  * block_size*head_dim*esize-byte range (4 KiB for bf16/fp16 with 16-token
  * blocks), so a block is read as a single coalesced burst.  K is stored
- * token-major (a token's key row is contiguous, the reduction axis of q.k);
- * V is stored dim-major inside the tile (the block's tokens for one value
- * dimension are contiguous, the reduction axis of w.V).  Both choices put
- * each product's reduction axis innermost, which is the operand layout the
- * gfx950 matrix cores consume directly.
+ * token-major (a token's key row is contiguous: the reduction axis of q.k).
+ * V is stored transposed inside each group of 16 tokens (for one value
+ * dimension the group's 16 values are contiguous: the reduction axis of
+ * w.V), groups in token order, so every 16 consecutive tokens of a block
+ * are one contiguous K range and one contiguous V range whatever the block
+ * size.  Both choices put each product's reduction axis innermost, which
+ * is the operand layout the gfx950 matrix cores consume directly.
  *
  * Table semantics.  Sequence b has n_b = ceil(L / block_size) logical
  * blocks; entries j >= n_b of its table row are never read (they may hold
@@ -135,8 +137,11 @@ int64_t pa_v_elem_offset(const pa_desc* desc, int32_t block, int32_t kv_head,
                          int32_t slot, int32_t dim);
 
 /* Bytes of device workspace that paged_attn_decode needs for this
- * descriptor (holds the partition partials of split sequences); 0 on a bad
- * descriptor.  The content needs no initialisation. */
+ * descriptor; 0 on a bad descriptor.  The workspace holds, for sequences
+ * split across workgroups, their partial results and one arrival counter
+ * per split.  It must be zero-filled once before its first use (e.g.
+ * hipMemset); every call leaves it zeroed again, so it can be reused
+ * without clearing.  Calls that share a workspace must not overlap. */
 size_t pa_workspace_bytes(const pa_desc* desc);
 
 /* Checks the descriptor, then the data-dependent preconditions on HOST
@@ -149,31 +154,23 @@ int32_t pa_validate_host(const pa_desc* desc, const int32_t* block_tables_host,
 /* Checks a descriptor alone (what every launching entry point checks). */
 int32_t pa_check_desc(const pa_desc* desc);
 
-/* Paged decode attention, whole operation: the decode kernel then, on the
- * same stream, the partition-merge kernel.  All pointers are device
- * pointers in the layouts above; `scale` multiplies q.k (1/sqrt(head_dim)
- * for standard attention).  workspace: device buffer of at least
- * pa_workspace_bytes(desc) bytes. */
+/* Paged decode attention: one kernel launch on `stream`.  All pointers are
+ * device pointers in the layouts above; `scale` multiplies q.k
+ * (1/sqrt(head_dim) for standard attention).  workspace: device buffer of
+ * at least pa_workspace_bytes(desc) bytes, zeroed before its first use.
+ *
+ * Work split (the sequence split of "PagedAttention: The Cache Was Storing
+ * Nothing", "Where this goes next"): the (sequence, KV head, logical block)
+ * units of the batch are cut into equal contiguous chunks, one per
+ * workgroup.  A (sequence, KV head) cut by chunk boundaries produces one
+ * (max, sum-of-exp, weighted-V) partial per chunk, and the workgroup that
+ * finishes last folds them with
+ *   m = max(m1, m2),  l = l1*e^(m1-m) + l2*e^(m2-m),  o = o1*e^(m1-m) + o2*e^(m2-m)
+ * ("39 · PagedAttention", §3 "On the GPU", merge equation) into out = o / l. */
 int32_t paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
                           const int32_t* block_tables, const int32_t* seq_lens,
                           float scale, void* out, const pa_desc* desc,
                           void* workspace, size_t workspace_bytes, void* stream);
-
-/* The two launches of paged_attn_decode, exposed separately so that each
- * kernel can be timed on its own.  pa_decode_partitions walks the block
- * tables, writes `out` for sequences processed whole by one workgroup and
- * (max, sum-of-exp, weighted-V) partials for the rest into the workspace;
- * pa_merge_partitions folds those partials with
- *   m = max(m1, m2),  l = l1*e^(m1-m) + l2*e^(m2-m),  o = o1*e^(m1-m) + o2*e^(m2-m)
- * ("39 · PagedAttention", §3 "On the GPU", merge equation) and writes
- * out = o / l.  Calling pa_decode_partitions then pa_merge_partitions with
- * the same arguments on one stream equals paged_attn_decode. */
-int32_t pa_decode_partitions(const void* q, const void* k_pool, const void* v_pool,
-                             const int32_t* block_tables, const int32_t* seq_lens,
-                             float scale, void* out, const pa_desc* desc,
-                             void* workspace, size_t workspace_bytes, void* stream);
-int32_t pa_merge_partitions(const int32_t* seq_lens, void* out, const pa_desc* desc,
-                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Number of decode workgroups a launch uses for this descriptor on the
  * current device (the split-K granularity), or -1 on error. */

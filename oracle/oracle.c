@@ -42,7 +42,9 @@
  * their definition, not shared):
  *    q        [S][Hq][D]
  *    k_pool   [num_blocks][Hkv][B][D]     (token-major tile)
- *    v_pool   [num_blocks][Hkv][D][B]     (dim-major tile)
+ *    v_pool   [num_blocks][Hkv][B/S][D][S] (value rows transposed within
+ *                                          groups of S tokens; S = 16 when
+ *                                          B is a multiple of 16, else S = B)
  *    tables   int32 [S][max_blocks_per_seq]
  * Element types: 0 = IEEE binary32, 1 = IEEE binary16, 2 = bfloat16.
  * Every element is widened to fp64 exactly.
@@ -104,6 +106,7 @@ int oracle_gather(const void* k_pool, const void* v_pool, const int32_t* block_t
                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
                   int32_t max_blocks_per_seq, int32_t dtype, double* K, double* V) {
   const int64_t D = head_dim, B = block_size, H = num_kv_heads;
+  const int64_t S = (B % 16 == 0) ? 16 : B; /* tokens per transposed V group */
   for (int64_t t = 0; t < L; ++t) {
     const int64_t j = t / B;    /* logical block */
     const int64_t slot = t % B; /* position inside the block */
@@ -113,7 +116,7 @@ int oracle_gather(const void* k_pool, const void* v_pool, const int32_t* block_t
     const int64_t tile = (phys * H + g) * B * D; /* same tile base in both pools */
     for (int64_t d = 0; d < D; ++d) {
       K[t * D + d] = elem(k_pool, dtype, tile + slot * D + d);
-      V[t * D + d] = elem(v_pool, dtype, tile + d * B + slot);
+      V[t * D + d] = elem(v_pool, dtype, tile + (slot / S) * D * S + d * S + slot % S);
     }
   }
   return 0;

@@ -38,9 +38,14 @@ def compile_source(src: str, out: str) -> str:
     return out
 
 
+def _stale() -> bool:
+    return (not os.path.exists(LIBRARY)) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE)
+
+
 def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so."""
-    if force or not os.path.exists(LIBRARY):
+    """Compile oracle.c into liboracle.so (always when force, else only if
+    the library is missing or older than the source)."""
+    if force or _stale():
         compile_source(SOURCE, LIBRARY)
     return LIBRARY
 
@@ -147,7 +152,8 @@ class Oracle:
                      num_threads: int = 0) -> np.ndarray:
         """fp64 out[S][Hq][D] of paged decode attention.
 
-        q: [S][Hq][D]; k_pool: [NB][Hkv][B][D]; v_pool: [NB][Hkv][D][B]
+        q: [S][Hq][D]; k_pool: [NB][Hkv][B][D]; v_pool: [NB][Hkv][B/G][D][G]
+        with G = 16 when B is a multiple of 16, else G = B
         (raw storage: float32, or 16-bit patterns for f16/bf16);
         block_tables int32 [S][max_blocks_per_seq]; seq_lens int32 [S];
         scale is used as given (pass the float32 value the GPU receives).
@@ -179,11 +185,12 @@ _default: Oracle | None = None
 
 
 def load() -> Oracle:
-    """The default build (oracle/liboracle.so), built first only if missing."""
+    """The default build (oracle/liboracle.so), (re)built first if missing or
+    older than oracle.c."""
     global _default
     with _lock:
         if _default is None:
-            if not os.path.exists(LIBRARY):
+            if _stale():
                 build(force=True)
             _default = Oracle(LIBRARY)
     return _default

@@ -19,10 +19,8 @@ from ._lib import (  # noqa: F401
     pa_blocks_for_len,
     pa_check_desc,
     pa_decode_grid,
-    pa_decode_partitions,
     pa_dtype_size,
     pa_k_elem_offset,
-    pa_merge_partitions,
     pa_pool_bytes,
     pa_v_elem_offset,
     pa_validate_host,
@@ -30,4 +28,4 @@ from ._lib import (  # noqa: F401
     paged_attn_decode,
     status_str,
 )
-from .api import decode, make_desc, ensure_built  # noqa: F401
+from .api import decode, ensure_built, make_desc, new_workspace  # noqa: F401

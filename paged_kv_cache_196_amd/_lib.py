@@ -23,7 +23,7 @@ PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
 EXPORTS = (
     "pa_status_str", "pa_dtype_size", "pa_blocks_for_len", "pa_pool_bytes", "pa_k_elem_offset",
     "pa_v_elem_offset", "pa_workspace_bytes", "pa_validate_host", "pa_check_desc",
-    "paged_attn_decode", "pa_decode_partitions", "pa_merge_partitions", "pa_decode_grid",
+    "paged_attn_decode", "pa_decode_grid",
 )
 
 
@@ -74,12 +74,9 @@ def load() -> ctypes.CDLL:
             lib.pa_validate_host.restype = ctypes.c_int32
             lib.pa_check_desc.argtypes = [_DP]
             lib.pa_check_desc.restype = ctypes.c_int32
-            for n in ("paged_attn_decode", "pa_decode_partitions"):
-                f = getattr(lib, n)
-                f.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, _P, _DP, _P, ctypes.c_size_t, _P]
-                f.restype = ctypes.c_int32
-            lib.pa_merge_partitions.argtypes = [_P, _P, _DP, _P, ctypes.c_size_t, _P]
-            lib.pa_merge_partitions.restype = ctypes.c_int32
+            lib.paged_attn_decode.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, _P, _DP, _P,
+                                              ctypes.c_size_t, _P]
+            lib.paged_attn_decode.restype = ctypes.c_int32
             lib.pa_decode_grid.argtypes = [_DP]
             lib.pa_decode_grid.restype = ctypes.c_int32
             _lib = lib
@@ -152,18 +149,3 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, o
                                   _ptr(seq_lens), float(scale), _ptr(out), ctypes.byref(desc),
                                   _ptr(workspace), int(workspace_bytes), _ptr(stream))
     return _check(rc, "paged_attn_decode")
-
-
-def pa_decode_partitions(q, k_pool, v_pool, block_tables, seq_lens, scale: float, out,
-                         desc: PaDesc, workspace, workspace_bytes: int, stream=None) -> int:
-    rc = load().pa_decode_partitions(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
-                                     _ptr(seq_lens), float(scale), _ptr(out), ctypes.byref(desc),
-                                     _ptr(workspace), int(workspace_bytes), _ptr(stream))
-    return _check(rc, "pa_decode_partitions")
-
-
-def pa_merge_partitions(seq_lens, out, desc: PaDesc, workspace, workspace_bytes: int,
-                        stream=None) -> int:
-    rc = load().pa_merge_partitions(_ptr(seq_lens), _ptr(out), ctypes.byref(desc),
-                                    _ptr(workspace), int(workspace_bytes), _ptr(stream))
-    return _check(rc, "pa_merge_partitions")

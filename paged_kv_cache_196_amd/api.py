@@ -42,14 +42,27 @@ def make_desc(q: torch.Tensor, k_pool: torch.Tensor, block_tables: torch.Tensor,
     return _lib.PaDesc(S, Hq, Hkv, D, B, NB, block_tables.shape[1], dt, odt, kernel)
 
 
+def new_workspace(desc: _lib.PaDesc, device) -> torch.Tensor:
+    """A zero-filled workspace for `desc` (the library keeps it zeroed
+    between calls, so it can be reused without clearing)."""
+    nbytes = _lib.pa_workspace_bytes(desc)
+    if nbytes == 0:
+        raise _lib.PagedAttnError(_lib.pa_check_desc(desc), "new_workspace")
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
 def decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, *,
            out: torch.Tensor | None = None, out_dtype: torch.dtype | None = torch.float32,
            kernel: int = _lib.PA_KERNEL_AUTO, workspace: torch.Tensor | None = None,
            stream: torch.cuda.Stream | None = None) -> torch.Tensor:
     """Paged decode attention on device tensors; returns out [S][Hq][D].
 
-    k_pool [NB][Hkv][B][D] (token-major), v_pool [NB][Hkv][D][B]
-    (dim-major), block_tables / seq_lens int32, all on one GPU."""
+    workspace: reuse one from new_workspace() to avoid an allocation per
+    call (it must have been zero-filled once; the library keeps it so).
+
+    k_pool [NB][Hkv][B][D] (token-major), v_pool [NB][Hkv][B/16][D][16]
+    (transposed within 16-token groups), block_tables / seq_lens int32,
+    all on one GPU."""
     for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool),
                     ("block_tables", block_tables), ("seq_lens", seq_lens)):
         if not t.is_cuda:
@@ -61,16 +74,13 @@ def decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, *,
     if k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
         raise TypeError("q, k_pool and v_pool must share a dtype")
     NB, Hkv, B, D = k_pool.shape
-    if tuple(v_pool.shape) != (NB, Hkv, D, B):
-        raise ValueError("v_pool must be [num_blocks][num_kv_heads][head_dim][block_size]")
+    if B % 16 != 0 or tuple(v_pool.shape) != (NB, Hkv, B // 16, D, 16):
+        raise ValueError("v_pool must be [num_blocks][num_kv_heads][block_size/16][head_dim][16]")
     desc = make_desc(q, k_pool, block_tables, out_dtype=out_dtype, kernel=kernel)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
-    nbytes = _lib.pa_workspace_bytes(desc)
-    if nbytes == 0:
-        raise _lib.PagedAttnError(_lib.pa_check_desc(desc), "decode")
-    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(desc, q.device)
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
     _lib.paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, scale, out, desc,
                            workspace, workspace.numel() * workspace.element_size(),

@@ -27,6 +27,9 @@ def command(out: str = LIB, extra=()) -> list:
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # packed fp32 VALU forms are kept out of the generated code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in ordinary VGPRs: the online softmax rescales
+        # them every sub-tile, which would otherwise shuttle them out of AGPRs
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", INCLUDE, "-I", os.path.join(PKG, "csrc"),
         *extra, SRC, "-o", out,
     ]

@@ -10,9 +10,10 @@
 //       4 x v_mfma_f32_16x16x32_{bf16,f16}; A = K rows straight from the
 //       token-major K tile, B = the query group (loaded once per piece).
 //   O^T[128 dims][16 heads] += V^T[128][16 tok] . P^T[16 tok][16 heads]
-//       8 dim tiles x v_mfma_f32_16x16x16_{bf16,f16}; A = the dim-major V
-//       tile read as-is, B = P^T, which is exactly the C-layout of S^T, so
-//       the probabilities never leave their registers.
+//       8 dim tiles x v_mfma_f32_16x16x16_{bf16,f16}; A = the V group of
+//       the sub-tile, stored transposed ([128][16]) and read as-is, B = P^T,
+//       which is exactly the C-layout of S^T, so the probabilities never
+//       leave their registers.
 // P is fed as hi + lo halves (p = hi + lo, both in the input type), so
 // the weighted sum keeps ~16 mantissa bits instead of the 8 (bf16) or 11
 // (fp16) one rounding would leave; this keeps the result within the fp32
@@ -67,8 +68,8 @@ struct MfmaEngine {
       return __builtin_amdgcn_mfma_f32_16x16x16f16(a, p, c, 0, 0, 0);
   }
 
-  static __device__ void piece(const Args& a, Smem& sm, int b, int kvh, int j0, int j1,
-                               int L, bool complete, int slot) {
+  static __device__ void piece(const Args& a, Smem& sm, const Piece& pc) {
+    const int b = pc.b, kvh = pc.kvh, j0 = pc.j0, j1 = pc.j1, L = pc.L;
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
     const int col = lane & 15;
@@ -87,22 +88,22 @@ struct MfmaEngine {
     const int tok_begin = j0 * B;
     const int tok_end = min(j1 * B, L);
     const int nsub = (tok_end - tok_begin + kSub - 1) / kSub;
-    const int32_t* __restrict__ row = a.bt + (int64_t)b * a.mbs;
-    const uint16_t* __restrict__ kbase = static_cast<const uint16_t*>(a.kp);
-    const uint16_t* __restrict__ vbase = static_cast<const uint16_t*>(a.vp);
+    const const_i32_ptr row = as_constant(a.bt + (int64_t)b * a.mbs);
 
-    auto load = [&](int i, Tile& t) {
-      const int tok = tok_begin + kSub * i;
-      const int j = tok / B;
-      const int s16 = tok - j * B;
-      const int phys = uniform(row[j]);
-      const int64_t tile = ((int64_t)phys * a.Hkv + kvh) * (int64_t)(B * kD);
-      const uint16_t* kp = kbase + tile + (s16 + col) * kD + 8 * grp;
+    // Physical block of sub-tile i (a scalar load: the table is read-only).
+    auto phys_of = [&](int i) { return row[(tok_begin + kSub * i) / B]; };
+    constexpr int kTileBytes = B * kD * 2;
+    const int koff = (col * kD + 8 * grp) * 2;  // this lane's K bytes inside a sub-tile
+    const int voff = (col * kSub + 4 * grp) * 2;  // this lane's V^T bytes inside a group
+    auto load = [&](int i, int phys, Tile& t) {
+      const int s16 = (tok_begin + kSub * i) % B;
+      const int64_t tile = ((int64_t)phys * a.Hkv + kvh) * kTileBytes;
+      const auto rk = tile_rsrc(a.kp, tile, kTileBytes);
+      const auto rv = tile_rsrc(a.vp, tile, kTileBytes);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) t.k[x] = *reinterpret_cast<const uint4*>(kp + 32 * x);
-      const uint16_t* vp = vbase + tile + col * B + s16 + 4 * grp;
+      for (int x = 0; x < 4; ++x) t.k[x] = tile_load16(rk, koff + 64 * x, s16 * kD * 2);
 #pragma unroll
-      for (int x = 0; x < 8; ++x) t.v[x] = *reinterpret_cast<const uint2*>(vp + 16 * x * B);
+      for (int x = 0; x < 8; ++x) t.v[x] = tile_load8(rv, voff + 32 * x * kSub, s16 * kD * 2);
     };
 
     f32x4 acc[8];
@@ -120,17 +121,22 @@ struct MfmaEngine {
 #pragma unroll
       for (int r = 0; r < 4; ++r) xr[r] = (4 * grp + r < valid) ? s[r] * a.scale_log2 : -INFINITY;
       float bm = fmaxf(fmaxf(xr[0], xr[1]), fmaxf(xr[2], xr[3]));
-      bm = fmaxf(bm, xor_lanes(bm, 16));
-      bm = fmaxf(bm, xor_lanes(bm, 32));
+      bm = max_xor16(bm);
+      bm = max_xor32(bm);
       const float mn = fmaxf(m, bm);
-      const float alpha = fast_exp2(m - mn);
-      m = mn;
+      if (wave_any(mn > m)) {
+        // The max grew somewhere in the wave: rescale sums and accumulators
+        // (alpha = 1 in lanes whose max did not move).
+        const float alpha = fast_exp2(m - mn);
+        lsum *= alpha;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[x] *= alpha;
+        m = mn;
+      }
       float p[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(xr[r] - mn);
-      lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-#pragma unroll
-      for (int x = 0; x < 8; ++x) acc[x] *= alpha;
+      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(xr[r] - m);
+      lsum += (p[0] + p[1]) + (p[2] + p[3]);
       Op4 phi, plo;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -141,8 +147,7 @@ struct MfmaEngine {
         // Slots past the sequence end may hold anything (NaN included):
         // zero them so that 0 * slot cannot poison the product.
         const int nv = valid - 4 * grp;  // valid tokens among this lane's 4
-        const uint32_t lo_keep = nv >= 1 ? 0x0000ffffu : 0u;
-        const uint32_t lo_mask = lo_keep | (nv >= 2 ? 0xffff0000u : 0u);
+        const uint32_t lo_mask = (nv >= 1 ? 0x0000ffffu : 0u) | (nv >= 2 ? 0xffff0000u : 0u);
         const uint32_t hi_mask = (nv >= 3 ? 0x0000ffffu : 0u) | (nv >= 4 ? 0xffff0000u : 0u);
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
@@ -157,24 +162,35 @@ struct MfmaEngine {
       }
     };
 
-    // Two sub-tiles in flight per wave: while one is consumed the next is loading.
-    Tile ta, tb;
-    int i = wave;
-    if (i < nsub) load(i, ta);
-    if (i + kWaves < nsub) load(i + kWaves, tb);
-    while (i < nsub) {
-      compute(ta, i);
-      if (i + 2 * kWaves < nsub) load(i + 2 * kWaves, ta);
-      i += kWaves;
-      if (i >= nsub) break;
-      compute(tb, i);
-      if (i + 2 * kWaves < nsub) load(i + 2 * kWaves, tb);
-      i += kWaves;
+    // Streaming loop, two sub-tiles in flight per wave.  Every iteration
+    // issues its prefetch unconditionally (past the wave's last sub-tile the
+    // index is clamped to it, a harmless re-read), so the compiler can wait
+    // for exactly the older tile instead of draining every outstanding load;
+    // the table entry for the load after next is fetched one step early.
+    if (wave < nsub) {
+      const int last = wave + kWaves * ((nsub - 1 - wave) / kWaves);
+      Tile ta, tb;
+      int i = wave;
+      load(i, phys_of(i), ta);
+      load(min(i + kWaves, last), phys_of(min(i + kWaves, last)), tb);
+      int pn = phys_of(min(i + 2 * kWaves, last));
+      while (true) {
+        compute(ta, i);
+        load(min(i + 2 * kWaves, last), pn, ta);
+        pn = phys_of(min(i + 3 * kWaves, last));
+        i += kWaves;
+        if (i > last) break;
+        compute(tb, i);
+        load(min(i + 2 * kWaves, last), pn, tb);
+        pn = phys_of(min(i + 3 * kWaves, last));
+        i += kWaves;
+        if (i > last) break;
+      }
     }
 
     // Wave partial -> LDS: lsum summed over the 4 row groups of each column.
-    lsum += xor_lanes(lsum, 16);
-    lsum += xor_lanes(lsum, 32);
+    lsum = sum_xor16(lsum);
+    lsum = sum_xor32(lsum);
     if (col < G) {
 #pragma unroll
       for (int x = 0; x < 8; ++x)
@@ -185,7 +201,7 @@ struct MfmaEngine {
       }
     }
     __syncthreads();
-    emit_piece<T, G>(a, sm, b, kvh, complete, slot);
+    emit_piece<T, G>(a, sm, pc);
     __syncthreads();
   }
 };

@@ -11,9 +11,9 @@
 // the RL partial sums of a row are then summed by DPP row moves (and one
 // cross-row exchange for fp32), leaving the token's score in all RL lanes.
 //
-// Weighted values.  The V sub-tile is dim-major (tokens of one value
-// dimension contiguous): each 16-byte chunk holds E consecutive tokens of
-// one dimension.  The probabilities of the sub-tile go through a 16-float
+// Weighted values.  The V group of the sub-tile is stored transposed
+// (its 16 tokens of one value dimension contiguous): each 16-byte chunk
+// holds E consecutive tokens of one dimension.  The probabilities of the sub-tile go through a 16-float
 // per-wave LDS line so every lane can read the E it needs; each lane then
 // accumulates o[dim] += sum_e p_e v_e for its dimensions, and the RV lanes
 // sharing a dimension are summed once at the end of the piece.
@@ -49,12 +49,12 @@ struct ValuEngine {
 
   static __device__ __forceinline__ float row_sum(float x) {
     x = row16_sum(x);
-    if constexpr (RL == 32) x += xor_lanes(x, 16);
+    if constexpr (RL == 32) x = sum_xor16(x);
     return x;
   }
 
-  static __device__ void piece(const Args& a, Smem& sm, int b, int kvh, int j0, int j1, int L,
-                               bool complete, int slot) {
+  static __device__ void piece(const Args& a, Smem& sm, const Piece& pc) {
+    const int b = pc.b, kvh = pc.kvh, j0 = pc.j0, j1 = pc.j1, L = pc.L;
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
     const int rlane = lane % RL;  // position inside a K row
@@ -75,24 +75,23 @@ struct ValuEngine {
     const int tok_begin = j0 * B;
     const int tok_end = min(j1 * B, L);
     const int nsub = (tok_end - tok_begin + kSub - 1) / kSub;
-    const int32_t* __restrict__ row = a.bt + (int64_t)b * a.mbs;
-    const char* __restrict__ kbase = static_cast<const char*>(a.kp);
-    const char* __restrict__ vbase = static_cast<const char*>(a.vp);
+    const const_i32_ptr row = as_constant(a.bt + (int64_t)b * a.mbs);
 
-    auto load = [&](int i, Tile& t) {
-      const int tok = tok_begin + kSub * i;
-      const int j = tok / B;
-      const int s16 = tok - j * B;
-      const int phys = uniform(row[j]);
-      const int64_t tile = ((int64_t)phys * a.Hkv + kvh) * (int64_t)(B * kD) * T::kEsize;
-      const char* kp = kbase + tile + ((int64_t)s16 * kD + lane / RL * kD + rlane * E) * T::kEsize;
+    auto phys_of = [&](int i) { return row[(tok_begin + kSub * i) / B]; };
+    constexpr int kTileBytes = B * kD * T::kEsize;
+    const int koff = ((lane / RL) * kD + rlane * E) * T::kEsize;  // K bytes of load 0
+    const int voff = ((lane / RV) * kSub + vlane * E) * T::kEsize;  // V bytes of load 0
+    auto load = [&](int i, int phys, Tile& t) {
+      const int s16 = (tok_begin + kSub * i) % B;
+      const int64_t tile = ((int64_t)phys * a.Hkv + kvh) * kTileBytes;
+      const auto rk = tile_rsrc(a.kp, tile, kTileBytes);
+      const auto rv = tile_rsrc(a.vp, tile, kTileBytes);
 #pragma unroll
       for (int n = 0; n < NK; ++n)
-        t.k[n] = *reinterpret_cast<const uint4*>(kp + (int64_t)n * TPL * kD * T::kEsize);
-      const char* vp = vbase + tile + ((int64_t)(lane / RV) * B + s16 + vlane * E) * T::kEsize;
+        t.k[n] = tile_load16(rk, koff + n * TPL * kD * T::kEsize, s16 * kD * T::kEsize);
 #pragma unroll
       for (int n = 0; n < NV; ++n)
-        t.v[n] = *reinterpret_cast<const uint4*>(vp + (int64_t)n * DPL * B * T::kEsize);
+        t.v[n] = tile_load16(rv, voff + n * DPL * kSub * T::kEsize, s16 * kD * T::kEsize);
     };
 
     float acc[NV][G];
@@ -129,8 +128,8 @@ struct ValuEngine {
         float bm = x[0][g];
 #pragma unroll
         for (int n = 1; n < NK; ++n) bm = fmaxf(bm, x[n][g]);
-#pragma unroll
-        for (int msk = RL; msk < 64; msk <<= 1) bm = fmaxf(bm, xor_lanes(bm, msk));
+        if constexpr (RL == 16) bm = max_xor16(bm);
+        bm = max_xor32(bm);
         const float mn = fmaxf(m[g], bm);
         const float alpha = fast_exp2(m[g] - mn);
         m[g] = mn;
@@ -178,18 +177,27 @@ struct ValuEngine {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
-    Tile ta, tb;
-    int i = wave;
-    if (i < nsub) load(i, ta);
-    if (i + kWaves < nsub) load(i + kWaves, tb);
-    while (i < nsub) {
-      compute(ta, i);
-      if (i + 2 * kWaves < nsub) load(i + 2 * kWaves, ta);
-      i += kWaves;
-      if (i >= nsub) break;
-      compute(tb, i);
-      if (i + 2 * kWaves < nsub) load(i + 2 * kWaves, tb);
-      i += kWaves;
+    // Streaming loop as in the matrix-core engine: unconditional, clamped
+    // prefetch of the sub-tile after next; table entry fetched one step early.
+    if (wave < nsub) {
+      const int last = wave + kWaves * ((nsub - 1 - wave) / kWaves);
+      Tile ta, tb;
+      int i = wave;
+      load(i, phys_of(i), ta);
+      load(min(i + kWaves, last), phys_of(min(i + kWaves, last)), tb);
+      int pn = phys_of(min(i + 2 * kWaves, last));
+      while (true) {
+        compute(ta, i);
+        load(min(i + 2 * kWaves, last), pn, ta);
+        pn = phys_of(min(i + 3 * kWaves, last));
+        i += kWaves;
+        if (i > last) break;
+        compute(tb, i);
+        load(min(i + 2 * kWaves, last), pn, tb);
+        pn = phys_of(min(i + 3 * kWaves, last));
+        i += kWaves;
+        if (i > last) break;
+      }
     }
 
     // Sum over the RV lanes of a dimension row and over the token rows.
@@ -200,8 +208,8 @@ struct ValuEngine {
         acc[n][g] += dpp<kQuadXor1>(acc[n][g]);
         if constexpr (RV == 4) acc[n][g] += dpp<kQuadXor2>(acc[n][g]);
       }
-#pragma unroll
-      for (int msk = RL; msk < 64; msk <<= 1) lsum[g] += xor_lanes(lsum[g], msk);
+      if constexpr (RL == 16) lsum[g] = sum_xor16(lsum[g]);
+      lsum[g] = sum_xor32(lsum[g]);
     }
     if (vlane == 0) {
 #pragma unroll
@@ -217,7 +225,7 @@ struct ValuEngine {
       }
     }
     __syncthreads();
-    emit_piece<T, G>(a, sm, b, kvh, complete, slot);
+    emit_piece<T, G>(a, sm, pc);
     __syncthreads();
   }
 };

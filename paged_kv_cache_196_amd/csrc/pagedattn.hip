@@ -1,13 +1,13 @@
 // pagedattn.hip — gfx950 paged decode attention: kernels instantiation and
 // the C ABI declared in include/pagedattn.h.
 //
-// Launch structure of one call (all on the caller's stream):
-//   1. decode kernel (matrix-core or vector-ALU engine), grid = one
-//      resident wave of workgroups; each workgroup rebuilds the block-count
-//      prefix in LDS and walks its equal share of the flattened
-//      (sequence, KV head, logical block) units;
-//   2. merge kernel, one workgroup per chunk boundary; a boundary that cuts
-//      a (sequence, KV head) for the first time folds all its partials.
+// One call is one kernel launch on the caller's stream: the decode kernel
+// (matrix-core or vector-ALU engine) with a grid of one resident wave of
+// workgroups.  Each workgroup rebuilds the block-count prefix in LDS, walks
+// its equal share of the flattened (sequence, KV head, logical block) units
+// and writes `out` for every (sequence, KV head) it holds whole; the pieces
+// of a (sequence, KV head) split across workgroups meet in the workspace,
+// where the last one to finish folds them.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -28,53 +28,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
     run_decode<T, B, G, ValuEngine<T, B, G>>(a);
 }
 
-// Folds the partials of every (sequence, KV head) that chunk boundaries cut
-// (merge equation of "39 · PagedAttention", §3) and writes out = o / l.
-template <class T, int G>
-__global__ __launch_bounds__(kThreads) void merge_kernel(Args a, int B) {
-  extern __shared__ int cum[];
-  __shared__ int wsum[kWaves];
-  build_prefix(a.lens, a.S, B, cum, wsum);
-  const int W = cum[a.S] * a.Hkv;
-  if (W == 0) return;
-  const int c = (W + a.nwg - 1) / a.nwg;
-  const int k = blockIdx.x + 1;  // boundary between chunks k-1 and k
-  const int f = k * c;
-  if (f >= W) return;
-  const int b = find_seq(cum, a.S, a.Hkv, f);
-  const int nb = cum[b + 1] - cum[b];
-  const int base = cum[b] * a.Hkv;
-  const int kvh = (f - base) / nb;
-  const int j = (f - base) - kvh * nb;
-  if (j == 0) return;  // a (sequence, KV head) starts here: nothing cut
-  const int ustart = base + kvh * nb;
-  const int kfirst = ustart / c;
-  if (k != kfirst + 1) return;  // handled at the first boundary inside it
-  const int klast = (ustart + nb - 1) / c;
-  const int first_slot = 2 * kfirst + (ustart != kfirst * c ? 1 : 0);
-  for (int idx = threadIdx.x; idx < G * kD; idx += kThreads) {
-    const int g = idx / kD, d = idx % kD;
-    float M = -INFINITY;
-    for (int kk = kfirst; kk <= klast; ++kk) {
-      const int slot = kk == kfirst ? first_slot : 2 * kk;
-      M = fmaxf(M, a.ws_ml[((int64_t)slot * G + g) * 2]);
-    }
-    float o = 0.f, l = 0.f;
-    for (int kk = kfirst; kk <= klast; ++kk) {
-      const int slot = kk == kfirst ? first_slot : 2 * kk;
-      const float f2 = rescale(a.ws_ml[((int64_t)slot * G + g) * 2], M);
-      o += f2 * a.ws_o[((int64_t)slot * G + g) * kD + d];
-      l += f2 * a.ws_ml[((int64_t)slot * G + g) * 2 + 1];
-    }
-    store_out<T>(a.out, ((int64_t)b * a.Hq + kvh * G + g) * kD + d, o / l, a.out_f32);
-  }
-}
-
 // ------------------------------------------------------------ dispatch
 
 using LaunchFn = hipError_t (*)(const Args&, int grid, size_t lds, hipStream_t);
 using OccFn = int (*)(size_t lds);
-using MergeFn = hipError_t (*)(const Args&, int B, int grid, size_t lds, hipStream_t);
 
 template <class T, int B, int G, bool M>
 hipError_t launch_decode(const Args& a, int grid, size_t lds, hipStream_t st) {
@@ -91,16 +48,9 @@ int occupancy(size_t lds) {
   return n;
 }
 
-template <class T, int G>
-hipError_t launch_merge(const Args& a, int B, int grid, size_t lds, hipStream_t st) {
-  hipLaunchKernelGGL((merge_kernel<T, G>), dim3(grid), dim3(kThreads), lds, st, a, B);
-  return hipGetLastError();
-}
-
 struct Variant {
   LaunchFn launch = nullptr;
   OccFn occ = nullptr;
-  MergeFn merge = nullptr;
 };
 
 template <class T, int B, int G, bool M>
@@ -108,7 +58,6 @@ Variant make_variant() {
   Variant v;
   v.launch = &launch_decode<T, B, G, M>;
   v.occ = &occupancy<T, B, G, M>;
-  v.merge = &launch_merge<T, G>;
   return v;
 }
 
@@ -178,9 +127,13 @@ DeviceInfo device_info() {
 
 size_t prefix_lds(int S) { return (size_t)(S + 1) * sizeof(int); }
 
-size_t ws_floats(const pa_desc* d) {
+// Workspace: [kMaxGrid] int32 split counters, then the partials
+// ws_o [2*kMaxGrid][G][kD] and ws_ml [2*kMaxGrid][G][2] (fp32).
+constexpr size_t kCounterBytes = sizeof(int) * kMaxGrid;
+
+size_t ws_bytes_for(const pa_desc* d) {
   const int64_t G = d->num_q_heads / d->num_kv_heads;
-  return (size_t)(2 * kMaxGrid) * G * (kD + 2);
+  return kCounterBytes + sizeof(float) * (size_t)(2 * kMaxGrid) * G * (kD + 2);
 }
 
 }  // namespace pa
@@ -258,12 +211,13 @@ int64_t pa_v_elem_offset(const pa_desc* d, int32_t block, int32_t kv_head, int32
   if (block < 0 || block >= d->num_blocks || kv_head < 0 || kv_head >= d->num_kv_heads || slot < 0 ||
       slot >= d->block_size || dim < 0 || dim >= d->head_dim)
     return -1;
-  return (((int64_t)block * d->num_kv_heads + kv_head) * d->head_dim + dim) * d->block_size + slot;
+  const int64_t tile = ((int64_t)block * d->num_kv_heads + kv_head) * d->block_size * d->head_dim;
+  return tile + ((int64_t)(slot / kSub) * d->head_dim + dim) * kSub + slot % kSub;
 }
 
 size_t pa_workspace_bytes(const pa_desc* d) {
   if (pa_check_desc(d) != PA_OK) return 0;
-  return ws_floats(d) * sizeof(float);
+  return ws_bytes_for(d);
 }
 
 int32_t pa_validate_host(const pa_desc* d, const int32_t* bt, const int32_t* lens) {
@@ -314,8 +268,9 @@ static int32_t prepare(const void* q, const void* k_pool, const void* v_pool, co
   a->bt = bt;
   a->lens = lens;
   a->out = out;
-  a->ws_o = static_cast<float*>(ws);
-  a->ws_ml = static_cast<float*>(ws) + (size_t)(2 * kMaxGrid) * G * kD;
+  a->counters = static_cast<int*>(ws);
+  a->ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
+  a->ws_ml = a->ws_o + (size_t)(2 * kMaxGrid) * G * kD;
   a->scale_log2 = scale * kLog2e;
   a->S = d->num_seqs;
   a->Hq = d->num_q_heads;
@@ -327,9 +282,9 @@ static int32_t prepare(const void* q, const void* k_pool, const void* v_pool, co
   return PA_OK;
 }
 
-int32_t pa_decode_partitions(const void* q, const void* k_pool, const void* v_pool,
-                             const int32_t* bt, const int32_t* lens, float scale, void* out,
-                             const pa_desc* d, void* ws, size_t ws_bytes, void* stream) {
+int32_t paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* bt, const int32_t* lens, float scale, void* out,
+                          const pa_desc* d, void* ws, size_t ws_bytes, void* stream) {
   Args a;
   int grid = 0;
   const int32_t st = prepare(q, k_pool, v_pool, bt, lens, scale, out, d, ws, ws_bytes, &a, &grid);
@@ -338,44 +293,6 @@ int32_t pa_decode_partitions(const void* q, const void* k_pool, const void* v_po
   if (v.launch(a, grid, prefix_lds(a.S), static_cast<hipStream_t>(stream)) != hipSuccess)
     return PA_ERR_LAUNCH;
   return PA_OK;
-}
-
-int32_t pa_merge_partitions(const int32_t* lens, void* out, const pa_desc* d, void* ws,
-                            size_t ws_bytes, void* stream) {
-  const int32_t st = pa_check_desc(d);
-  if (st != PA_OK) return st;
-  if (d->num_seqs == 0) return PA_OK;
-  if (!lens || !out) return PA_ERR_NULL;
-  if ((uintptr_t)out & 15u) return PA_ERR_ALIGN;
-  if (!ws || ws_bytes < pa_workspace_bytes(d) || ((uintptr_t)ws & 15u)) return PA_ERR_WORKSPACE;
-  const int g = pa_decode_grid(d);
-  if (g <= 0) return PA_ERR_DEVICE;
-  if (g < 2) return PA_OK;
-  const int G = d->num_q_heads / d->num_kv_heads;
-  Args a;
-  memset(&a, 0, sizeof a);
-  a.lens = lens;
-  a.out = out;
-  a.ws_o = static_cast<float*>(ws);
-  a.ws_ml = static_cast<float*>(ws) + (size_t)(2 * kMaxGrid) * G * kD;
-  a.S = d->num_seqs;
-  a.Hq = d->num_q_heads;
-  a.Hkv = d->num_kv_heads;
-  a.mbs = d->max_blocks_per_seq;
-  a.nwg = g;
-  a.out_f32 = d->out_dtype == PA_F32 ? 1 : 0;
-  const Variant v = pick(d);
-  if (v.merge(a, d->block_size, g - 1, prefix_lds(a.S), static_cast<hipStream_t>(stream)) != hipSuccess)
-    return PA_ERR_LAUNCH;
-  return PA_OK;
-}
-
-int32_t paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
-                          const int32_t* bt, const int32_t* lens, float scale, void* out,
-                          const pa_desc* d, void* ws, size_t ws_bytes, void* stream) {
-  const int32_t st = pa_decode_partitions(q, k_pool, v_pool, bt, lens, scale, out, d, ws, ws_bytes, stream);
-  if (st != PA_OK) return st;
-  return pa_merge_partitions(lens, out, d, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -29,19 +29,25 @@ def _golden(name):
 # Written independently of the oracle: numpy fancy indexing instead of the
 # oracle's per-token loops.
 
+def vgroup(B):
+    """Tokens per transposed V group: 16 when B is a multiple of 16, else B."""
+    return 16 if B % 16 == 0 else B
+
+
 def scatter(Klog, Vlog, tables, lens, num_blocks, B, fill=np.nan):
     """Place logical fp64 K/V [S][Hkv][Lmax][D] into pools of the library
-    layout: K [NB][Hkv][B][D], V [NB][Hkv][D][B]; untouched slots = fill."""
+    layout: K [NB][Hkv][B][D], V [NB][Hkv][B/G][D][G]; untouched slots = fill."""
     S, H, _, D = Klog.shape
+    Gv = vgroup(B)
     kp = np.full((num_blocks, H, B, D), fill)
-    vp = np.full((num_blocks, H, D, B), fill)
+    vp = np.full((num_blocks, H, B // Gv, D, Gv), fill)
     for b in range(S):
         t = np.arange(int(lens[b]))
         phys = np.asarray(tables[b])[t // B]
         slot = t % B
         for g in range(H):
             kp[phys, g, slot, :] = Klog[b, g, : t.size]
-            vp[phys, g, :, slot] = Vlog[b, g, : t.size]
+            vp[phys, g, slot // Gv, :, slot % Gv] = Vlog[b, g, : t.size]
     return kp, vp
 
 
@@ -67,9 +73,10 @@ def numpy_reference(q, kp, vp, bt, lens, scale, Hkv, B):
             continue
         t = np.arange(L)
         phys, slot = bt[b, t // B], t % B
+        Gv = vgroup(B)
         for h in range(Hq):
             K = kp[phys, h // G, slot, :]
-            V = vp[phys, h // G, :, slot]
+            V = vp[phys, h // G, slot // Gv, :, slot % Gv]
             s = scale * (K @ q[b, h])
             w = np.exp(s - s.max())
             out[b, h] = (w / w.sum()) @ V
@@ -158,11 +165,11 @@ def pin_worked_example_walk(O):
     B, L, table = fx["block_size"], fx["num_tokens"], fx["block_table"]
     NB, D = 16, 2
     kp = np.full((NB, 1, B, D), np.nan, np.float32)
-    vp = np.full((NB, 1, D, B), np.nan, np.float32)
+    vp = np.full((NB, 1, B // 16, D, 16), np.nan, np.float32)
     for p in range(NB):
         for s in range(B):
             kp[p, 0, s] = [p, s]          # K row encodes (physical block, slot)
-            vp[p, 0, :, s] = [-p, -s]
+            vp[p, 0, s // 16, :, s % 16] = [-p, -s]
     bt = np.array([table], np.int32)
     K, V = O.gather(kp, vp, bt, 0, 0, L, num_kv_heads=1, head_dim=D, block_size=B, dtype="f32")
     t = 0
@@ -240,23 +247,23 @@ def pin_two_tokens_by_hand(O):
     s0, s1 = c * q * k0, c * q * k1
     want = (v0 * math.exp(s0) + v1 * math.exp(s1)) / (math.exp(s0) + math.exp(s1))
     kp = np.full((3, 1, 2, 1), np.nan)
-    vp = np.full((3, 1, 1, 2), np.nan)
+    vp = np.full((3, 1, 1, 1, 2), np.nan)
     kp[2, 0, 0, 0], kp[2, 0, 1, 0] = k0, k1
-    vp[2, 0, 0, 0], vp[2, 0, 0, 1] = v0, v1
+    vp[2, 0, 0, 0, 0], vp[2, 0, 0, 0, 1] = v0, v1
     out = decode_f64(O, [[[q]]], kp, vp, np.array([[2]], np.int32), [2], c, 1, 2)
     assert abs(out[0, 0, 0] - want) < 1e-15
 
 
 def pin_empty_sequence_is_zero(O):
     kp = np.full((2, 1, 4, 3), np.nan)
-    vp = np.full((2, 1, 3, 4), np.nan)
+    vp = np.full((2, 1, 1, 3, 4), np.nan)
     out = decode_f64(O, np.ones((1, 1, 3)), kp, vp, np.array([[-1]], np.int32), [0], 1.0, 1, 4)
     assert np.array_equal(out, np.zeros((1, 1, 3)))
 
 
 def pin_table_out_of_range_is_an_error(O):
     kp = np.zeros((2, 1, 4, 3))
-    vp = np.zeros((2, 1, 3, 4))
+    vp = np.zeros((2, 1, 1, 3, 4))
     try:
         decode_f64(O, np.ones((1, 1, 3)), kp, vp, np.array([[2]], np.int32), [3], 1.0, 1, 4)
     except ValueError:

@@ -147,17 +147,29 @@ def test_repeat_runs_are_bitwise_identical():
         assert torch.equal(r1, r2), kern
 
 
-def test_split_entry_points_equal_whole_call():
+@pytest.mark.parametrize("cfg,batch,max_len", [(4, 2, 8192), (3, 8, 4000), (5, 40, None)])
+def test_reused_workspace_folds_every_split(O, cfg, batch, max_len):
+    """One workspace for many calls: each call must find its split counters
+    at zero and leave them so.  `out` is NaN-filled before every call, so a
+    split whose fold did not run (or ran twice on stale partials) shows up.
+    Every repeat must equal the first bitwise and match the oracle."""
     import paged_kv_cache_196_amd as pa
-    w = workload.make(4, 14, batch=2, max_len=4096)
+    w = workload.make(cfg, 15, batch=batch, max_len=max_len)
+    ref = O.run_workload(w)
     up = Uploaded(w)
-    whole = up.run("mfma")
-    desc = pa.make_desc(up.q, up.k, up.bt, kernel=pa.PA_KERNEL_MFMA)
-    nbytes = pa.pa_workspace_bytes(desc)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    out = torch.empty_like(whole)
-    st = torch.cuda.current_stream().cuda_stream
-    pa.pa_decode_partitions(up.q, up.k, up.v, up.bt, up.lens, float(w.scale), out, desc, ws, nbytes, st)
-    pa.pa_merge_partitions(up.lens, out, desc, ws, nbytes, st)
-    torch.cuda.synchronize()
-    assert torch.equal(out, whole)
+    for kern in kernels_for(w.dtype):
+        k = pa.PA_KERNEL_VALU if kern == "valu" else pa.PA_KERNEL_MFMA
+        desc = pa.make_desc(up.q, up.k, up.bt, kernel=k)
+        ws = pa.new_workspace(desc, "cuda")
+        out = torch.empty(up.q.shape, dtype=torch.float32, device="cuda")
+        first = None
+        for rep in range(12):
+            out.fill_(float("nan"))
+            pa.decode(up.q, up.k, up.v, up.bt, up.lens, float(w.scale), out=out, kernel=k,
+                      workspace=ws)
+            torch.cuda.synchronize()
+            if first is None:
+                first = out.clone()
+                assert max_err(out, ref) <= TOL[w.dtype], kern
+            else:
+                assert torch.equal(out, first), (kern, rep)

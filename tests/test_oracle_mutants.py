@@ -13,8 +13,11 @@ MUTANTS = [
     ("no_normalisation", "const double w = s[t] / z;", "const double w = s[t];"),
     ("scale_dropped", "s[t] = scale * dot;", "s[t] = dot;"),
     ("strided_gqa_mapping", "const int64_t h = g * G + k;", "const int64_t h = k * num_kv_heads + g;"),
-    ("v_read_token_major", "V[t * D + d] = elem(v_pool, dtype, tile + d * B + slot);",
+    ("v_read_token_major", "V[t * D + d] = elem(v_pool, dtype, tile + (slot / S) * D * S + d * S + slot % S);",
      "V[t * D + d] = elem(v_pool, dtype, tile + slot * D + d);"),
+    ("v_groups_ignored", "V[t * D + d] = elem(v_pool, dtype, tile + (slot / S) * D * S + d * S + slot % S);",
+     "V[t * D + d] = elem(v_pool, dtype, tile + d * B + slot);"),
+    ("v_group_size_wrong", "const int64_t S = (B % 16 == 0) ? 16 : B;", "const int64_t S = (B % 32 == 0) ? 32 : B;"),
     ("k_read_dim_major", "K[t * D + d] = elem(k_pool, dtype, tile + slot * D + d);",
      "K[t * D + d] = elem(k_pool, dtype, tile + d * B + slot);"),
     ("slot_off_by_one", "const int64_t slot = t % B;", "const int64_t slot = (t + 1) % B;"),

@@ -8,7 +8,8 @@ gfx950 library consume what it produces.
 Storage layouts produced (element = one value of the config dtype):
     q        [S][Hq][D]
     k_pool   [num_blocks][Hkv][B][D]     token-major tile
-    v_pool   [num_blocks][Hkv][D][B]     dim-major tile
+    v_pool   [num_blocks][Hkv][B/16][D][16]   value rows transposed within
+                                              each group of 16 tokens
     tables   int32 [S][max_blocks_per_seq], -1 in unused entries
     seq_lens int32 [S]
 fp16 data is numpy float16; bf16 data is the raw bits as uint16; fp32 is
@@ -62,7 +63,7 @@ class Workload:
     block_tables: np.ndarray  # int32 [S][max_blocks_per_seq]
     q: np.ndarray             # [S][Hq][D]
     k_pool: np.ndarray        # [NB][Hkv][B][D]
-    v_pool: np.ndarray        # [NB][Hkv][D][B]
+    v_pool: np.ndarray        # [NB][Hkv][B/16][D][16]
     scale: np.float32
     seed: int = 0
 
@@ -184,8 +185,10 @@ def build(*, name: str, dtype: str, seq_lens, num_q_heads: int, num_kv_heads: in
     ref = np.nonzero(valid)[0]
 
     Hkv, D = num_kv_heads, head_dim
+    assert B % 16 == 0, "the library's V layout groups tokens by 16"
+    NG = B // 16
     k_pool = _empty_pool((num_blocks, Hkv, B, D), dtype)
-    v_pool = _empty_pool((num_blocks, Hkv, D, B), dtype)
+    v_pool = _empty_pool((num_blocks, Hkv, NG, D, 16), dtype)
     kscale = None if k_head_scale is None else np.asarray(k_head_scale, np.float32).reshape(1, Hkv, 1, 1)
     for c0 in range(0, ref.shape[0], chunk_blocks):
         sel = ref[c0: c0 + chunk_blocks]
@@ -193,12 +196,13 @@ def build(*, name: str, dtype: str, seq_lens, num_q_heads: int, num_kv_heads: in
         if kscale is not None:
             kv *= kscale
         k_pool[sel] = round_to(kv, dtype).reshape(kv.shape).view(k_pool.dtype)
-        vv = rng_v.standard_normal((sel.shape[0], Hkv, D, B), dtype=np.float32)
+        vv = rng_v.standard_normal((sel.shape[0], Hkv, NG, D, 16), dtype=np.float32)
         v_pool[sel] = round_to(vv, dtype).reshape(vv.shape).view(v_pool.dtype)
     nanv = _nan_value(dtype)
     for p in np.nonzero((valid > 0) & (valid < B))[0]:
         k_pool[p, :, valid[p]:, :] = nanv
-        v_pool[p, :, :, valid[p]:] = nanv
+        for slot in range(int(valid[p]), B):
+            v_pool[p, :, slot // 16, :, slot % 16] = nanv
 
     qf = rng_q.standard_normal((S, num_q_heads, D), dtype=np.float32)
     q = round_to(qf, dtype).reshape(qf.shape)
