@@ -77,13 +77,89 @@ def read_traffic(src_hash: str, kernel_name: str, workload_name: str):
     return t.get("hbm_bytes_per_launch")
 
 
+COPY_BYTES = 512 << 20  # calibration copy: reads and writes this many bytes per launch
+
+
+def copy_calibration(launches: int = 5) -> int:
+    """A plain elementwise copy (out = src * 1) of COPY_BYTES, `launches`
+    times: the reference that FETCH_SIZE / WRITE_SIZE are scaled by."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(launches):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "launches": launches}), flush=True)
+    return 0
+
+
+def _counter_rows(path: str):
+    """(kernel name, counter name, value) rows of rocprofv3 counter CSVs
+    found under `path`."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                rows.append((r.get("Kernel_Name", ""), r.get("Counter_Name", ""),
+                             float(r.get("Counter_Value", "nan"))))
+    return rows
+
+
+def _mean_counter(rows, counter: str, name_part: str) -> float:
+    vals = [v for k, c, v in rows if c == counter and name_part in k]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernels matching {name_part!r}")
+    return sum(vals) / len(vals)
+
+
+def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, workload_id, kernel):
+    """Turns four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE, each on
+    this benchmark and on the calibration copy) into HBM bytes per decode
+    launch, scaled by the copy's known bytes, and writes TRAFFIC_FILE."""
+    import workload as wl
+    w = wl.make(workload_id)
+    use_mfma = kernel == "mfma" or (kernel == "auto" and w.dtype != "f32")
+    kname = f"decode_kernel<{w.dtype},B{w.block_size},G{w.group},{'mfma' if use_mfma else 'valu'}>"
+    kib = 1024.0
+    dec_fetch = _mean_counter(_counter_rows(fetch_dir), "FETCH_SIZE", "decode_kernel") * kib
+    dec_write = _mean_counter(_counter_rows(write_dir), "WRITE_SIZE", "decode_kernel") * kib
+    cp_fetch = _mean_counter(_counter_rows(copy_fetch_dir), "FETCH_SIZE", "Mul") * kib
+    cp_write = _mean_counter(_counter_rows(copy_write_dir), "WRITE_SIZE", "Mul") * kib
+    f_fetch = COPY_BYTES / cp_fetch
+    f_write = COPY_BYTES / cp_write
+    alg = algorithmic_bytes(w, wl.kv_bytes(w, unique=True))
+    hbm = dec_fetch * f_fetch + dec_write * f_write
+    out = {
+        "kernel": kname,
+        "workload": w.name,
+        "source_hash": kernel_source_hash(),
+        "hbm_bytes_per_launch": round(hbm),
+        "read_bytes_per_launch": round(dec_fetch * f_fetch),
+        "write_bytes_per_launch": round(dec_write * f_write),
+        "raw_fetch_size_bytes": round(dec_fetch),
+        "raw_write_size_bytes": round(dec_write),
+        "copy_calibration": {"bytes": COPY_BYTES, "fetch_counter_bytes": round(cp_fetch),
+                             "write_counter_bytes": round(cp_write),
+                             "fetch_scale": round(f_fetch, 4), "write_scale": round(f_write, 4)},
+        "algorithmic_bytes_per_launch": alg["total"],
+        "traffic_over_algorithmic": round(hbm / alg["total"], 4),
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def cpu_baseline(w, kv_bytes: int, budget_s: float) -> dict:
     import oracle
     O = oracle.load()
     threads = len(os.sched_getaffinity(0))
     times = []
     t_all = time.perf_counter()
-    while len(times) < 3 or (time.perf_counter() - t_all < budget_s and len(times) < 50):
+    while len(times) < 3 or (time.perf_counter() - t_all < budget_s and len(times) < 500):
         t0 = time.perf_counter()
         O.run_workload(w, num_threads=threads)
         times.append(time.perf_counter() - t0)
@@ -124,7 +200,16 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the oracle spot check")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only the calibration copy (for rocprofv3 counter scaling)")
+    ap.add_argument("--summarize-counters", nargs=4, metavar="DIR",
+                    help="FETCH_SIZE run, WRITE_SIZE run, copy FETCH_SIZE run, copy WRITE_SIZE run")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        return summarize_counters(*args.summarize_counters, args.workload, args.kernel)
+    if args.copy_calibration:
+        return copy_calibration()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -273,11 +273,17 @@ def make(cfg: int, seed: int | None = None, *, batch: int | None = None,
     raise ValueError(f"unknown config {cfg}")
 
 
+def kv_bytes_per_token(num_kv_heads: int, head_dim: int, esize: int, layers: int = 1) -> int:
+    """K and V bytes one token occupies: 2 x KV heads x head dim x layers x
+    element bytes ("PagedAttention: The Cache Was Storing Nothing", §3)."""
+    return 2 * num_kv_heads * head_dim * layers * esize
+
+
 def kv_bytes(w: Workload, unique: bool = False) -> int:
     """K+V bytes the attended tokens occupy: 2 * L * D * esize per
     (sequence, KV head), summed.  unique=True counts each physical
     (block, slot) once, so shared prefix blocks are counted once."""
-    per_token = 2 * w.num_kv_heads * w.head_dim * w.esize
+    per_token = kv_bytes_per_token(w.num_kv_heads, w.head_dim, w.esize)
     if not unique:
         return int(w.seq_lens.astype(np.int64).sum()) * per_token
     B = w.block_size
