@@ -42,6 +42,7 @@ struct MfmaEngine {
   static_assert(B % kSub == 0, "block size must be a multiple of 16");
 
   using Smem = MergeSmem<G>;
+  static constexpr int kDepth = 2;  // sub-tiles in flight per wave
   using Op8 = typename std::conditional<T::kCode == BF16::kCode, bf16x8, f16x8>::type;
   using Op4 = typename std::conditional<T::kCode == BF16::kCode, bf16x4, f16x4>::type;
   using Elem = typename std::conditional<T::kCode == BF16::kCode, __bf16, _Float16>::type;
@@ -162,31 +163,11 @@ struct MfmaEngine {
       }
     };
 
-    // Streaming loop, two sub-tiles in flight per wave.  Every iteration
-    // issues its prefetch unconditionally (past the wave's last sub-tile the
-    // index is clamped to it, a harmless re-read), so the compiler can wait
-    // for exactly the older tile instead of draining every outstanding load;
-    // the table entry for the load after next is fetched one step early.
-    if (wave < nsub) {
-      const int last = wave + kWaves * ((nsub - 1 - wave) / kWaves);
-      Tile ta, tb;
-      int i = wave;
-      load(i, phys_of(i), ta);
-      load(min(i + kWaves, last), phys_of(min(i + kWaves, last)), tb);
-      int pn = phys_of(min(i + 2 * kWaves, last));
-      while (true) {
-        compute(ta, i);
-        load(min(i + 2 * kWaves, last), pn, ta);
-        pn = phys_of(min(i + 3 * kWaves, last));
-        i += kWaves;
-        if (i > last) break;
-        compute(tb, i);
-        load(min(i + 2 * kWaves, last), pn, tb);
-        pn = phys_of(min(i + 3 * kWaves, last));
-        i += kWaves;
-        if (i > last) break;
-      }
-    }
+    if (wave < nsub)
+      stream_subtiles<kDepth, Tile>(
+          wave, wave + kWaves * ((nsub - 1 - wave) / kWaves), phys_of, load, compute, [&](int i) {
+            set_priority_for_progress(pc.done_before + (kSub * i) / B, pc.chunk_len);
+          });
 
     // Wave partial -> LDS: lsum summed over the 4 row groups of each column.
     lsum = sum_xor16(lsum);

@@ -38,6 +38,8 @@ struct ValuEngine {
   static constexpr int NV = kD * RV / 64;   // V loads per lane per sub-tile
   static constexpr int DPL = 64 / RV;       // dimensions per V load
 
+  static constexpr int kDepth = 2;  // sub-tiles in flight per wave
+
   struct Smem : MergeSmem<G> {
     float p[kWaves][G][kSub];
   };
@@ -177,28 +179,11 @@ struct ValuEngine {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
-    // Streaming loop as in the matrix-core engine: unconditional, clamped
-    // prefetch of the sub-tile after next; table entry fetched one step early.
-    if (wave < nsub) {
-      const int last = wave + kWaves * ((nsub - 1 - wave) / kWaves);
-      Tile ta, tb;
-      int i = wave;
-      load(i, phys_of(i), ta);
-      load(min(i + kWaves, last), phys_of(min(i + kWaves, last)), tb);
-      int pn = phys_of(min(i + 2 * kWaves, last));
-      while (true) {
-        compute(ta, i);
-        load(min(i + 2 * kWaves, last), pn, ta);
-        pn = phys_of(min(i + 3 * kWaves, last));
-        i += kWaves;
-        if (i > last) break;
-        compute(tb, i);
-        load(min(i + 2 * kWaves, last), pn, tb);
-        pn = phys_of(min(i + 3 * kWaves, last));
-        i += kWaves;
-        if (i > last) break;
-      }
-    }
+    if (wave < nsub)
+      stream_subtiles<kDepth, Tile>(
+          wave, wave + kWaves * ((nsub - 1 - wave) / kWaves), phys_of, load, compute, [&](int i) {
+            set_priority_for_progress(pc.done_before + (kSub * i) / B, pc.chunk_len);
+          });
 
     // Sum over the RV lanes of a dimension row and over the token rows.
 #pragma unroll

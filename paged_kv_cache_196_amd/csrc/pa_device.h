@@ -169,6 +169,40 @@ __device__ __forceinline__ uint2 tile_load8(__amdgpu_buffer_rsrc_t r, int voff, 
   return make_uint2(v.x, v.y);
 }
 
+// Streaming loop of one wave over its sub-tiles first, first + kWaves, ...,
+// last, with kDepth sub-tiles in flight.  Every step issues its prefetch
+// unconditionally (past `last` the index is clamped to it, a harmless
+// re-read), so the compiler waits for exactly the oldest tile instead of
+// draining every outstanding load; the table entry of the load after next
+// is fetched (scalar load) one step early.
+template <int kDepth, class Tile, class PhysFn, class LoadFn, class ComputeFn, class ProgressFn>
+__device__ __forceinline__ void stream_subtiles(int first, int last, PhysFn phys_of, LoadFn load,
+                                                ComputeFn compute, ProgressFn progress) {
+  static_assert(kDepth >= 1 && kDepth <= 4, "prefetch depth");
+  Tile t[kDepth];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) {
+    const int j = min(first + d * kWaves, last);
+    load(j, phys_of(j), t[d]);
+  }
+  int pn = phys_of(min(first + kDepth * kWaves, last));
+  int i = first;
+  auto step = [&](Tile& tile) -> bool {
+    progress(i);
+    compute(tile, i);
+    load(min(i + kDepth * kWaves, last), pn, tile);
+    pn = phys_of(min(i + (kDepth + 1) * kWaves, last));
+    i += kWaves;
+    return i > last;
+  };
+  while (true) {
+    if (step(t[0])) break;
+    if constexpr (kDepth > 1) { if (step(t[1])) break; }
+    if constexpr (kDepth > 2) { if (step(t[2])) break; }
+    if constexpr (kDepth > 3) { if (step(t[3])) break; }
+  }
+}
+
 // True in every lane when any lane of the wave has `pred` set.
 __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 
@@ -299,7 +333,23 @@ struct Piece {
   int b, kvh, j0, j1, L;
   bool complete;
   int slot, kfirst, npieces, first_slot;
+  int done_before;  // units of the chunk finished before this piece
+  int chunk_len;    // units in the chunk
 };
+
+// Issue priority from a workgroup's progress through its chunk.  Two or more
+// workgroups share a CU, and the older one's waves win arbitration; left
+// alone, the first workgroup on every CU finished its (equal) chunk in ~60 %
+// of the time of the second, which then streamed with half the CU's loads
+// in flight.  Waves that are further behind get the higher priority, so the
+// co-resident workgroups progress together.
+__device__ __forceinline__ void set_priority_for_progress(int done, int total) {
+  const int q = (4 * done) / max(total, 1);
+  if (q <= 0) __builtin_amdgcn_s_setprio(3);
+  else if (q == 1) __builtin_amdgcn_s_setprio(2);
+  else if (q == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
 
 // Folds the npieces partials of a split (sequence, KV head) from the
 // workspace and writes out = o / l.  All threads of the workgroup call.
@@ -462,6 +512,8 @@ __device__ inline void run_decode(const Args& a) {
     pc.kfirst = ustart / c;
     pc.npieces = (ustart + nb - 1) / c - pc.kfirst + 1;
     pc.first_slot = 2 * pc.kfirst + (ustart != pc.kfirst * c ? 1 : 0);
+    pc.done_before = f - s;
+    pc.chunk_len = e - s;
     Engine::piece(a, sm, pc);
     f = pe;
   }
