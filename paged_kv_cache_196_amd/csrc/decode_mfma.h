@@ -1,8 +1,8 @@
 // decode_mfma.h — decode engine on the gfx950 matrix cores (fp16 / bf16).
 //
-// One workgroup piece = logical blocks [j0, j1) of one (sequence b, KV head).
-// Its tokens are streamed in 16-token sub-tiles; wave w of the workgroup
-// takes sub-tiles w, w+4, w+8, ... and keeps its own online-softmax state.
+// The driver (pa_device.h) streams 16-token sub-tiles of each piece (tokens
+// of one (sequence b, KV head)); this engine loads a sub-tile and folds it
+// into a wave's online-softmax state.
 //
 // Per sub-tile the query group of the KV head (G heads, padded to 16 MFMA
 // columns) meets the 16 keys as a dense tile:
@@ -41,15 +41,23 @@ struct MfmaEngine {
   static_assert(G >= 1 && G <= 16, "query group padded to 16 MFMA columns");
   static_assert(B % kSub == 0, "block size must be a multiple of 16");
 
-  using Smem = MergeSmem<G>;
-  static constexpr int kDepth = 2;  // sub-tiles in flight per wave
+  using Smem = MergeSmem<T, G>;
   using Op8 = typename std::conditional<T::kCode == BF16::kCode, bf16x8, f16x8>::type;
   using Op4 = typename std::conditional<T::kCode == BF16::kCode, bf16x4, f16x4>::type;
   using Elem = typename std::conditional<T::kCode == BF16::kCode, __bf16, _Float16>::type;
+  static constexpr int kTileBytes = B * kD * 2;
 
   struct Tile {
     uint4 k[4];  // K rows: token `col`, dims 32x + 8grp .. +8   (x = 0..3)
     uint2 v[8];  // V^T: dim 16x + col, tokens 4grp .. 4grp+3   (x = 0..7)
+  };
+  struct Query {
+    uint4 op[4];  // B operand of the score product: head `col`, dims 32x + 8grp .. +8
+  };
+  struct State {
+    f32x4 acc[8];  // O^T tile x: dims 16x + 4grp .. +4 of head `col`
+    float m;       // running max of head `col` (base-2 units)
+    float lsum;    // this lane's share of the running sum of 2^(s - m)
   };
 
   static __device__ __forceinline__ f32x4 mma_qk(const uint4& k, const uint4& q, f32x4 c) {
@@ -69,121 +77,105 @@ struct MfmaEngine {
       return __builtin_amdgcn_mfma_f32_16x16x16f16(a, p, c, 0, 0, 0);
   }
 
-  static __device__ void piece(const Args& a, Smem& sm, const Piece& pc) {
-    const int b = pc.b, kvh = pc.kvh, j0 = pc.j0, j1 = pc.j1, L = pc.L;
-    const int lane = threadIdx.x & 63;
-    const int wave = uniform(threadIdx.x >> 6);
-    const int col = lane & 15;
-    const int grp = lane >> 4;
-
-    // Query group as the B operand of the score product (zero columns >= G).
-    uint4 qop[4];
-    {
-      const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                           ((int64_t)b * a.Hq + (int64_t)kvh * G + col) * kD + 8 * grp;
+  static __device__ __forceinline__ void reset(State& st) {
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
-        qop[x] = col < G ? *reinterpret_cast<const uint4*>(qp + 32 * x) : make_uint4(0, 0, 0, 0);
-    }
+    for (int x = 0; x < 8; ++x) st.acc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m = -INFINITY;
+    st.lsum = 0.f;
+  }
 
-    const int tok_begin = j0 * B;
-    const int tok_end = min(j1 * B, L);
-    const int nsub = (tok_end - tok_begin + kSub - 1) / kSub;
-    const const_i32_ptr row = as_constant(a.bt + (int64_t)b * a.mbs);
+  // Query group of piece p from its LDS staging (zero columns >= G).
+  static __device__ __forceinline__ void load_query(const Smem& sm, int p, Query& q) {
+    const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+    const int c0 = (col * kD + 8 * grp) * 2 / 16;  // 16-byte chunk of dims 8grp.. of head col
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      q.op[x] = col < G ? sm.q[p][c0 + 4 * x] : make_uint4(0, 0, 0, 0);
+  }
 
-    // Physical block of sub-tile i (a scalar load: the table is read-only).
-    auto phys_of = [&](int i) { return row[(tok_begin + kSub * i) / B]; };
-    constexpr int kTileBytes = B * kD * 2;
-    const int koff = (col * kD + 8 * grp) * 2;  // this lane's K bytes inside a sub-tile
+  // Sub-tile i of piece pc (physical block `phys`) into t.
+  static __device__ __forceinline__ void load_tile(const Args& a, const Piece& pc, int i, int phys,
+                                                   Tile& t) {
+    const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+    const int s16 = (pc.tok_begin + kSub * i) % B;
+    const int64_t tile = ((int64_t)phys * a.Hkv + pc.kvh) * kTileBytes;
+    const auto rk = tile_rsrc(a.kp, tile, kTileBytes);
+    const auto rv = tile_rsrc(a.vp, tile, kTileBytes);
+    const int koff = (col * kD + 8 * grp) * 2;    // this lane's K bytes inside a sub-tile
     const int voff = (col * kSub + 4 * grp) * 2;  // this lane's V^T bytes inside a group
-    auto load = [&](int i, int phys, Tile& t) {
-      const int s16 = (tok_begin + kSub * i) % B;
-      const int64_t tile = ((int64_t)phys * a.Hkv + kvh) * kTileBytes;
-      const auto rk = tile_rsrc(a.kp, tile, kTileBytes);
-      const auto rv = tile_rsrc(a.vp, tile, kTileBytes);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) t.k[x] = tile_load16(rk, koff + 64 * x, s16 * kD * 2);
+    for (int x = 0; x < 4; ++x) t.k[x] = tile_load16(rk, koff + 64 * x, s16 * kD * 2);
 #pragma unroll
-      for (int x = 0; x < 8; ++x) t.v[x] = tile_load8(rv, voff + 32 * x * kSub, s16 * kD * 2);
-    };
+    for (int x = 0; x < 8; ++x) t.v[x] = tile_load8(rv, voff + 32 * x * kSub, s16 * kD * 2);
+  }
 
-    f32x4 acc[8];
+  // Fold sub-tile i of piece pc into the wave state.
+  static __device__ __forceinline__ void compute(const Args& a, Smem&, const Piece& pc,
+                                                 const Query& q, State& st, Tile& t, int i) {
+    const int lane = threadIdx.x & 63, grp = lane >> 4;
+    const int valid = pc.tok_end - (pc.tok_begin + kSub * i);  // >= 1
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int x = 0; x < 8; ++x) acc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY;  // running max of head `col` (base-2 units)
-    float lsum = 0.f;     // this lane's share of the running sum of 2^(s - m)
-
-    auto compute = [&](Tile& t, int i) {
-      const int valid = tok_end - (tok_begin + kSub * i);  // >= 1
-      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int x = 0; x < 4; ++x) s = mma_qk(t.k[x], q.op[x], s);
+    float xr[4];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) s = mma_qk(t.k[x], qop[x], s);
-      float xr[4];
+    for (int r = 0; r < 4; ++r) xr[r] = (4 * grp + r < valid) ? s[r] * a.scale_log2 : -INFINITY;
+    float bm = fmaxf(fmaxf(xr[0], xr[1]), fmaxf(xr[2], xr[3]));
+    bm = max_xor16(bm);
+    bm = max_xor32(bm);
+    const float mn = fmaxf(st.m, bm);
+    if (wave_any(mn > st.m)) {
+      // The max grew somewhere in the wave: rescale sums and accumulators
+      // (alpha = 1 in lanes whose max did not move).
+      const float alpha = fast_exp2(st.m - mn);
+      st.lsum *= alpha;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) xr[r] = (4 * grp + r < valid) ? s[r] * a.scale_log2 : -INFINITY;
-      float bm = fmaxf(fmaxf(xr[0], xr[1]), fmaxf(xr[2], xr[3]));
-      bm = max_xor16(bm);
-      bm = max_xor32(bm);
-      const float mn = fmaxf(m, bm);
-      if (wave_any(mn > m)) {
-        // The max grew somewhere in the wave: rescale sums and accumulators
-        // (alpha = 1 in lanes whose max did not move).
-        const float alpha = fast_exp2(m - mn);
-        lsum *= alpha;
+      for (int x = 0; x < 8; ++x) st.acc[x] *= alpha;
+      st.m = mn;
+    }
+    float p[4];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) acc[x] *= alpha;
-        m = mn;
-      }
-      float p[4];
+    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(xr[r] - st.m);
+    st.lsum += (p[0] + p[1]) + (p[2] + p[3]);
+    Op4 phi, plo;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(xr[r] - m);
-      lsum += (p[0] + p[1]) + (p[2] + p[3]);
-      Op4 phi, plo;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        phi[r] = (Elem)p[r];
-        plo[r] = (Elem)(p[r] - (float)phi[r]);
-      }
-      if (valid < kSub) {
-        // Slots past the sequence end may hold anything (NaN included):
-        // zero them so that 0 * slot cannot poison the product.
-        const int nv = valid - 4 * grp;  // valid tokens among this lane's 4
-        const uint32_t lo_mask = (nv >= 1 ? 0x0000ffffu : 0u) | (nv >= 2 ? 0xffff0000u : 0u);
-        const uint32_t hi_mask = (nv >= 3 ? 0x0000ffffu : 0u) | (nv >= 4 ? 0xffff0000u : 0u);
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          t.v[x].x &= lo_mask;
-          t.v[x].y &= hi_mask;
-        }
-      }
+    for (int r = 0; r < 4; ++r) {
+      phi[r] = (Elem)p[r];
+      plo[r] = (Elem)(p[r] - (float)phi[r]);
+    }
+    if (valid < kSub) {
+      // Slots past the sequence end may hold anything (NaN included):
+      // zero them so that 0 * slot cannot poison the product.
+      const int nv = valid - 4 * grp;  // valid tokens among this lane's 4
+      const uint32_t lo_mask = (nv >= 1 ? 0x0000ffffu : 0u) | (nv >= 2 ? 0xffff0000u : 0u);
+      const uint32_t hi_mask = (nv >= 3 ? 0x0000ffffu : 0u) | (nv >= 4 ? 0xffff0000u : 0u);
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
-        acc[x] = mma_pv(t.v[x], phi, acc[x]);
-        acc[x] = mma_pv(t.v[x], plo, acc[x]);
+        t.v[x].x &= lo_mask;
+        t.v[x].y &= hi_mask;
       }
-    };
+    }
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      st.acc[x] = mma_pv(t.v[x], phi, st.acc[x]);
+      st.acc[x] = mma_pv(t.v[x], plo, st.acc[x]);
+    }
+  }
 
-    if (wave < nsub)
-      stream_subtiles<kDepth, Tile>(
-          wave, wave + kWaves * ((nsub - 1 - wave) / kWaves), phys_of, load, compute, [&](int i) {
-            set_priority_for_progress(pc.done_before + (kSub * i) / B, pc.chunk_len);
-          });
-
-    // Wave partial -> LDS: lsum summed over the 4 row groups of each column.
-    lsum = sum_xor16(lsum);
+  // Wave partial -> LDS (lsum summed over the 4 row groups of each column).
+  static __device__ __forceinline__ void to_lds(Smem& sm, const State& st, int wave) {
+    const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+    float lsum = sum_xor16(st.lsum);
     lsum = sum_xor32(lsum);
     if (col < G) {
 #pragma unroll
       for (int x = 0; x < 8; ++x)
-        *reinterpret_cast<f32x4*>(&sm.o[wave][col][16 * x + 4 * grp]) = acc[x];
+        *reinterpret_cast<f32x4*>(&sm.o[wave][col][16 * x + 4 * grp]) = st.acc[x];
       if (grp == 0) {
-        sm.m[wave][col] = m;
+        sm.m[wave][col] = st.m;
         sm.l[wave][col] = lsum;
       }
     }
-    __syncthreads();
-    emit_piece<T, G>(a, sm, pc);
-    __syncthreads();
   }
 };
 

@@ -169,40 +169,6 @@ __device__ __forceinline__ uint2 tile_load8(__amdgpu_buffer_rsrc_t r, int voff, 
   return make_uint2(v.x, v.y);
 }
 
-// Streaming loop of one wave over its sub-tiles first, first + kWaves, ...,
-// last, with kDepth sub-tiles in flight.  Every step issues its prefetch
-// unconditionally (past `last` the index is clamped to it, a harmless
-// re-read), so the compiler waits for exactly the oldest tile instead of
-// draining every outstanding load; the table entry of the load after next
-// is fetched (scalar load) one step early.
-template <int kDepth, class Tile, class PhysFn, class LoadFn, class ComputeFn, class ProgressFn>
-__device__ __forceinline__ void stream_subtiles(int first, int last, PhysFn phys_of, LoadFn load,
-                                                ComputeFn compute, ProgressFn progress) {
-  static_assert(kDepth >= 1 && kDepth <= 4, "prefetch depth");
-  Tile t[kDepth];
-#pragma unroll
-  for (int d = 0; d < kDepth; ++d) {
-    const int j = min(first + d * kWaves, last);
-    load(j, phys_of(j), t[d]);
-  }
-  int pn = phys_of(min(first + kDepth * kWaves, last));
-  int i = first;
-  auto step = [&](Tile& tile) -> bool {
-    progress(i);
-    compute(tile, i);
-    load(min(i + kDepth * kWaves, last), pn, tile);
-    pn = phys_of(min(i + (kDepth + 1) * kWaves, last));
-    i += kWaves;
-    return i > last;
-  };
-  while (true) {
-    if (step(t[0])) break;
-    if constexpr (kDepth > 1) { if (step(t[1])) break; }
-    if constexpr (kDepth > 2) { if (step(t[2])) break; }
-    if constexpr (kDepth > 3) { if (step(t[3])) break; }
-  }
-}
-
 // True in every lane when any lane of the wave has `pred` set.
 __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 
@@ -226,22 +192,27 @@ __device__ __forceinline__ const_i32_ptr as_constant(const int32_t* p) {
 //     cum[b] * Hkv + kvh * n_b + j,      n_b = ceil(L_b / B),
 // and cum[] is the exclusive prefix sum of n_b.  The W = cum[S] * Hkv units
 // are cut into nwg equal contiguous chunks; chunk k (one workgroup) handles
-// [k*c, min((k+1)*c, W)) with c = ceil(W / nwg).  A chunk meets at most two
-// (sequence, KV head) pairs only partly (its first and its last piece);
-// every pair in between is processed whole and written straight to `out`.
-// Partial pieces store (max, sum of exp, weighted V) in the workspace slot
-// 2*k + (piece is first in chunk ? 0 : 1); the merge kernel folds them.
+// [k*c, min((k+1)*c, W)) with c = ceil(W / nwg).  Within a chunk the work
+// falls into pieces, one per (sequence, KV head) it meets; at most the first
+// and the last piece are partial (the pair continues in a neighbouring
+// chunk).  Whole pairs are written straight to `out`; a partial piece
+// leaves (max, sum of exp, weighted V) in workspace slot
+// 2*k + (piece is first in chunk ? 0 : 1), and the split is folded by the
+// workgroup that counts its last piece in.
 
 __device__ __forceinline__ int blocks_of(int len, int B) { return len > 0 ? (len + B - 1) / B : 0; }
 
-// cum[0..S] in LDS (exclusive prefix of block counts).  All threads call.
+// cum[0..S] (exclusive prefix of block counts) and a copy of the lengths in
+// LDS.  All threads call.
 __device__ inline void build_prefix(const int32_t* __restrict__ lens, int S, int B, int* cum,
-                                    int* wsum) {
+                                    int* lens_s, int* wsum) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int carry = 0;
   for (int base = 0; base < S; base += kThreads) {
     const int b = base + tid;
-    int x = b < S ? blocks_of(lens[b], B) : 0;
+    const int len = b < S ? lens[b] : 0;
+    if (b < S) lens_s[b] = len;
+    int x = blocks_of(len, B);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(x, off);
@@ -282,6 +253,33 @@ __device__ __forceinline__ int chunk_of_wg(int wg, int nwg) {
   return (wg % 8) * (nwg / 8) + wg / 8;
 }
 
+// One piece of work: the tokens [tok_begin, tok_end) of (sequence b, KV
+// head kvh), nsub 16-token sub-tiles.  When the pair is split over several
+// chunks, its pieces occupy workspace slots first_slot (chunk kfirst) and
+// 2*k (chunks kfirst+1 .. kfirst+npieces-1); this piece is `slot`.
+struct Piece {
+  int b, kvh, L;
+  int tok_begin, tok_end, nsub;
+  int complete;
+  int slot, kfirst, npieces, first_slot;
+};
+
+__device__ __forceinline__ Piece uniform_piece(const Piece& p) {
+  Piece u;
+  u.b = uniform(p.b);
+  u.kvh = uniform(p.kvh);
+  u.L = uniform(p.L);
+  u.tok_begin = uniform(p.tok_begin);
+  u.tok_end = uniform(p.tok_end);
+  u.nsub = uniform(p.nsub);
+  u.complete = uniform(p.complete);
+  u.slot = uniform(p.slot);
+  u.kfirst = uniform(p.kfirst);
+  u.npieces = uniform(p.npieces);
+  u.first_slot = uniform(p.first_slot);
+  return u;
+}
+
 // ------------------------------------------------ partial combination
 //
 // Merge of softmax partials ("39 · PagedAttention", §3 "On the GPU", merge
@@ -292,13 +290,23 @@ __device__ __forceinline__ int chunk_of_wg(int wg, int nwg) {
 //
 // Two levels use it: the kWaves waves of a workgroup (through LDS, at the
 // end of every piece) and the pieces of a (sequence, KV head) that chunk
-// boundaries cut (through the workspace, done by the workgroup that
-// finishes the last of those pieces).
+// boundaries cut (through the workspace, by the workgroup that counts the
+// last of those pieces in).
 
 constexpr int kMergeBatch = 128;  // pieces staged in LDS at a time when folding a split
+constexpr int kQueryLdsBytes = 32768;
 
-template <int G>
+// Pieces listed per batch: their query groups are staged in LDS together.
+template <class T, int G>
+constexpr int piece_batch() {
+  constexpr int per = G * kD * T::kEsize;
+  constexpr int n = kQueryLdsBytes / per;
+  return n > 32 ? 32 : n;
+}
+
+template <class T, int G>
 struct MergeSmem {
+  static constexpr int kBatch = piece_batch<T, G>();
   float o[kWaves][G][kD + 4];
   float m[kWaves][G];
   float l[kWaves][G];
@@ -306,7 +314,14 @@ struct MergeSmem {
   float pm[kMergeBatch * G];
   float pl[kMergeBatch * G];
   float M[G], L[G], scale[G];
-  int last;
+  int last[2];
+  // the chunk's current batch of pieces and their query groups
+  Piece plist[kBatch];
+  int npl, next_f;
+  uint4 q[kBatch][G * kD * T::kEsize / 16];
+  // partial pieces of this chunk awaiting their count (first, last)
+  Piece commit[2];
+  int ncommit;
 };
 
 __device__ __forceinline__ float rescale(float mi, float m) {
@@ -325,36 +340,10 @@ __device__ __forceinline__ float ld_agent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One piece of work: logical blocks [j0, j1) of (sequence b, KV head kvh).
-// When the (sequence, KV head) is split over several chunks, its pieces
-// occupy workspace slots first_slot (chunk kfirst) and 2*k (chunks
-// kfirst+1 .. kfirst+npieces-1); this piece is `slot`.
-struct Piece {
-  int b, kvh, j0, j1, L;
-  bool complete;
-  int slot, kfirst, npieces, first_slot;
-  int done_before;  // units of the chunk finished before this piece
-  int chunk_len;    // units in the chunk
-};
-
-// Issue priority from a workgroup's progress through its chunk.  Two or more
-// workgroups share a CU, and the older one's waves win arbitration; left
-// alone, the first workgroup on every CU finished its (equal) chunk in ~60 %
-// of the time of the second, which then streamed with half the CU's loads
-// in flight.  Waves that are further behind get the higher priority, so the
-// co-resident workgroups progress together.
-__device__ __forceinline__ void set_priority_for_progress(int done, int total) {
-  const int q = (4 * done) / max(total, 1);
-  if (q <= 0) __builtin_amdgcn_s_setprio(3);
-  else if (q == 1) __builtin_amdgcn_s_setprio(2);
-  else if (q == 2) __builtin_amdgcn_s_setprio(1);
-  else __builtin_amdgcn_s_setprio(0);
-}
-
 // Folds the npieces partials of a split (sequence, KV head) from the
 // workspace and writes out = o / l.  All threads of the workgroup call.
 template <class T, int G>
-__device__ inline void fold_split(const Args& a, MergeSmem<G>& sm, const Piece& pc) {
+__device__ inline void fold_split(const Args& a, MergeSmem<T, G>& sm, const Piece& pc) {
   auto slot_of = [&](int p) { return p == 0 ? pc.first_slot : 2 * (pc.kfirst + p); };
   constexpr int kOut = (G * kD + kThreads - 1) / kThreads;  // outputs per thread
   float o[kOut];
@@ -421,14 +410,15 @@ __device__ inline void fold_split(const Args& a, MergeSmem<G>& sm, const Piece& 
       store_out<T>(a.out, ((int64_t)pc.b * a.Hq + pc.kvh * G + g) * kD + d, o[r] / sm.L[g], a.out_f32);
     }
   }
+  __syncthreads();
 }
 
 // Combine the kWaves wave partials held in `sm` and emit the piece's result:
-// the final output (complete piece), or a workspace partial followed, when
-// this is the last piece of its split to finish, by the fold of the split.
-// All threads call; the caller has synchronised after the waves wrote `sm`.
+// the final output (whole piece) or its workspace partial, which is counted
+// in later (commit_splits).  All threads call; the caller has synchronised
+// after the waves wrote `sm`.
 template <class T, int G>
-__device__ inline void emit_piece(const Args& a, MergeSmem<G>& sm, const Piece& pc) {
+__device__ inline void emit_piece(const Args& a, MergeSmem<T, G>& sm, const Piece& pc) {
   for (int idx = threadIdx.x; idx < G * kD; idx += kThreads) {
     const int g = idx / kD, d = idx % kD;
     float M = sm.m[0][g];
@@ -452,71 +442,224 @@ __device__ inline void emit_piece(const Args& a, MergeSmem<G>& sm, const Piece& 
       }
     }
   }
-  if (pc.complete) return;
-  // Count this piece in once every thread's partial stores have completed;
-  // the workgroup that brings the count to npieces folds the split and
-  // returns the counter to zero for the next call.
+  if (!pc.complete && threadIdx.x == 0) sm.commit[sm.ncommit++] = pc;
+}
+
+// At the end of the chunk: wait until this workgroup's partial stores have
+// completed, count each partial piece in on its split's counter, and fold
+// the splits this workgroup completed (returning their counters to zero).
+template <class T, int G>
+__device__ inline void commit_splits(const Args& a, MergeSmem<T, G>& sm) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  const int n = sm.ncommit;
   if (threadIdx.x == 0) {
-    const int old = __hip_atomic_fetch_add(a.counters + pc.kfirst, 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    const int last = old == pc.npieces - 1;
-    if (last) __hip_atomic_store(a.counters + pc.kfirst, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm.last = last;
+    for (int k = 0; k < n; ++k) {
+      const Piece& pc = sm.commit[k];
+      const int old = __hip_atomic_fetch_add(a.counters + pc.kfirst, 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      const int last = old == pc.npieces - 1;
+      if (last)
+        __hip_atomic_store(a.counters + pc.kfirst, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sm.last[k] = last;
+    }
   }
   __syncthreads();
-  if (sm.last) fold_split<T, G>(a, sm, pc);
+  for (int k = 0; k < n; ++k)
+    if (sm.last[k]) fold_split<T, G>(a, sm, sm.commit[k]);
 }
 
 // out = 0 for sequences of length 0 (every query head).  Sequences are
 // shared among workgroups round-robin.
 template <class T>
-__device__ inline void zero_empty_sequences(const Args& a, int chunk) {
+__device__ inline void zero_empty_sequences(const Args& a, int chunk, const int* lens_s) {
   for (int b = chunk; b < a.S; b += a.nwg) {
-    if (a.lens[b] > 0) continue;
+    if (lens_s[b] > 0) continue;
     for (int i = threadIdx.x; i < a.Hq * kD; i += kThreads)
       store_out<T>(a.out, (int64_t)b * a.Hq * kD + i, 0.f, a.out_f32);
   }
 }
 
-// Drives one decode workgroup: builds the prefix, walks its chunk piece by
-// piece and hands each piece to Engine::piece.
+// ------------------------------------------------------------ driver
+//
+// Per workgroup: the chunk's pieces are listed in LDS a batch at a time and
+// their query groups staged in LDS.  Each wave then streams its sub-tiles
+// (wave w takes sub-tiles w, w + kWaves, ... of every piece) with one pair
+// of sub-tiles in flight while it computes the previous pair.  The prefetch
+// runs across piece boundaries, so the next piece's first tiles are already
+// in flight while the workgroup merges and emits a finished piece.  A
+// wave's sub-tile count in each piece is padded to even with a dummy (a
+// re-read, not computed) so the two tile registers keep a fixed role; past
+// the batch the prefetch re-reads the last pair.  Every prefetch is issued
+// unconditionally so the compiler waits for exactly the pair it consumes.
+
+template <class T, int B, int G, class Engine>
+__device__ inline void stream_batch(const Args& a, typename Engine::Smem& sm, int chunk) {
+  using Tile = typename Engine::Tile;
+  using State = typename Engine::State;
+  using Query = typename Engine::Query;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int npl = uniform(sm.npl);
+
+  auto count = [&](int p) {  // this wave's sub-tiles in piece p
+    const int n = uniform(sm.plist[p].nsub);
+    return n > wave ? (n - 1 - wave) / kWaves + 1 : 0;
+  };
+  auto first_piece_from = [&](int p) {
+    while (p < npl && count(p) == 0) ++p;
+    return p;
+  };
+  // Pair cursor: piece p, local pair start k (even).  Advances to the next
+  // piece in which this wave has sub-tiles.
+  struct Cur {
+    int p, k;
+  };
+  auto advance = [&](Cur c) {
+    c.k += 2;
+    if (c.k >= count(c.p)) {
+      c.p = first_piece_from(c.p + 1);
+      c.k = 0;
+    }
+    return c;
+  };
+  auto row_of = [&](const Piece& pc) { return as_constant(a.bt + (int64_t)pc.b * a.mbs); };
+  // physical blocks of the pair at cursor c (second = first for a dummy)
+  auto pair_phys = [&](Cur c, int& ph0, int& ph1) {
+    const Piece pc = uniform_piece(sm.plist[c.p]);
+    const int n = count(c.p);
+    const int i0 = wave + kWaves * c.k;
+    const int i1 = wave + kWaves * min(c.k + 1, n - 1);
+    const auto row = row_of(pc);
+    ph0 = row[(pc.tok_begin + kSub * i0) / B];
+    ph1 = row[(pc.tok_begin + kSub * i1) / B];
+  };
+  auto pair_load = [&](Cur c, int ph0, int ph1, Tile& t0, Tile& t1) {
+    const Piece pc = uniform_piece(sm.plist[c.p]);
+    const int n = count(c.p);
+    Engine::load_tile(a, pc, wave + kWaves * c.k, ph0, t0);
+    Engine::load_tile(a, pc, wave + kWaves * min(c.k + 1, n - 1), ph1, t1);
+  };
+
+  Cur cc{first_piece_from(0), 0};
+  if (cc.p < npl) {
+    // prologue: the first pair, then the scalar table reads of the next
+    Cur pf = cc, lastv = cc;
+    Tile t0, t1;
+    int ph0, ph1;
+    pair_phys(pf, ph0, ph1);
+    pair_load(pf, ph0, ph1, t0, t1);
+    pf = advance(pf);
+    if (pf.p >= npl) pf = lastv; else lastv = pf;
+    pair_phys(pf, ph0, ph1);
+    __syncthreads();  // query groups staged (see run_decode)
+
+    for (int p = 0; p < npl; ++p) {
+      State st;
+      Engine::reset(st);
+      const Piece pc = uniform_piece(sm.plist[p]);
+      if (cc.p == p) {
+        Query q;
+        Engine::load_query(sm, p, q);
+        const int n = count(p);
+        while (true) {
+          Engine::compute(a, sm, pc, q, st, t0, wave + kWaves * cc.k);
+          // prefetch the next pair (possibly in a later piece) into t0, t1
+          const Piece pn = uniform_piece(sm.plist[pf.p]);
+          const int nn = count(pf.p);
+          Engine::load_tile(a, pn, wave + kWaves * pf.k, ph0, t0);
+          if (cc.k + 1 < n) Engine::compute(a, sm, pc, q, st, t1, wave + kWaves * (cc.k + 1));
+          Engine::load_tile(a, pn, wave + kWaves * min(pf.k + 1, nn - 1), ph1, t1);
+          cc = advance(cc);
+          pf = advance(pf);
+          if (pf.p >= npl) pf = lastv; else lastv = pf;
+          pair_phys(pf, ph0, ph1);
+          if (cc.p != p) break;
+        }
+      }
+      Engine::to_lds(sm, st, wave);
+      __syncthreads();
+      emit_piece<T, G>(a, sm, pc);
+      __syncthreads();
+    }
+  } else {
+    __syncthreads();  // query groups staged
+    for (int p = 0; p < npl; ++p) {
+      State st;
+      Engine::reset(st);
+      Engine::to_lds(sm, st, wave);
+      __syncthreads();
+      emit_piece<T, G>(a, sm, uniform_piece(sm.plist[p]));
+      __syncthreads();
+    }
+  }
+  (void)chunk;
+}
+
 template <class T, int B, int G, class Engine>
 __device__ inline void run_decode(const Args& a) {
-  extern __shared__ int cum[];                      // S + 1 ints
+  using Smem = typename Engine::Smem;
+  extern __shared__ int dyn[];
+  int* cum = dyn;               // S + 1
+  int* lens_s = dyn + a.S + 1;  // S
   __shared__ int wsum[kWaves];
-  __shared__ typename Engine::Smem sm;
-  build_prefix(a.lens, a.S, B, cum, wsum);
+  __shared__ Smem sm;
+  build_prefix(a.lens, a.S, B, cum, lens_s, wsum);
   const int chunk = chunk_of_wg(blockIdx.x, a.nwg);
-  zero_empty_sequences<T>(a, chunk);
+  zero_empty_sequences<T>(a, chunk, lens_s);
   const int W = cum[a.S] * a.Hkv;
   if (W == 0) return;
   const int c = (W + a.nwg - 1) / a.nwg;
   const int s = chunk * c;
   const int e = min(W, s + c);
-  int f = s;
-  while (f < e) {
-    Piece pc;
-    pc.b = find_seq(cum, a.S, a.Hkv, f);
-    const int nb = cum[pc.b + 1] - cum[pc.b];
-    const int base = cum[pc.b] * a.Hkv;
-    pc.kvh = (f - base) / nb;
-    pc.j0 = (f - base) - pc.kvh * nb;
-    const int ustart = base + pc.kvh * nb;
-    const int pe = min(e, ustart + nb);
-    pc.j1 = pc.j0 + (pe - f);
-    pc.L = a.lens[pc.b];
-    pc.complete = (pc.j0 == 0) && (pc.j1 == nb);
-    pc.slot = 2 * chunk + (f == s ? 0 : 1);
-    pc.kfirst = ustart / c;
-    pc.npieces = (ustart + nb - 1) / c - pc.kfirst + 1;
-    pc.first_slot = 2 * pc.kfirst + (ustart != pc.kfirst * c ? 1 : 0);
-    pc.done_before = f - s;
-    pc.chunk_len = e - s;
-    Engine::piece(a, sm, pc);
-    f = pe;
+  if (threadIdx.x == 0) {
+    sm.next_f = s;
+    sm.ncommit = 0;
   }
+  __syncthreads();
+  constexpr int kQChunks = G * kD * T::kEsize / 16;  // 16-byte chunks per query group
+  while (true) {
+    if (threadIdx.x == 0) {
+      int f = sm.next_f, n = 0;
+      while (f < e && n < Smem::kBatch) {
+        Piece pc;
+        pc.b = find_seq(cum, a.S, a.Hkv, f);
+        const int nb = cum[pc.b + 1] - cum[pc.b];
+        const int base = cum[pc.b] * a.Hkv;
+        pc.kvh = (f - base) / nb;
+        const int j0 = (f - base) - pc.kvh * nb;
+        const int ustart = base + pc.kvh * nb;
+        const int pe = min(e, ustart + nb);
+        const int j1 = j0 + (pe - f);
+        pc.L = lens_s[pc.b];
+        pc.tok_begin = j0 * B;
+        pc.tok_end = min(j1 * B, pc.L);
+        pc.nsub = (pc.tok_end - pc.tok_begin + kSub - 1) / kSub;
+        pc.complete = (j0 == 0) && (j1 == nb);
+        pc.slot = 2 * chunk + (f == s ? 0 : 1);
+        pc.kfirst = ustart / c;
+        pc.npieces = (ustart + nb - 1) / c - pc.kfirst + 1;
+        pc.first_slot = 2 * pc.kfirst + (ustart != pc.kfirst * c ? 1 : 0);
+        sm.plist[n++] = pc;
+        f = pe;
+      }
+      sm.npl = n;
+      sm.next_f = f;
+    }
+    __syncthreads();
+    const int npl = sm.npl;
+    if (npl == 0) break;
+    // Stage the batch's query groups in LDS (issued before any tile load).
+    for (int x = threadIdx.x; x < npl * kQChunks; x += kThreads) {
+      const int p = x / kQChunks, k = x % kQChunks;
+      const Piece& pc = sm.plist[p];
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
+          ((int64_t)pc.b * a.Hq + (int64_t)pc.kvh * G) * kD * T::kEsize);
+      sm.q[p][k] = src[k];
+    }
+    stream_batch<T, B, G, Engine>(a, sm, chunk);
+    __syncthreads();
+  }
+  commit_splits<T, G>(a, sm);
 }
 
 }  // namespace pa

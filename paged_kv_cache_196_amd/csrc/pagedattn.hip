@@ -125,7 +125,9 @@ DeviceInfo device_info() {
   return cache[dev];
 }
 
-size_t prefix_lds(int S) { return (size_t)(S + 1) * sizeof(int); }
+// Dynamic LDS of a decode workgroup: the block-count prefix (S + 1 ints)
+// and a copy of the lengths (S ints).
+size_t prefix_lds(int S) { return (size_t)(2 * S + 1) * sizeof(int); }
 
 // Workspace: [kMaxGrid] int32 split counters, then the partials
 // ws_o [2*kMaxGrid][G][kD] and ws_ml [2*kMaxGrid][G][2] (fp32).
