@@ -93,12 +93,11 @@ struct MfmaEngine {
       q.op[x] = col < G ? sm.q[p][c0 + 4 * x] : make_uint4(0, 0, 0, 0);
   }
 
-  // Sub-tile i of piece pc (physical block `phys`) into t.
-  static __device__ __forceinline__ void load_tile(const Args& a, const Piece& pc, int i, int phys,
+  // The sub-tile starting at slot s16 of physical block `phys`, KV head kvh.
+  static __device__ __forceinline__ void load_tile(const Args& a, int kvh, int s16, int phys,
                                                    Tile& t) {
     const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
-    const int s16 = (pc.tok_begin + kSub * i) % B;
-    const int64_t tile = ((int64_t)phys * a.Hkv + pc.kvh) * kTileBytes;
+    const int64_t tile = ((int64_t)phys * a.Hkv + kvh) * kTileBytes;
     const auto rk = tile_rsrc(a.kp, tile, kTileBytes);
     const auto rv = tile_rsrc(a.vp, tile, kTileBytes);
     const int koff = (col * kD + 8 * grp) * 2;    // this lane's K bytes inside a sub-tile
@@ -109,11 +108,11 @@ struct MfmaEngine {
     for (int x = 0; x < 8; ++x) t.v[x] = tile_load8(rv, voff + 32 * x * kSub, s16 * kD * 2);
   }
 
-  // Fold sub-tile i of piece pc into the wave state.
-  static __device__ __forceinline__ void compute(const Args& a, Smem&, const Piece& pc,
-                                                 const Query& q, State& st, Tile& t, int i) {
+  // Fold a sub-tile whose first `valid` tokens (1 .. 16) are attended into
+  // the wave state.
+  static __device__ __forceinline__ void compute(const Args& a, Smem&, const Query& q, State& st,
+                                                 Tile& t, int valid) {
     const int lane = threadIdx.x & 63, grp = lane >> 4;
-    const int valid = pc.tok_end - (pc.tok_begin + kSub * i);  // >= 1
     f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int x = 0; x < 4; ++x) s = mma_qk(t.k[x], q.op[x], s);

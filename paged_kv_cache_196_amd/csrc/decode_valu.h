@@ -78,11 +78,11 @@ struct ValuEngine {
     for (int g = 0; g < G; ++g) chunk_to_float<T>(sm.q[p][g * kD / E + rlane], q.f[g]);
   }
 
-  static __device__ __forceinline__ void load_tile(const Args& a, const Piece& pc, int i, int phys,
+  // The sub-tile starting at slot s16 of physical block `phys`, KV head kvh.
+  static __device__ __forceinline__ void load_tile(const Args& a, int kvh, int s16, int phys,
                                                    Tile& t) {
     const int lane = threadIdx.x & 63, rlane = lane % RL, vlane = lane % RV;
-    const int s16 = (pc.tok_begin + kSub * i) % B;
-    const int64_t tile = ((int64_t)phys * a.Hkv + pc.kvh) * kTileBytes;
+    const int64_t tile = ((int64_t)phys * a.Hkv + kvh) * kTileBytes;
     const auto rk = tile_rsrc(a.kp, tile, kTileBytes);
     const auto rv = tile_rsrc(a.vp, tile, kTileBytes);
     const int koff = ((lane / RL) * kD + rlane * E) * T::kEsize;    // K bytes of load 0
@@ -95,11 +95,12 @@ struct ValuEngine {
       t.v[n] = tile_load16(rv, voff + n * DPL * kSub * T::kEsize, s16 * kD * T::kEsize);
   }
 
-  static __device__ __forceinline__ void compute(const Args& a, Smem& sm, const Piece& pc,
-                                                 const Query& q, State& st, Tile& t, int i) {
+  // Fold a sub-tile whose first `valid` tokens (1 .. 16) are attended into
+  // the wave state.
+  static __device__ __forceinline__ void compute(const Args& a, Smem& sm, const Query& q, State& st,
+                                                 Tile& t, int valid) {
     const int lane = threadIdx.x & 63, rlane = lane % RL, vlane = lane % RV;
     const int wave = uniform(threadIdx.x >> 6);
-    const int valid = pc.tok_end - (pc.tok_begin + kSub * i);  // >= 1
     float x[NK][G];
 #pragma unroll
     for (int n = 0; n < NK; ++n) {

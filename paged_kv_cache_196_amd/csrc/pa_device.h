@@ -195,10 +195,12 @@ __device__ __forceinline__ const_i32_ptr as_constant(const int32_t* p) {
 // [k*c, min((k+1)*c, W)) with c = ceil(W / nwg).  Within a chunk the work
 // falls into pieces, one per (sequence, KV head) it meets; at most the first
 // and the last piece are partial (the pair continues in a neighbouring
-// chunk).  Whole pairs are written straight to `out`; a partial piece
-// leaves (max, sum of exp, weighted V) in workspace slot
-// 2*k + (piece is first in chunk ? 0 : 1), and the split is folded by the
-// workgroup that counts its last piece in.
+// chunk).  Whole pairs are written straight to `out`.  A partial piece's
+// (max, sum of exp, weighted V) belongs in workspace slot
+// 2*k + (piece is first in chunk ? 0 : 1); each split is folded exactly
+// once, by the workgroup that completes it: the one whose count-in is the
+// last, or a chunk's final piece that finds every other piece already
+// counted in and folds without publishing its own (finish_late).
 
 __device__ __forceinline__ int blocks_of(int len, int B) { return len > 0 ? (len + B - 1) / B : 0; }
 
@@ -257,10 +259,18 @@ __device__ __forceinline__ int chunk_of_wg(int wg, int nwg) {
 // head kvh), nsub 16-token sub-tiles.  When the pair is split over several
 // chunks, its pieces occupy workspace slots first_slot (chunk kfirst) and
 // 2*k (chunks kfirst+1 .. kfirst+npieces-1); this piece is `slot`.
+//
+// Kinds.  A whole piece covers its pair and writes `out` itself.  A partial
+// piece that opens its chunk and has more work after it is "early": it is
+// published and counted in as soon as it is merged, mid-chunk.  Any other
+// partial piece ends its chunk ("late"); by then its partners have usually
+// been counted in, so it folds the split without publishing its own part.
+enum : int { kWhole = 0, kEarly = 1, kLate = 2 };
+
 struct Piece {
   int b, kvh, L;
   int tok_begin, tok_end, nsub;
-  int complete;
+  int kind;
   int slot, kfirst, npieces, first_slot;
 };
 
@@ -272,7 +282,7 @@ __device__ __forceinline__ Piece uniform_piece(const Piece& p) {
   u.tok_begin = uniform(p.tok_begin);
   u.tok_end = uniform(p.tok_end);
   u.nsub = uniform(p.nsub);
-  u.complete = uniform(p.complete);
+  u.kind = uniform(p.kind);
   u.slot = uniform(p.slot);
   u.kfirst = uniform(p.kfirst);
   u.npieces = uniform(p.npieces);
@@ -293,8 +303,8 @@ __device__ __forceinline__ Piece uniform_piece(const Piece& p) {
 // boundaries cut (through the workspace, by the workgroup that counts the
 // last of those pieces in).
 
-constexpr int kMergeBatch = 128;  // pieces staged in LDS at a time when folding a split
 constexpr int kQueryLdsBytes = 32768;
+constexpr int kFoldLoads = 64;  // workspace loads per thread in flight when folding a split
 
 // Pieces listed per batch: their query groups are staged in LDS together.
 template <class T, int G>
@@ -304,24 +314,37 @@ constexpr int piece_batch() {
   return n > 32 ? 32 : n;
 }
 
+// A softmax partial (log2-domain max m, sum of exponentials l, weighted-V
+// sum o) for the outputs this thread owns: flat index idx = threadIdx.x +
+// r * kThreads of the G x kD outputs, (g, d) = (idx / kD, idx % kD).
+template <int G>
+struct Partial {
+  static constexpr int kOut = (G * kD + kThreads - 1) / kThreads;
+  static constexpr int kPer = kFoldLoads / kOut < 32 ? kFoldLoads / kOut : 32;  // pieces per fold round
+  float m[kOut], l[kOut], o[kOut];
+};
+
 template <class T, int G>
 struct MergeSmem {
   static constexpr int kBatch = piece_batch<T, G>();
+  static constexpr int kFoldMl = Partial<G>::kPer * G;
   float o[kWaves][G][kD + 4];
   float m[kWaves][G];
   float l[kWaves][G];
-  // folding the pieces of a split (sequence, KV head)
-  float pm[kMergeBatch * G];
-  float pl[kMergeBatch * G];
-  float M[G], L[G], scale[G];
-  int last[2];
+  // (max, sum) of the pieces of one folding round
+  float pm[kFoldMl];
+  float pl[kFoldMl];
+  int flag;
+  int seen;        // arrival count read for the piece being finished (-1: not read)
+  int early_seen;  // count returned to this chunk's early piece (-1: none)
   // the chunk's current batch of pieces and their query groups
   Piece plist[kBatch];
   int npl, next_f;
   uint4 q[kBatch][G * kD * T::kEsize / 16];
-  // partial pieces of this chunk awaiting their count (first, last)
-  Piece commit[2];
-  int ncommit;
+  // this chunk's early and late pieces (folded at the end of the chunk
+  // when this workgroup completes their split)
+  Piece early, late;
+  int fold_late;
 };
 
 __device__ __forceinline__ float rescale(float mi, float m) {
@@ -332,94 +355,37 @@ __device__ __forceinline__ float rescale(float mi, float m) {
 // different XCDs (separate L2s).  They are written and read with relaxed
 // agent-scope atomics (coherent at device scope without whole-L2
 // write-back / invalidate), and a writer waits for its stores to complete
-// before it counts itself in.
+// before it counts itself in; a reader reads partials only after it has
+// seen every other piece counted in.
 __device__ __forceinline__ void st_agent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float ld_agent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-// Folds the npieces partials of a split (sequence, KV head) from the
-// workspace and writes out = o / l.  All threads of the workgroup call.
-template <class T, int G>
-__device__ inline void fold_split(const Args& a, MergeSmem<T, G>& sm, const Piece& pc) {
-  auto slot_of = [&](int p) { return p == 0 ? pc.first_slot : 2 * (pc.kfirst + p); };
-  constexpr int kOut = (G * kD + kThreads - 1) / kThreads;  // outputs per thread
-  float o[kOut];
-#pragma unroll
-  for (int r = 0; r < kOut; ++r) o[r] = 0.f;
-  if (threadIdx.x < G) {
-    sm.M[threadIdx.x] = -INFINITY;
-    sm.L[threadIdx.x] = 0.f;
-  }
-  for (int p0 = 0; p0 < pc.npieces; p0 += kMergeBatch) {
-    const int np = min(kMergeBatch, pc.npieces - p0);
-    for (int e = threadIdx.x; e < np * G; e += kThreads) {
-      const float* ml = a.ws_ml + ((int64_t)slot_of(p0 + e / G) * G + e % G) * 2;
-      sm.pm[e] = ld_agent(ml);
-      sm.pl[e] = ld_agent(ml + 1);
-    }
-    __syncthreads();
-    if (threadIdx.x < G) {
-      const int g = threadIdx.x;
-      float Mb = sm.M[g];
-      for (int p = 0; p < np; ++p) Mb = fmaxf(Mb, sm.pm[p * G + g]);
-      const float sc = rescale(sm.M[g], Mb);
-      float L = sm.L[g] * sc;
-      for (int p = 0; p < np; ++p) L += rescale(sm.pm[p * G + g], Mb) * sm.pl[p * G + g];
-      sm.scale[g] = sc;
-      sm.M[g] = Mb;
-      sm.L[g] = L;
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < np * G; e += kThreads) sm.pm[e] = rescale(sm.pm[e], sm.M[e % G]);
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < kOut; ++r) {
-      const int idx = threadIdx.x + r * kThreads;
-      if (idx < G * kD) o[r] *= sm.scale[idx / kD];
-    }
-    // kChunk pieces x kOut outputs of loads in flight before any is used.
-    constexpr int kChunk = kOut >= 8 ? 2 : 16 / kOut;
-    for (int p = 0; p < np; p += kChunk) {
-      float v[kOut][kChunk];
-#pragma unroll
-      for (int r = 0; r < kOut; ++r) {
-        const int idx = min(threadIdx.x + r * kThreads, G * kD - 1);
-        const int g = idx / kD, d = idx % kD;
-#pragma unroll
-        for (int q = 0; q < kChunk; ++q)
-          v[r][q] = p + q < np ? ld_agent(a.ws_o + ((int64_t)slot_of(p0 + p + q) * G + g) * kD + d) : 0.f;
-      }
-#pragma unroll
-      for (int r = 0; r < kOut; ++r) {
-        const int g = min(threadIdx.x + r * kThreads, G * kD - 1) / kD;
-#pragma unroll
-        for (int q = 0; q < kChunk; ++q)
-          if (p + q < np) o[r] += sm.pm[(p + q) * G + g] * v[r][q];
-      }
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int r = 0; r < kOut; ++r) {
-    const int idx = threadIdx.x + r * kThreads;
-    if (idx < G * kD) {
-      const int g = idx / kD, d = idx % kD;
-      store_out<T>(a.out, ((int64_t)pc.b * a.Hq + pc.kvh * G + g) * kD + d, o[r] / sm.L[g], a.out_f32);
-    }
-  }
-  __syncthreads();
+__device__ __forceinline__ int count_in(int* c) {
+  return __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ int counted(const int* c) {
+  return __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void reset_count(int* c) {
+  __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until this wave's stores (and loads) have completed.
+__device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Combine the kWaves wave partials held in `sm` and emit the piece's result:
-// the final output (whole piece) or its workspace partial, which is counted
-// in later (commit_splits).  All threads call; the caller has synchronised
-// after the waves wrote `sm`.
+// Merge the kWaves wave partials the waves left in `sm` into this thread's
+// outputs.  Callers synchronise before (waves wrote sm) and after.
 template <class T, int G>
-__device__ inline void emit_piece(const Args& a, MergeSmem<T, G>& sm, const Piece& pc) {
-  for (int idx = threadIdx.x; idx < G * kD; idx += kThreads) {
+__device__ inline void merge_waves(const MergeSmem<T, G>& sm, Partial<G>& pt) {
+#pragma unroll
+  for (int r = 0; r < Partial<G>::kOut; ++r) {
+    const int idx = threadIdx.x + r * kThreads;
+    pt.m[r] = -INFINITY;
+    pt.l[r] = 0.f;
+    pt.o[r] = 0.f;
+    if (idx >= G * kD) continue;
     const int g = idx / kD, d = idx % kD;
     float M = sm.m[0][g];
 #pragma unroll
@@ -431,42 +397,213 @@ __device__ inline void emit_piece(const Args& a, MergeSmem<T, G>& sm, const Piec
       o += f * sm.o[w][g][d];
       l += f * sm.l[w][g];
     }
-    if (pc.complete) {
-      const int64_t oi = ((int64_t)pc.b * a.Hq + pc.kvh * G + g) * kD + d;
-      store_out<T>(a.out, oi, o / l, a.out_f32);
-    } else {
-      st_agent(a.ws_o + ((int64_t)pc.slot * G + g) * kD + d, o);
-      if (d == 0) {
-        st_agent(a.ws_ml + ((int64_t)pc.slot * G + g) * 2 + 0, M);
-        st_agent(a.ws_ml + ((int64_t)pc.slot * G + g) * 2 + 1, l);
-      }
-    }
+    pt.m[r] = M;
+    pt.l[r] = l;
+    pt.o[r] = o;
   }
-  if (!pc.complete && threadIdx.x == 0) sm.commit[sm.ncommit++] = pc;
 }
 
-// At the end of the chunk: wait until this workgroup's partial stores have
-// completed, count each partial piece in on its split's counter, and fold
-// the splits this workgroup completed (returning their counters to zero).
 template <class T, int G>
-__device__ inline void commit_splits(const Args& a, MergeSmem<T, G>& sm) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  const int n = sm.ncommit;
-  if (threadIdx.x == 0) {
-    for (int k = 0; k < n; ++k) {
-      const Piece& pc = sm.commit[k];
-      const int old = __hip_atomic_fetch_add(a.counters + pc.kfirst, 1, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-      const int last = old == pc.npieces - 1;
-      if (last)
-        __hip_atomic_store(a.counters + pc.kfirst, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      sm.last[k] = last;
+__device__ inline void store_result(const Args& a, const Piece& pc, const Partial<G>& pt) {
+#pragma unroll
+  for (int r = 0; r < Partial<G>::kOut; ++r) {
+    const int idx = threadIdx.x + r * kThreads;
+    if (idx >= G * kD) continue;
+    const int g = idx / kD, d = idx % kD;
+    store_out<T>(a.out, ((int64_t)pc.b * a.Hq + pc.kvh * G + g) * kD + d, pt.o[r] / pt.l[r],
+                 a.out_f32);
+  }
+}
+
+template <int G>
+__device__ inline void store_partial(const Args& a, int slot, const Partial<G>& pt) {
+#pragma unroll
+  for (int r = 0; r < Partial<G>::kOut; ++r) {
+    const int idx = threadIdx.x + r * kThreads;
+    if (idx >= G * kD) continue;
+    const int g = idx / kD, d = idx % kD;
+    st_agent(a.ws_o + ((int64_t)slot * G + g) * kD + d, pt.o[r]);
+    if (d == 0) {
+      st_agent(a.ws_ml + ((int64_t)slot * G + g) * 2 + 0, pt.m[r]);
+      st_agent(a.ws_ml + ((int64_t)slot * G + g) * 2 + 1, pt.l[r]);
     }
   }
+}
+
+// Folds the npieces partials of a split (sequence, KV head) and writes
+// out = o / l.  The pieces are combined in piece order whoever folds, so
+// the result does not depend on which workgroup arrived last.  The
+// partial in workspace slot `own_slot` is the caller's own and is taken
+// from `own` (its outputs) and sm.m[0] / sm.l[0] (its per-head max and
+// sum) instead of memory; own_slot = -1 reads every piece.  Each round
+// issues the weighted-V loads of up to kPer pieces together with their
+// (max, sum) loads, so a split of up to kPer pieces costs one round trip.
+// All threads call; the caller has seen every piece counted in.
+template <class T, int G>
+__device__ inline void fold_split(const Args& a, MergeSmem<T, G>& sm, const Piece& pc,
+                                  const Partial<G>& own, int own_slot) {
+  constexpr int kOut = Partial<G>::kOut;
+  constexpr int kPer = Partial<G>::kPer;
+  auto slot_of = [&](int p) { return p == 0 ? pc.first_slot : 2 * (pc.kfirst + p); };
+  Partial<G> acc;
+#pragma unroll
+  for (int r = 0; r < kOut; ++r) {
+    acc.m[r] = -INFINITY;
+    acc.l[r] = 0.f;
+    acc.o[r] = 0.f;
+  }
+  for (int p0 = 0; p0 < pc.npieces; p0 += kPer) {
+    const int np = min(kPer, pc.npieces - p0);
+    float v[kOut][kPer];
+#pragma unroll
+    for (int r = 0; r < kOut; ++r) {
+      const int idx = min(threadIdx.x + r * kThreads, G * kD - 1);
+      const int g = idx / kD, d = idx % kD;
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int slot = slot_of(p0 + q);
+        v[r][q] = q >= np ? 0.f
+                  : slot == own_slot ? own.o[r]
+                  : ld_agent(a.ws_o + ((int64_t)slot * G + g) * kD + d);
+      }
+    }
+    for (int e = threadIdx.x; e < np * G; e += kThreads) {
+      const int slot = slot_of(p0 + e / G), g = e % G;
+      const float* ml = a.ws_ml + ((int64_t)slot * G + g) * 2;
+      const bool mine = slot == own_slot;
+      sm.pm[e] = mine ? sm.m[0][g] : ld_agent(ml);
+      sm.pl[e] = mine ? sm.l[0][g] : ld_agent(ml + 1);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kOut; ++r) {
+      const int g = min(threadIdx.x + r * kThreads, G * kD - 1) / kD;
+      float M = acc.m[r];
+#pragma unroll
+      for (int q = 0; q < kPer; ++q)
+        if (q < np) M = fmaxf(M, sm.pm[q * G + g]);
+      const float f0 = rescale(acc.m[r], M);
+      float l = acc.l[r] * f0, o = acc.o[r] * f0;
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        if (q < np) {
+          const float f = rescale(sm.pm[q * G + g], M);
+          l += f * sm.pl[q * G + g];
+          o += f * v[r][q];
+        }
+      }
+      acc.m[r] = M;
+      acc.l[r] = l;
+      acc.o[r] = o;
+    }
+    __syncthreads();
+  }
+  store_result<T, G>(a, pc, acc);
+}
+
+// The last piece of a chunk when it is partial ("late").  sm.seen is the
+// split's arrival count read while the waves were merging (-1 if not
+// read).  When every other piece has already counted in, this workgroup
+// folds the split from its own partial: no store of its own part and no
+// atomic.  Otherwise it publishes its partial, counts itself in, and folds
+// if it turned out to be the last.  The fold itself runs at the end of the
+// chunk (finish_chunk), outside the streaming loop, from the own partial
+// left in LDS.
+template <class T, int G>
+__device__ inline void finish_late(const Args& a, MergeSmem<T, G>& sm, const Piece& pc,
+                                   const Partial<G>& pt) {
+  int* cnt = a.counters + pc.kfirst;
+  bool fold = uniform(sm.seen) == pc.npieces - 1;
+  if (fold) {
+    if (threadIdx.x == 0) reset_count(cnt);
+  } else {
+    store_partial<G>(a, pc.slot, pt);
+    drain_vmem();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int last = count_in(cnt) == pc.npieces - 1;
+      if (last) reset_count(cnt);
+      sm.flag = last;
+    }
+    __syncthreads();
+    fold = uniform(sm.flag);
+  }
+  if (!fold) return;
+  // every thread has finished reading the wave partials (barrier above)
+#pragma unroll
+  for (int r = 0; r < Partial<G>::kOut; ++r) {
+    const int idx = threadIdx.x + r * kThreads;
+    if (idx >= G * kD) continue;
+    const int g = idx / kD, d = idx % kD;
+    sm.o[0][g][d] = pt.o[r];
+    if (d == 0) {
+      sm.m[0][g] = pt.m[r];
+      sm.l[0][g] = pt.l[r];
+    }
+  }
+  if (threadIdx.x == 0) {
+    sm.late = pc;
+    sm.fold_late = 1;
+  }
+}
+
+// Emit a piece after its waves wrote their partials to LDS (to_lds) and
+// thread 0 set sm.seen.  All threads call.  A whole piece writes `out`.
+// An early piece publishes its partial and counts itself in at once
+// (sm.early_seen keeps the returned count; the rare case that it was the
+// last is folded at the end of the chunk).  A late piece finishes its
+// split (finish_late).  Values returned by memory are moved to LDS where
+// they arrive, so no load is left in flight into a register that the
+// streaming loop reuses.
+template <class T, int G>
+__device__ inline void finish_piece(const Args& a, MergeSmem<T, G>& sm, const Piece& pc) {
   __syncthreads();
-  for (int k = 0; k < n; ++k)
-    if (sm.last[k]) fold_split<T, G>(a, sm, sm.commit[k]);
+  Partial<G> pt;
+  merge_waves<T, G>(sm, pt);
+  if (pc.kind == kWhole) {
+    store_result<T, G>(a, pc, pt);
+  } else if (pc.kind == kEarly) {
+    store_partial<G>(a, pc.slot, pt);
+    drain_vmem();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      sm.early_seen = count_in(a.counters + pc.kfirst);
+      sm.early = pc;
+    }
+  } else {
+    finish_late<T, G>(a, sm, pc, pt);
+  }
+  __syncthreads();
+}
+
+// End of the chunk: fold the late piece's split if finish_late chose to
+// (own partial in LDS), and the early piece's split if its count-in was
+// the last one.  All threads call.
+template <class T, int G>
+__device__ inline void finish_chunk(const Args& a, MergeSmem<T, G>& sm) {
+  if (threadIdx.x == 0) sm.flag = sm.early_seen >= 0 && sm.early_seen == sm.early.npieces - 1;
+  __syncthreads();
+  if (uniform(sm.fold_late)) {
+    const Piece pc = uniform_piece(sm.late);
+    Partial<G> own;
+#pragma unroll
+    for (int r = 0; r < Partial<G>::kOut; ++r) {
+      const int idx = min(threadIdx.x + r * kThreads, G * kD - 1);
+      const int g = idx / kD, d = idx % kD;
+      own.m[r] = sm.m[0][g];
+      own.l[r] = sm.l[0][g];
+      own.o[r] = sm.o[0][g][d];
+    }
+    fold_split<T, G>(a, sm, pc, own, pc.slot);
+  }
+  if (uniform(sm.flag)) {
+    const Piece pc = uniform_piece(sm.early);
+    if (threadIdx.x == 0) reset_count(a.counters + pc.kfirst);
+    Partial<G> none;
+#pragma unroll
+    for (int r = 0; r < Partial<G>::kOut; ++r) none.m[r] = none.l[r] = none.o[r] = 0.f;
+    fold_split<T, G>(a, sm, pc, none, -1);
+  }
 }
 
 // out = 0 for sequences of length 0 (every query head).  Sequences are
@@ -483,116 +620,142 @@ __device__ inline void zero_empty_sequences(const Args& a, int chunk, const int*
 // ------------------------------------------------------------ driver
 //
 // Per workgroup: the chunk's pieces are listed in LDS a batch at a time and
-// their query groups staged in LDS.  Each wave then streams its sub-tiles
-// (wave w takes sub-tiles w, w + kWaves, ... of every piece) with one pair
-// of sub-tiles in flight while it computes the previous pair.  The prefetch
-// runs across piece boundaries, so the next piece's first tiles are already
-// in flight while the workgroup merges and emits a finished piece.  A
-// wave's sub-tile count in each piece is padded to even with a dummy (a
-// re-read, not computed) so the two tile registers keep a fixed role; past
-// the batch the prefetch re-reads the last pair.  Every prefetch is issued
-// unconditionally so the compiler waits for exactly the pair it consumes.
+// their query groups staged in LDS.  The batch's sub-tiles are numbered
+// through its pieces in order and dealt round-robin to the waves (wave w
+// takes sub-tiles w, w + kWaves, ...), so every wave streams one
+// continuous sequence of sub-tiles whatever the piece boundaries: each
+// wave's count differs from the others' by at most one per batch.  A wave
+// keeps two sub-tiles in flight (registers t0, t1) and computes one while
+// the next loads; its table lookups run one sub-tile ahead on the scalar
+// unit.  When the next sub-tile belongs to a later piece, the wave first
+// finishes the pieces in between (finish_piece; every wave finishes every
+// piece, in order, so their barriers pair up), and the loads already in
+// flight keep streaming meanwhile.  Past the end of its share a wave
+// re-reads its last sub-tile (never computed), so every load is issued
+// unconditionally and the compiler waits for exactly the one it consumes.
+
+// Arrival count of a late two-piece split, read by thread 0 as its waves
+// finish streaming (the load overlaps the wave merge); -1 otherwise.  Splits
+// over more pieces have partners that end at the same time, so the read
+// would rarely find them all counted in.
+__device__ __forceinline__ int split_seen(const Args& a, const Piece& pc) {
+  if (pc.kind != kLate || pc.npieces != 2 || threadIdx.x != 0) return -1;
+  return counted(a.counters + pc.kfirst);
+}
 
 template <class T, int B, int G, class Engine>
-__device__ inline void stream_batch(const Args& a, typename Engine::Smem& sm, int chunk) {
+__device__ inline void stream_batch(const Args& a, typename Engine::Smem& sm) {
   using Tile = typename Engine::Tile;
   using State = typename Engine::State;
   using Query = typename Engine::Query;
   const int wave = uniform(threadIdx.x >> 6);
   const int npl = uniform(sm.npl);
 
-  auto count = [&](int p) {  // this wave's sub-tiles in piece p
-    const int n = uniform(sm.plist[p].nsub);
-    return n > wave ? (n - 1 - wave) / kWaves + 1 : 0;
-  };
-  auto first_piece_from = [&](int p) {
-    while (p < npl && count(p) == 0) ++p;
-    return p;
-  };
-  // Pair cursor: piece p, local pair start k (even).  Advances to the next
-  // piece in which this wave has sub-tiles.
+  // Stream position: sub-tile j of piece p (p == npl: past the end), with
+  // the fields of piece p that addressing and masking need.
   struct Cur {
-    int p, k;
+    int p, j, n, b, kvh, tb, te;
   };
-  auto advance = [&](Cur c) {
-    c.k += 2;
-    if (c.k >= count(c.p)) {
-      c.p = first_piece_from(c.p + 1);
-      c.k = 0;
+  auto settle = [&](Cur& c) {  // move an overflowing j on to the piece holding it
+    while (c.p < npl) {
+      c.n = uniform(sm.plist[c.p].nsub);
+      if (c.j < c.n) break;
+      c.j -= c.n;
+      ++c.p;
     }
-    return c;
+    if (c.p < npl) {
+      c.b = uniform(sm.plist[c.p].b);
+      c.kvh = uniform(sm.plist[c.p].kvh);
+      c.tb = uniform(sm.plist[c.p].tok_begin);
+      c.te = uniform(sm.plist[c.p].tok_end);
+    }
   };
-  auto row_of = [&](const Piece& pc) { return as_constant(a.bt + (int64_t)pc.b * a.mbs); };
-  // physical blocks of the pair at cursor c (second = first for a dummy)
-  auto pair_phys = [&](Cur c, int& ph0, int& ph1) {
-    const Piece pc = uniform_piece(sm.plist[c.p]);
-    const int n = count(c.p);
-    const int i0 = wave + kWaves * c.k;
-    const int i1 = wave + kWaves * min(c.k + 1, n - 1);
-    const auto row = row_of(pc);
-    ph0 = row[(pc.tok_begin + kSub * i0) / B];
-    ph1 = row[(pc.tok_begin + kSub * i1) / B];
+  auto advance = [&](Cur& c) {
+    c.j += kWaves;
+    if (c.j >= c.n) settle(c);
   };
-  auto pair_load = [&](Cur c, int ph0, int ph1, Tile& t0, Tile& t1) {
-    const Piece pc = uniform_piece(sm.plist[c.p]);
-    const int n = count(c.p);
-    Engine::load_tile(a, pc, wave + kWaves * c.k, ph0, t0);
-    Engine::load_tile(a, pc, wave + kWaves * min(c.k + 1, n - 1), ph1, t1);
-  };
+  Cur c{0, wave, 0, 0, 0, 0, 0};
+  settle(c);
 
-  Cur cc{first_piece_from(0), 0};
-  if (cc.p < npl) {
-    // prologue: the first pair, then the scalar table reads of the next
-    Cur pf = cc, lastv = cc;
-    Tile t0, t1;
-    int ph0, ph1;
-    pair_phys(pf, ph0, ph1);
-    pair_load(pf, ph0, ph1, t0, t1);
-    pf = advance(pf);
-    if (pf.p >= npl) pf = lastv; else lastv = pf;
-    pair_phys(pf, ph0, ph1);
-    __syncthreads();  // query groups staged (see run_decode)
-
-    for (int p = 0; p < npl; ++p) {
-      State st;
-      Engine::reset(st);
-      const Piece pc = uniform_piece(sm.plist[p]);
-      if (cc.p == p) {
-        Query q;
-        Engine::load_query(sm, p, q);
-        const int n = count(p);
-        while (true) {
-          Engine::compute(a, sm, pc, q, st, t0, wave + kWaves * cc.k);
-          // prefetch the next pair (possibly in a later piece) into t0, t1
-          const Piece pn = uniform_piece(sm.plist[pf.p]);
-          const int nn = count(pf.p);
-          Engine::load_tile(a, pn, wave + kWaves * pf.k, ph0, t0);
-          if (cc.k + 1 < n) Engine::compute(a, sm, pc, q, st, t1, wave + kWaves * (cc.k + 1));
-          Engine::load_tile(a, pn, wave + kWaves * min(pf.k + 1, nn - 1), ph1, t1);
-          cc = advance(cc);
-          pf = advance(pf);
-          if (pf.p >= npl) pf = lastv; else lastv = pf;
-          pair_phys(pf, ph0, ph1);
-          if (cc.p != p) break;
-        }
-      }
+  int cur = 0;  // piece whose state the wave holds
+  State st;
+  Engine::reset(st);
+  Query q;
+  // Finish pieces cur .. p-1 and start piece p (p <= npl).  The late
+  // piece is the last of the chunk, so it is only ever finished after the
+  // streaming loop (enter(npl, true)); only there is its arrival count
+  // read, which keeps that load and its wait out of the loop.
+  auto enter = [&](int p, bool last) {
+    if (cur >= p) return;
+    do {
+      const Piece pc = uniform_piece(sm.plist[cur]);
+      const int seen = last ? split_seen(a, pc) : -1;
       Engine::to_lds(sm, st, wave);
-      __syncthreads();
-      emit_piece<T, G>(a, sm, pc);
-      __syncthreads();
+      if (threadIdx.x == 0) sm.seen = seen;
+      finish_piece<T, G>(a, sm, pc);
+      Engine::reset(st);
+    } while (++cur < p);
+    if (p < npl) Engine::load_query(sm, p, q);
+  };
+
+  if (c.p < npl) {
+    Cur last = c;  // last position inside the batch (re-read past the end)
+    auto row_phys = [&](const Cur& u) {
+      return as_constant(a.bt + (int64_t)u.b * a.mbs)[(u.tb + kSub * u.j) / B];
+    };
+    auto load = [&](const Cur& u, int phys, Tile& t) {
+      Engine::load_tile(a, u.kvh, (u.tb + kSub * u.j) % B, phys, t);
+    };
+    // Each tile register carries (piece, valid tokens) of its sub-tile.
+    int p0 = c.p, v0 = c.te - (c.tb + kSub * c.j);
+    Tile t0, t1;
+    load(c, row_phys(c), t0);
+    advance(c);
+    if (c.p < npl) last = c;
+    int p1 = c.p, v1 = c.te - (c.tb + kSub * c.j);
+    load(last, row_phys(last), t1);
+    advance(c);
+    if (c.p < npl) last = c;
+    int ph = row_phys(last);
+    __syncthreads();  // query groups staged (see run_decode)
+    Engine::load_query(sm, 0, q);
+    // Load the stream's next sub-tile into t and return its (piece, valid
+    // tokens).
+    auto refill = [&](Tile& t, int& pn, int& vn) {
+      pn = c.p;
+      vn = c.te - (c.tb + kSub * c.j);
+      load(last, ph, t);
+      advance(c);
+      if (c.p < npl) last = c;
+      ph = row_phys(last);
+    };
+    // Every pass through the body refills t0 and then t1 (a re-read when
+    // past the end), so the loads in flight at the top of the loop are
+    // always t0's followed by t1's and the compiler's wait before each
+    // compute covers exactly that tile.  The loop leaves only at the
+    // bottom.
+    enter(p0, false);
+    while (true) {
+      int n0, w0, n1, w1;
+      Engine::compute(a, sm, q, st, t0, v0);
+      refill(t0, n0, w0);
+      const bool more = p1 < npl;
+      if (more) {
+        enter(p1, false);
+        Engine::compute(a, sm, q, st, t1, v1);
+      }
+      refill(t1, n1, w1);
+      p0 = n0;
+      v0 = w0;
+      p1 = n1;
+      v1 = w1;
+      if (!more || p0 >= npl) break;
+      enter(p0, false);
     }
   } else {
     __syncthreads();  // query groups staged
-    for (int p = 0; p < npl; ++p) {
-      State st;
-      Engine::reset(st);
-      Engine::to_lds(sm, st, wave);
-      __syncthreads();
-      emit_piece<T, G>(a, sm, uniform_piece(sm.plist[p]));
-      __syncthreads();
-    }
   }
-  (void)chunk;
+  enter(npl, true);
 }
 
 template <class T, int B, int G, class Engine>
@@ -613,7 +776,8 @@ __device__ inline void run_decode(const Args& a) {
   const int e = min(W, s + c);
   if (threadIdx.x == 0) {
     sm.next_f = s;
-    sm.ncommit = 0;
+    sm.fold_late = 0;
+    sm.early_seen = -1;
   }
   __syncthreads();
   constexpr int kQChunks = G * kD * T::kEsize / 16;  // 16-byte chunks per query group
@@ -634,7 +798,7 @@ __device__ inline void run_decode(const Args& a) {
         pc.tok_begin = j0 * B;
         pc.tok_end = min(j1 * B, pc.L);
         pc.nsub = (pc.tok_end - pc.tok_begin + kSub - 1) / kSub;
-        pc.complete = (j0 == 0) && (j1 == nb);
+        pc.kind = (j0 == 0 && j1 == nb) ? kWhole : (f == s && pe < e) ? kEarly : kLate;
         pc.slot = 2 * chunk + (f == s ? 0 : 1);
         pc.kfirst = ustart / c;
         pc.npieces = (ustart + nb - 1) / c - pc.kfirst + 1;
@@ -656,10 +820,10 @@ __device__ inline void run_decode(const Args& a) {
           ((int64_t)pc.b * a.Hq + (int64_t)pc.kvh * G) * kD * T::kEsize);
       sm.q[p][k] = src[k];
     }
-    stream_batch<T, B, G, Engine>(a, sm, chunk);
+    stream_batch<T, B, G, Engine>(a, sm);
     __syncthreads();
   }
-  commit_splits<T, G>(a, sm);
+  finish_chunk<T, G>(a, sm);
 }
 
 }  // namespace pa
