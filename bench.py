@@ -197,6 +197,8 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--kernel", choices=["auto", "valu", "mfma"], default="auto")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--no-prefix-hint", action="store_true",
+                    help="do not pass the shared-prefix cache hint (cached_prefix_blocks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the oracle spot check")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -245,7 +247,8 @@ def main() -> int:
     bt = torch.from_numpy(w.block_tables).to(dev)
     lens = torch.from_numpy(w.seq_lens).to(dev)
     kern = {"auto": pa.PA_KERNEL_AUTO, "valu": pa.PA_KERNEL_VALU, "mfma": pa.PA_KERNEL_MFMA}[args.kernel]
-    desc = pa.make_desc(q, kp, bt, out_dtype=torch.float32, kernel=kern)
+    hint = 0 if args.no_prefix_hint else w.shared_prefix_blocks
+    desc = pa.make_desc(q, kp, bt, out_dtype=torch.float32, kernel=kern, cached_prefix_blocks=hint)
     ws_bytes = pa.pa_workspace_bytes(desc)
     ws = pa.new_workspace(desc, dev)
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
@@ -326,6 +329,8 @@ def main() -> int:
             "seq_len_min": int(w.seq_lens.min()),
             "seq_len_max": int(w.seq_lens.max()),
             "num_blocks": w.num_blocks,
+            "shared_prefix_blocks": w.shared_prefix_blocks,
+            "cached_prefix_blocks": hint,
             "seed": w.seed,
             "kernel": args.kernel,
             "decode_grid": grid,

@@ -74,7 +74,7 @@ extern "C" {
 typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_NULL = 1,        /* a required pointer is NULL */
-  PA_ERR_SHAPE = 2,       /* a size is <= 0, or num_q_heads % num_kv_heads != 0 */
+  PA_ERR_SHAPE = 2,       /* a size is <= 0 (cached_prefix_blocks < 0), or num_q_heads % num_kv_heads != 0 */
   PA_ERR_DTYPE = 3,       /* unknown dtype, or out_dtype neither PA_F32 nor dtype */
   PA_ERR_UNSUPPORTED = 4, /* valid but not built: head_dim, block_size, group size, kernel/dtype pair */
   PA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than pa_workspace_bytes() */
@@ -110,6 +110,14 @@ typedef struct pa_desc {
   int32_t dtype;              /* pa_dtype of q, k_pool, v_pool */
   int32_t out_dtype;          /* PA_F32, or equal to dtype (round to nearest even) */
   int32_t kernel;             /* pa_kernel */
+  /* Cache hint, >= 0 (0: none).  The first cached_prefix_blocks logical
+   * blocks of every sequence may be shared with other sequences of the
+   * batch (prefix sharing, "PagedAttention: The Cache Was Storing
+   * Nothing", §2.3): they are read with a cache-retaining policy so that
+   * the sequences sharing them hit in L2 / Infinity Cache.  All other K/V
+   * is streamed with a non-temporal policy (read once per call).  Results
+   * do not depend on it. */
+  int32_t cached_prefix_blocks;
 } pa_desc;
 
 /* Human-readable name of a status code (static storage, never NULL). */

@@ -30,7 +30,7 @@ EXPORTS = (
 class PaDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "block_size", "num_blocks",
-        "max_blocks_per_seq", "dtype", "out_dtype", "kernel")]
+        "max_blocks_per_seq", "dtype", "out_dtype", "kernel", "cached_prefix_blocks")]
 
 
 class PagedAttnError(RuntimeError):

@@ -30,16 +30,19 @@ def pa_dtype_of(t: torch.dtype) -> int:
 
 
 def make_desc(q: torch.Tensor, k_pool: torch.Tensor, block_tables: torch.Tensor, *,
-              out_dtype: torch.dtype | None = torch.float32, kernel: int = _lib.PA_KERNEL_AUTO
-              ) -> _lib.PaDesc:
-    """q [S][Hq][D]; k_pool [NB][Hkv][B][D]; block_tables int32 [S][max_blocks]."""
+              out_dtype: torch.dtype | None = torch.float32, kernel: int = _lib.PA_KERNEL_AUTO,
+              cached_prefix_blocks: int = 0) -> _lib.PaDesc:
+    """q [S][Hq][D]; k_pool [NB][Hkv][B][D]; block_tables int32 [S][max_blocks].
+    cached_prefix_blocks: leading logical blocks of every sequence that may
+    be shared with other sequences (a cache hint; results do not change)."""
     S, Hq, D = q.shape
     NB, Hkv, B, Dk = k_pool.shape
     if Dk != D:
         raise ValueError("q and k_pool head_dim differ")
     dt = pa_dtype_of(q.dtype)
     odt = dt if out_dtype is None else pa_dtype_of(out_dtype)
-    return _lib.PaDesc(S, Hq, Hkv, D, B, NB, block_tables.shape[1], dt, odt, kernel)
+    return _lib.PaDesc(S, Hq, Hkv, D, B, NB, block_tables.shape[1], dt, odt, kernel,
+                       cached_prefix_blocks)
 
 
 def new_workspace(desc: _lib.PaDesc, device) -> torch.Tensor:
@@ -54,11 +57,14 @@ def new_workspace(desc: _lib.PaDesc, device) -> torch.Tensor:
 def decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, *,
            out: torch.Tensor | None = None, out_dtype: torch.dtype | None = torch.float32,
            kernel: int = _lib.PA_KERNEL_AUTO, workspace: torch.Tensor | None = None,
-           stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+           stream: torch.cuda.Stream | None = None, cached_prefix_blocks: int = 0
+           ) -> torch.Tensor:
     """Paged decode attention on device tensors; returns out [S][Hq][D].
 
     workspace: reuse one from new_workspace() to avoid an allocation per
     call (it must have been zero-filled once; the library keeps it so).
+    cached_prefix_blocks: cache hint for a prefix shared across the batch
+    (pa_desc.cached_prefix_blocks).
 
     k_pool [NB][Hkv][B][D] (token-major), v_pool [NB][Hkv][B/16][D][16]
     (transposed within 16-token groups), block_tables / seq_lens int32,
@@ -76,7 +82,8 @@ def decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, *,
     NB, Hkv, B, D = k_pool.shape
     if B % 16 != 0 or tuple(v_pool.shape) != (NB, Hkv, B // 16, D, 16):
         raise ValueError("v_pool must be [num_blocks][num_kv_heads][block_size/16][head_dim][16]")
-    desc = make_desc(q, k_pool, block_tables, out_dtype=out_dtype, kernel=kernel)
+    desc = make_desc(q, k_pool, block_tables, out_dtype=out_dtype, kernel=kernel,
+                     cached_prefix_blocks=cached_prefix_blocks)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     if workspace is None:

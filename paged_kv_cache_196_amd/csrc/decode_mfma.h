@@ -94,6 +94,7 @@ struct MfmaEngine {
   }
 
   // The sub-tile starting at slot s16 of physical block `phys`, KV head kvh.
+  template <int kPolicy>
   static __device__ __forceinline__ void load_tile(const Args& a, int kvh, int s16, int phys,
                                                    Tile& t) {
     const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
@@ -103,9 +104,9 @@ struct MfmaEngine {
     const int koff = (col * kD + 8 * grp) * 2;    // this lane's K bytes inside a sub-tile
     const int voff = (col * kSub + 4 * grp) * 2;  // this lane's V^T bytes inside a group
 #pragma unroll
-    for (int x = 0; x < 4; ++x) t.k[x] = tile_load16(rk, koff + 64 * x, s16 * kD * 2);
+    for (int x = 0; x < 4; ++x) t.k[x] = tile_load16<kPolicy>(rk, koff + 64 * x, s16 * kD * 2);
 #pragma unroll
-    for (int x = 0; x < 8; ++x) t.v[x] = tile_load8(rv, voff + 32 * x * kSub, s16 * kD * 2);
+    for (int x = 0; x < 8; ++x) t.v[x] = tile_load8<kPolicy>(rv, voff + 32 * x * kSub, s16 * kD * 2);
   }
 
   // Fold a sub-tile whose first `valid` tokens (1 .. 16) are attended into

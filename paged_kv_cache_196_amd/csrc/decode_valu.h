@@ -79,6 +79,7 @@ struct ValuEngine {
   }
 
   // The sub-tile starting at slot s16 of physical block `phys`, KV head kvh.
+  template <int kPolicy>
   static __device__ __forceinline__ void load_tile(const Args& a, int kvh, int s16, int phys,
                                                    Tile& t) {
     const int lane = threadIdx.x & 63, rlane = lane % RL, vlane = lane % RV;
@@ -89,10 +90,10 @@ struct ValuEngine {
     const int voff = ((lane / RV) * kSub + vlane * E) * T::kEsize;  // V bytes of load 0
 #pragma unroll
     for (int n = 0; n < NK; ++n)
-      t.k[n] = tile_load16(rk, koff + n * TPL * kD * T::kEsize, s16 * kD * T::kEsize);
+      t.k[n] = tile_load16<kPolicy>(rk, koff + n * TPL * kD * T::kEsize, s16 * kD * T::kEsize);
 #pragma unroll
     for (int n = 0; n < NV; ++n)
-      t.v[n] = tile_load16(rv, voff + n * DPL * kSub * T::kEsize, s16 * kD * T::kEsize);
+      t.v[n] = tile_load16<kPolicy>(rv, voff + n * DPL * kSub * T::kEsize, s16 * kD * T::kEsize);
   }
 
   // Fold a sub-tile whose first `valid` tokens (1 .. 16) are attended into

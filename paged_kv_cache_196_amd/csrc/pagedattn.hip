@@ -177,7 +177,8 @@ int64_t pa_blocks_for_len(int64_t len, int32_t block_size) {
 int32_t pa_check_desc(const pa_desc* d) {
   if (!d) return PA_ERR_NULL;
   if (d->num_seqs < 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0 ||
-      d->block_size <= 0 || d->num_blocks <= 0 || d->max_blocks_per_seq <= 0)
+      d->block_size <= 0 || d->num_blocks <= 0 || d->max_blocks_per_seq <= 0 ||
+      d->cached_prefix_blocks < 0)
     return PA_ERR_SHAPE;
   if (d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_SHAPE;
   if (pa_dtype_size(d->dtype) == 0) return PA_ERR_DTYPE;
@@ -280,6 +281,7 @@ static int32_t prepare(const void* q, const void* k_pool, const void* v_pool, co
   a->mbs = d->max_blocks_per_seq;
   a->nwg = g;
   a->out_f32 = d->out_dtype == PA_F32 ? 1 : 0;
+  a->cached_blocks = d->cached_prefix_blocks;
   *grid = g;
   return PA_OK;
 }

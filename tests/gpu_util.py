@@ -27,10 +27,10 @@ class Uploaded:
         self.bt = torch.from_numpy(w.block_tables).cuda()
         self.lens = torch.from_numpy(w.seq_lens).cuda()
 
-    def run(self, kernel="auto", out_dtype=torch.float32):
+    def run(self, kernel="auto", out_dtype=torch.float32, cached_prefix_blocks=0):
         k = pa.PA_KERNEL_AUTO if kernel == "auto" else KERNELS[kernel]
         out = pa.decode(self.q, self.k, self.v, self.bt, self.lens, float(self.w.scale),
-                        out_dtype=out_dtype, kernel=k)
+                        out_dtype=out_dtype, kernel=k, cached_prefix_blocks=cached_prefix_blocks)
         torch.cuda.synchronize()
         return out
 

@@ -1,6 +1,7 @@
 """The C ABI on the CPU: every declared symbol is exported, the host-side
 entry points behave as include/pagedattn.h states, and argument errors are
 reported before any device work.  No kernel is launched here."""
+import ctypes
 import json
 import os
 import re
@@ -88,11 +89,21 @@ def _desc(**kw):
     ("num_q_heads", 0, 2), ("num_kv_heads", 3, 2), ("num_seqs", -1, 2), ("block_size", 0, 2),
     ("num_blocks", 0, 2), ("max_blocks_per_seq", 0, 2), ("dtype", 5, 3), ("out_dtype", pa.PA_F16, 3),
     ("head_dim", 64, 4), ("block_size", 8, 4), ("block_size", 48, 4), ("kernel", 9, 4),
-    ("num_q_heads", 8 * 32, 4), ("num_seqs", 9000, 4),
+    ("num_q_heads", 8 * 32, 4), ("num_seqs", 9000, 4), ("cached_prefix_blocks", -1, 2),
 ])
 def test_descriptor_errors(lib, field, value, code):
     assert pa.pa_check_desc(_desc()) == 0
     assert pa.pa_check_desc(_desc(**{field: value})) == code
+
+
+def test_descriptor_fields_match_the_header():
+    """The ctypes descriptor mirrors include/pagedattn.h field for field."""
+    hdr = open(os.path.join(ROOT, "include", "pagedattn.h")).read()
+    body = re.search(r"typedef struct pa_desc \{(.*?)\} pa_desc;", hdr, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"int32_t\s+(\w+);", body)
+    assert fields == [n for n, _ in pa.PaDesc._fields_]
+    assert ctypes.sizeof(pa.PaDesc) == 4 * len(fields)
 
 
 def test_mfma_with_fp32_is_unsupported(lib):

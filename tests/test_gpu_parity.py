@@ -139,6 +139,24 @@ def test_block_permutation_gives_bitwise_equal_output(O):
         assert torch.equal(a.run(kern), b.run(kern)), kern
 
 
+@pytest.mark.parametrize("B", [16, 32])
+def test_cached_prefix_hint_changes_no_bits(O, B):
+    """The shared-prefix cache hint only selects the load cache policy:
+    identical bits with no hint, a hint covering the shared prefix, one
+    reaching past every sequence, and a block size of 32 (a 16-token
+    sub-tile in the second half of a cached block)."""
+    w = workload.build(name="prefix", dtype="bf16", seq_lens=[700, 40, 1333, 512, 97, 2048, 513, 64],
+                       num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=B, seed=21,
+                       prefix_group=4, prefix_blocks=512 // B)
+    up = Uploaded(w)
+    ref = O.run_workload(w)
+    for kern in ("valu", "mfma"):
+        base = up.run(kern)
+        assert max_err(base, ref) <= TOL["bf16"], kern
+        for hint in (512 // B, 3, 1 << 20):
+            assert torch.equal(up.run(kern, cached_prefix_blocks=hint), base), (kern, hint)
+
+
 def test_repeat_runs_are_bitwise_identical():
     w = workload.make(4, 13, batch=2, max_len=8192)
     up = Uploaded(w)

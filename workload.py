@@ -66,6 +66,7 @@ class Workload:
     v_pool: np.ndarray        # [NB][Hkv][B/16][D][16]
     scale: np.float32
     seed: int = 0
+    shared_prefix_blocks: int = 0  # leading logical blocks shared within prefix groups
 
     @property
     def num_seqs(self) -> int:
@@ -211,7 +212,8 @@ def build(*, name: str, dtype: str, seq_lens, num_q_heads: int, num_kv_heads: in
                     max_blocks_per_seq=int(max_blocks_per_seq),
                     seq_lens=lens.astype(np.int32), block_tables=bt, q=q,
                     k_pool=k_pool, v_pool=v_pool,
-                    scale=np.float32(1.0 / math.sqrt(head_dim)), seed=seed)
+                    scale=np.float32(1.0 / math.sqrt(head_dim)), seed=seed,
+                    shared_prefix_blocks=int(prefix_blocks) if prefix_group > 1 else 0)
 
 
 CONFIG_NAMES = {
