@@ -710,12 +710,16 @@ __device__ inline void stream_batch(const Args& a, typename Engine::Smem& sm) {
     auto row_phys = [&](const Cur& u) {
       return as_constant(a.bt + (int64_t)u.b * a.mbs)[(u.tb + kSub * u.j) / B];
     };
+    // The tile's address is wave-uniform; say so, so that the buffer
+    // resource stays in scalar registers whatever the compiler concludes
+    // about the cursor's control flow.
     auto load = [&](const Cur& u, int phys, Tile& t) {
-      const int tok = u.tb + kSub * u.j;
+      const int tok = uniform(u.tb + kSub * u.j), kvh = uniform(u.kvh);
+      phys = uniform(phys);
       if (tok / B < a.cached_blocks)
-        Engine::template load_tile<kCachedPolicy>(a, u.kvh, tok % B, phys, t);
+        Engine::template load_tile<kCachedPolicy>(a, kvh, tok % B, phys, t);
       else
-        Engine::template load_tile<kStreamPolicy>(a, u.kvh, tok % B, phys, t);
+        Engine::template load_tile<kStreamPolicy>(a, kvh, tok % B, phys, t);
     };
     // Each tile register carries (piece, valid tokens) of its sub-tile.
     int p0 = c.p, v0 = c.te - (c.tb + kSub * c.j);
@@ -769,6 +773,65 @@ __device__ inline void stream_batch(const Args& a, typename Engine::Smem& sm) {
   enter(npl, true);
 }
 
+// Lists the chunk's next batch of pieces (flat range [sm.next_f, e)) in
+// sm.plist with the 64 lanes of wave 0: lane t looks at the t-th
+// (sequence, KV head) pair after the one holding the batch's first block,
+// a ballot drops pairs of empty sequences and gives every piece its place,
+// and further rounds of 64 continue until the batch is full or the chunk
+// ends.  Pieces are contiguous in flat order, so the next batch starts
+// where the last listed piece ends.
+template <int B, class Smem>
+__device__ inline void list_batch(const Args& a, Smem& sm, const int* cum, const int* lens_s, int s,
+                                  int e, int chunk, int c) {
+  const int lane = threadIdx.x & 63;
+  const int f0 = uniform(sm.next_f);
+  if (lane == 0) {
+    sm.npl = 0;
+    sm.next_f = e;
+  }
+  if (f0 >= e) return;
+  const int b0 = uniform(find_seq(cum, a.S, a.Hkv, f0));
+  const int nb0 = cum[b0 + 1] - cum[b0];
+  const int kvh0 = uniform((f0 - cum[b0] * a.Hkv) / nb0);
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  int n = 0;
+  for (int lin = kvh0; n < Smem::kBatch; lin += 64) {
+    const int L = lin + lane;
+    const int b = b0 + L / a.Hkv, kvh = L % a.Hkv;
+    int nb = 0, ustart = 0;
+    if (b < a.S) {
+      nb = cum[b + 1] - cum[b];
+      ustart = cum[b] * a.Hkv + kvh * nb;
+    }
+    const bool past = b >= a.S || (nb > 0 && ustart >= e);
+    const bool ok = !past && nb > 0;
+    const uint64_t okm = __builtin_amdgcn_ballot_w64(ok);
+    const int idx = n + __builtin_popcountll(okm & below);
+    if (ok && idx < Smem::kBatch) {
+      const int f = L == kvh0 ? f0 : ustart;
+      const int pe = min(e, ustart + nb);
+      const int j0 = f - ustart, j1 = pe - ustart;
+      Piece pc;
+      pc.b = b;
+      pc.kvh = kvh;
+      pc.L = lens_s[b];
+      pc.tok_begin = j0 * B;
+      pc.tok_end = min(j1 * B, pc.L);
+      pc.nsub = (pc.tok_end - pc.tok_begin + kSub - 1) / kSub;
+      pc.kind = (j0 == 0 && j1 == nb) ? kWhole : (f == s && pe < e) ? kEarly : kLate;
+      pc.slot = 2 * chunk + (f == s ? 0 : 1);
+      pc.kfirst = ustart / c;
+      pc.npieces = (ustart + nb - 1) / c - pc.kfirst + 1;
+      pc.first_slot = 2 * pc.kfirst + (ustart != pc.kfirst * c ? 1 : 0);
+      sm.plist[idx] = pc;
+      if (idx == Smem::kBatch - 1) sm.next_f = pe;
+    }
+    n += __builtin_popcountll(okm);
+    if (__builtin_amdgcn_ballot_w64(past) != 0) break;
+  }
+  if (lane == 0) sm.npl = min(n, Smem::kBatch);
+}
+
 template <class T, int B, int G, class Engine>
 __device__ inline void run_decode(const Args& a) {
   using Smem = typename Engine::Smem;
@@ -793,33 +856,7 @@ __device__ inline void run_decode(const Args& a) {
   __syncthreads();
   constexpr int kQChunks = G * kD * T::kEsize / 16;  // 16-byte chunks per query group
   while (true) {
-    if (threadIdx.x == 0) {
-      int f = sm.next_f, n = 0;
-      while (f < e && n < Smem::kBatch) {
-        Piece pc;
-        pc.b = find_seq(cum, a.S, a.Hkv, f);
-        const int nb = cum[pc.b + 1] - cum[pc.b];
-        const int base = cum[pc.b] * a.Hkv;
-        pc.kvh = (f - base) / nb;
-        const int j0 = (f - base) - pc.kvh * nb;
-        const int ustart = base + pc.kvh * nb;
-        const int pe = min(e, ustart + nb);
-        const int j1 = j0 + (pe - f);
-        pc.L = lens_s[pc.b];
-        pc.tok_begin = j0 * B;
-        pc.tok_end = min(j1 * B, pc.L);
-        pc.nsub = (pc.tok_end - pc.tok_begin + kSub - 1) / kSub;
-        pc.kind = (j0 == 0 && j1 == nb) ? kWhole : (f == s && pe < e) ? kEarly : kLate;
-        pc.slot = 2 * chunk + (f == s ? 0 : 1);
-        pc.kfirst = ustart / c;
-        pc.npieces = (ustart + nb - 1) / c - pc.kfirst + 1;
-        pc.first_slot = 2 * pc.kfirst + (ustart != pc.kfirst * c ? 1 : 0);
-        sm.plist[n++] = pc;
-        f = pe;
-      }
-      sm.npl = n;
-      sm.next_f = f;
-    }
+    if (threadIdx.x < 64) list_batch<B>(a, sm, cum, lens_s, s, e, chunk, c);
     __syncthreads();
     const int npl = sm.npl;
     if (npl == 0) break;
