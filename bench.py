@@ -153,6 +153,71 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, wor
     return 0
 
 
+PROBE_SRC = os.path.join(ROOT, "bench_read_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "bench_read_probe.so")
+
+
+def build_read_probe(verbose: bool = False) -> str:
+    """hipcc bench_read_probe.hip -> bench_read_probe.so (gfx950)."""
+    import subprocess
+    from paged_kv_cache_196_amd import build as hipbuild
+    tmp = PROBE_LIB + f".tmp{os.getpid()}"
+    cmd = [hipbuild.hipcc(), f"--offload-arch={hipbuild.ARCH}", "-O3", "-std=c++17", "-fPIC",
+           "-shared", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + r.stderr)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
+def read_probe(flush, dev, reps: int = 10) -> dict:
+    """Best streaming-read rate on this device: bench_read_probe.hip over a
+    separate 1 GiB buffer for a few grid sizes and both load policies, the
+    flush run before each rep so that no part of the probe buffer is still
+    cached.  Reported: the best median."""
+    import ctypes
+    import torch
+    if not os.path.exists(PROBE_LIB):
+        build_read_probe()
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.pa_bench_read_probe.restype = ctypes.c_int
+    lib.pa_bench_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    nbytes = 1 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    grids = (1024, 2048, 4096, 8192)
+    sink = torch.zeros(max(grids), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    best = None
+    for variant in (0, 1):
+        for grid in grids:
+            ms = []
+            for i in range(reps + 2):
+                flush()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                rc = lib.pa_bench_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), grid, variant,
+                                             stream.cuda_stream)
+                e1.record(stream)
+                if rc != 0:
+                    raise RuntimeError(f"read probe launch failed: {rc}")
+                e1.synchronize()
+                if i >= 2:
+                    ms.append(e0.elapsed_time(e1))
+            med = statistics.median(ms)
+            if best is None or med < best[0]:
+                best = (med, grid, variant)
+    del buf, sink
+    med, grid, variant = best
+    return {"kernel": "bench_read_probe.hip: 16-byte loads, 8 in flight per lane",
+            "bytes": nbytes, "grid": grid, "loads": "nontemporal" if variant else "default",
+            "ms_median": round(med, 5), "gbps": round(nbytes / (med * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(w, kv_bytes: int, budget_s: float) -> dict:
     import oracle
     O = oracle.load()
@@ -191,8 +256,8 @@ def cpu_baseline(w, kv_bytes: int, budget_s: float) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--kernel", choices=["auto", "valu", "mfma"], default="auto")
@@ -202,6 +267,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the oracle spot check")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-read-probe", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the calibration copy (for rocprofv3 counter scaling)")
     ap.add_argument("--summarize-counters", nargs=4, metavar="DIR",
@@ -304,6 +370,7 @@ def main() -> int:
 
     src_hash = kernel_source_hash()
     traffic = read_traffic(src_hash, kname, w.name)
+    probe = None if args.no_read_probe else read_probe(flush, dev)
 
     result = {
         "metric": METRIC,
@@ -340,6 +407,9 @@ def main() -> int:
         "tokens_per_s": round(w.num_seqs / (t_step * 1e-3), 1),
         "kv_bytes": kv_unique,
         "kv_bytes_logical": kv_logical,
+        "kv_gbps_logical": round(kv_logical / (t_step * 1e-3) / 1e9, 2),
+        "read_probe": probe,
+        "frac_of_read_probe": round(kv_gbps / probe["gbps"], 4) if probe else None,
         "ms": {
             "step_mean": round(t_step, 5), "step_median": round(statistics.median(tot_ms), 5),
             "step_p10": round(sorted(tot_ms)[len(tot_ms) // 10], 5),

@@ -523,6 +523,8 @@ __device__ inline void finish_late(const Args& a, MergeSmem<T, G>& sm, const Pie
   bool fold = uniform(sm.seen) == pc.npieces - 1;
   if (fold) {
     if (threadIdx.x == 0) reset_count(cnt);
+    // merge_waves of every wave reads sm.m[0] / sm.l[0], overwritten below
+    __syncthreads();
   } else {
     store_partial<G>(a, pc.slot, pt);
     drain_vmem();
