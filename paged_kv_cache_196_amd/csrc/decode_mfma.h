@@ -96,11 +96,11 @@ struct MfmaEngine {
   // The sub-tile starting at slot s16 of physical block `phys`, KV head kvh.
   template <int kPolicy>
   static __device__ __forceinline__ void load_tile(const Args& a, int kvh, int s16, int phys,
-                                                   Tile& t) {
+                                                   int bytes, Tile& t) {
     const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
     const int64_t tile = ((int64_t)phys * a.Hkv + kvh) * kTileBytes;
-    const auto rk = tile_rsrc(a.kp, tile, kTileBytes);
-    const auto rv = tile_rsrc(a.vp, tile, kTileBytes);
+    const auto rk = tile_rsrc(a.kp, tile, bytes);
+    const auto rv = tile_rsrc(a.vp, tile, bytes);
     const int koff = (col * kD + 8 * grp) * 2;    // this lane's K bytes inside a sub-tile
     const int voff = (col * kSub + 4 * grp) * 2;  // this lane's V^T bytes inside a group
 #pragma unroll

@@ -81,11 +81,11 @@ struct ValuEngine {
   // The sub-tile starting at slot s16 of physical block `phys`, KV head kvh.
   template <int kPolicy>
   static __device__ __forceinline__ void load_tile(const Args& a, int kvh, int s16, int phys,
-                                                   Tile& t) {
+                                                   int bytes, Tile& t) {
     const int lane = threadIdx.x & 63, rlane = lane % RL, vlane = lane % RV;
     const int64_t tile = ((int64_t)phys * a.Hkv + kvh) * kTileBytes;
-    const auto rk = tile_rsrc(a.kp, tile, kTileBytes);
-    const auto rv = tile_rsrc(a.vp, tile, kTileBytes);
+    const auto rk = tile_rsrc(a.kp, tile, bytes);
+    const auto rv = tile_rsrc(a.vp, tile, bytes);
     const int koff = ((lane / RL) * kD + rlane * E) * T::kEsize;    // K bytes of load 0
     const int voff = ((lane / RV) * kSub + vlane * E) * T::kEsize;  // V bytes of load 0
 #pragma unroll

@@ -640,8 +640,9 @@ __device__ inline void zero_empty_sequences(const Args& a, int chunk, const int*
 // finishes the pieces in between (finish_piece; every wave finishes every
 // piece, in order, so their barriers pair up), and the loads already in
 // flight keep streaming meanwhile.  Past the end of its share a wave
-// re-reads its last sub-tile (never computed), so every load is issued
-// unconditionally and the compiler waits for exactly the one it consumes.
+// issues the same loads at its last sub-tile through an empty resource (no
+// memory access, never computed), so every load is issued unconditionally
+// and the compiler waits for exactly the one it consumes.
 
 // Arrival count of a late two-piece split, read by thread 0 as its waves
 // finish streaming (the load overlaps the wave merge); -1 otherwise.  Splits
@@ -708,29 +709,34 @@ __device__ inline void stream_batch(const Args& a, typename Engine::Smem& sm) {
   };
 
   if (c.p < npl) {
-    Cur last = c;  // last position inside the batch (re-read past the end)
+    Cur last = c;  // last position inside the batch (address of the empty loads past the end)
     auto row_phys = [&](const Cur& u) {
       return as_constant(a.bt + (int64_t)u.b * a.mbs)[(u.tb + kSub * u.j) / B];
     };
     // The tile's address is wave-uniform; say so, so that the buffer
     // resource stays in scalar registers whatever the compiler concludes
     // about the cursor's control flow.
-    auto load = [&](const Cur& u, int phys, Tile& t) {
+    // A load past the end of the wave's share (live = false) keeps the
+    // instruction stream unconditional but goes through a resource of zero
+    // bytes: the range check drops every lane's access, so it returns zeros
+    // without touching memory.
+    auto load = [&](const Cur& u, int phys, bool live, Tile& t) {
       const int tok = uniform(u.tb + kSub * u.j), kvh = uniform(u.kvh);
       phys = uniform(phys);
+      const int bytes = uniform(live ? B * kD * T::kEsize : 0);
       if (tok / B < a.cached_blocks)
-        Engine::template load_tile<kCachedPolicy>(a, kvh, tok % B, phys, t);
+        Engine::template load_tile<kCachedPolicy>(a, kvh, tok % B, phys, bytes, t);
       else
-        Engine::template load_tile<kStreamPolicy>(a, kvh, tok % B, phys, t);
+        Engine::template load_tile<kStreamPolicy>(a, kvh, tok % B, phys, bytes, t);
     };
     // Each tile register carries (piece, valid tokens) of its sub-tile.
     int p0 = c.p, v0 = c.te - (c.tb + kSub * c.j);
     Tile t0, t1;
-    load(c, row_phys(c), t0);
+    load(c, row_phys(c), true, t0);
     advance(c);
     if (c.p < npl) last = c;
     int p1 = c.p, v1 = c.te - (c.tb + kSub * c.j);
-    load(last, row_phys(last), t1);
+    load(last, row_phys(last), c.p < npl, t1);
     advance(c);
     if (c.p < npl) last = c;
     int ph = row_phys(last);
@@ -741,13 +747,13 @@ __device__ inline void stream_batch(const Args& a, typename Engine::Smem& sm) {
     auto refill = [&](Tile& t, int& pn, int& vn) {
       pn = c.p;
       vn = c.te - (c.tb + kSub * c.j);
-      load(last, ph, t);
+      load(last, ph, c.p < npl, t);
       advance(c);
       if (c.p < npl) last = c;
       ph = row_phys(last);
     };
-    // Every pass through the body refills t0 and then t1 (a re-read when
-    // past the end), so the loads in flight at the top of the loop are
+    // Every pass through the body refills t0 and then t1 (an empty load
+    // when past the end), so the loads in flight at the top of the loop are
     // always t0's followed by t1's and the compiler's wait before each
     // compute covers exactly that tile.  The loop leaves only at the
     // bottom.
