@@ -184,6 +184,73 @@ int32_t paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
  * current device (the split-K granularity), or -1 on error. */
 int32_t pa_decode_grid(const pa_desc* desc);
 
+/* ------------------------------------------------------------------
+ * Writing the cache: the steps around the decode call on the same layout.
+ * ------------------------------------------------------------------ */
+
+/* Append one new token per sequence.  For every sequence b with
+ * t = positions[b] >= 0, the token's key and value rows of every KV head
+ * are written to logical slot t of the sequence: physical block
+ * block_tables[b][t / block_size], slot t % block_size, in the pool
+ * layouts above.  The block table maps logical blocks to physical ones,
+ * so the writer follows it exactly like the reader, and only a sequence's
+ * last block is ever partly filled ("PagedAttention: The Cache Was Storing
+ * Nothing", §2.2 "Borrowing paging from the 1960s").  For the usual decode
+ * step positions[b] = seq_lens[b] before the step (the caller grows the
+ * table by one block first when t % block_size == 0); positions[b] < 0
+ * writes nothing for b.
+ *
+ *   k_new, v_new  [num_seqs][num_kv_heads][head_dim]  dtype, device
+ *   k_pool, v_pool, block_tables                    as above, device
+ *   positions     int32 [num_seqs], device
+ *
+ * Uses num_seqs, num_kv_heads, head_dim, block_size, num_blocks,
+ * max_blocks_per_seq and dtype of `desc` (which must pass pa_check_desc).
+ * One kernel launch on `stream`; every other pool byte is left as it was.
+ * Data-dependent preconditions are not checked on the device (see
+ * pa_validate_append_host): t < max_blocks_per_seq*block_size, the table
+ * entry in [0, num_blocks), and no two sequences of one call writing the
+ * same (block, slot) -- such a pair races and either value may land.
+ * Returns PA_OK, a descriptor error, PA_ERR_NULL, PA_ERR_ALIGN (pointers
+ * not 16-byte aligned), PA_ERR_DEVICE or PA_ERR_LAUNCH. */
+int32_t paged_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                        const int32_t* block_tables, const int32_t* positions,
+                        const pa_desc* desc, void* stream);
+
+/* Host check of paged_kv_append's data-dependent preconditions on HOST
+ * copies: every positions[b] >= 0 below max_blocks_per_seq*block_size,
+ * its table entry in [0, num_blocks), and (block, slot) targets pairwise
+ * distinct.  PA_OK, a descriptor error, PA_ERR_NULL or PA_ERR_TABLE. */
+int32_t pa_validate_append_host(const pa_desc* desc, const int32_t* block_tables_host,
+                                const int32_t* positions_host);
+
+/* Copy whole physical blocks, the copy-on-write step of block sharing: a
+ * shared block is copied only when one of the sequences pointing at it
+ * diverges and writes into it ("PagedAttention: The Cache Was Storing
+ * Nothing", §2.3 "What the table buys that reservations could not").
+ * For i < num_pairs, block dst_blocks[i] of both pools becomes a copy of
+ * block src_blocks[i] (every KV head, every slot: one contiguous
+ * num_kv_heads*block_size*head_dim*esize-byte range per pool).  The
+ * caller then points the diverging sequence's table entry at the copy.
+ *
+ *   src_blocks, dst_blocks  int32 [num_pairs], device
+ *
+ * num_pairs == 0 launches nothing.  One kernel launch on `stream`.
+ * Preconditions not checked on the device (see pa_validate_copy_host):
+ * ids in [0, num_blocks), destinations pairwise distinct and none of
+ * them also a source (otherwise the result depends on the order of the
+ * copies).  Returns PA_OK, a descriptor error, PA_ERR_SHAPE (num_pairs <
+ * 0), PA_ERR_NULL, PA_ERR_ALIGN, PA_ERR_DEVICE or PA_ERR_LAUNCH. */
+int32_t paged_kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_blocks,
+                             const int32_t* dst_blocks, int32_t num_pairs,
+                             const pa_desc* desc, void* stream);
+
+/* Host check of paged_kv_copy_blocks' preconditions on HOST copies of the
+ * id lists.  PA_OK, a descriptor error, PA_ERR_SHAPE, PA_ERR_NULL or
+ * PA_ERR_TABLE. */
+int32_t pa_validate_copy_host(const pa_desc* desc, const int32_t* src_blocks_host,
+                              const int32_t* dst_blocks_host, int32_t num_pairs);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,5 +1,7 @@
 /*
- * oracle.c — plain fp64 CPU oracle for single-token paged decode attention.
+ * oracle.c — plain fp64 CPU oracle for single-token paged decode attention,
+ * and the plain byte-level definition of the two cache writes around it
+ * (appending a decode token, copy-on-write block copy; end of this file).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or
  * calls this file: only the test suite, the smoke check and the CPU-baseline
@@ -249,4 +251,67 @@ int oracle_max_threads(void) {
 #else
   return 1;
 #endif
+}
+
+/* ------------------------------------------------------------------
+ * Writing the cache (pure data movement: element bits are copied, never
+ * converted, so the oracle works on raw bytes of `esize` per element).
+ * ------------------------------------------------------------------ */
+
+/* Append one token per sequence ("PagedAttention: The Cache Was Storing
+ * Nothing", §2.2: the block table maps logical blocks to physical ones;
+ * only the last block of a request is partly filled).  For every sequence
+ * b with t = positions[b] >= 0: the key row k_new[b][g][:] of every KV
+ * head g is written at logical position t, i.e. physical block
+ * block_tables[b][t / B], slot t % B, of k_pool, and v_new[b][g][:] at the
+ * same place of v_pool.  Sequences are handled in order b = 0, 1, ...
+ * Layout as restated at the top of this file: K element (slot, d) of a
+ * tile at slot*D + d, V element at (slot/16)*D*16 + d*16 + slot%16.
+ * Returns 0, or -1 if a position or a table entry is out of range
+ * (nothing more is written then). */
+int oracle_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                  const int32_t* block_tables, const int32_t* positions, int32_t num_seqs,
+                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                  int32_t num_blocks, int32_t max_blocks_per_seq, int32_t esize) {
+  const int64_t D = head_dim, B = block_size, H = num_kv_heads;
+  const int64_t G = (B % 16 == 0) ? 16 : B; /* tokens per transposed V group */
+  for (int64_t b = 0; b < num_seqs; ++b) {
+    const int64_t t = positions[b];
+    if (t < 0) continue;
+    const int64_t j = t / B, slot = t % B;
+    if (j >= max_blocks_per_seq) return -1;
+    const int64_t phys = block_tables[b * max_blocks_per_seq + j];
+    if (phys < 0 || phys >= num_blocks) return -1;
+    for (int64_t g = 0; g < H; ++g) {
+      const int64_t tile = (phys * H + g) * B * D;
+      const int64_t src = (b * H + g) * D;
+      for (int64_t d = 0; d < D; ++d) {
+        const int64_t kdst = tile + slot * D + d;
+        const int64_t vdst = tile + (slot / G) * D * G + d * G + slot % G;
+        memcpy((char*)k_pool + kdst * esize, (const char*)k_new + (src + d) * esize, esize);
+        memcpy((char*)v_pool + vdst * esize, (const char*)v_new + (src + d) * esize, esize);
+      }
+    }
+  }
+  return 0;
+}
+
+/* Copy-on-write block copy (same page, §2.3: a shared block is copied only
+ * when a sequence diverges and writes into it).  For i = 0 .. n-1 in
+ * order, physical block dst[i] of each pool becomes a copy of block
+ * src[i]: all KV heads and slots, i.e. the block_bytes = Hkv*B*D*esize
+ * bytes starting at block*block_bytes.  Returns 0, or -1 if an id is out
+ * of range (nothing more is copied then). */
+int oracle_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst,
+                       int32_t n, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t num_blocks, int32_t esize) {
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * esize;
+  for (int32_t i = 0; i < n; ++i) {
+    if (src[i] < 0 || src[i] >= num_blocks || dst[i] < 0 || dst[i] >= num_blocks) return -1;
+    memmove((char*)k_pool + dst[i] * block_bytes, (const char*)k_pool + src[i] * block_bytes,
+            block_bytes);
+    memmove((char*)v_pool + dst[i] * block_bytes, (const char*)v_pool + src[i] * block_bytes,
+            block_bytes);
+  }
+  return 0;
 }

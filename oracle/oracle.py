@@ -77,6 +77,11 @@ class Oracle:
         lib.oracle_paged_decode.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                             _I32, _I32, _I32, _I32, _D, _P, _I32]
         lib.oracle_paged_decode.restype = ctypes.c_int
+        lib.oracle_append.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                      _I32, _I32]
+        lib.oracle_append.restype = ctypes.c_int
+        lib.oracle_copy_blocks.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32]
+        lib.oracle_copy_blocks.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -172,6 +177,36 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"oracle_paged_decode failed with code {rc}")
         return out
+
+    def append(self, k_new, v_new, k_pool, v_pool, block_tables, positions):
+        """New pools (copies) after appending k_new / v_new [S][Hkv][D] at
+        logical slot positions[b] of every sequence (skipped where < 0).
+        Pools as in paged_decode (raw storage); the inputs are not modified."""
+        kp = np.array(k_pool, copy=True, order="C")
+        vp = np.array(v_pool, copy=True, order="C")
+        kn = _c(k_new)
+        vn = _c(v_new)
+        bt = _c(block_tables, np.int32)
+        pos = _c(positions, np.int32)
+        NB, Hkv, B, D = kp.shape
+        rc = self.lib.oracle_append(_ptr(kn), _ptr(vn), _ptr(kp), _ptr(vp), _ptr(bt), _ptr(pos),
+                                    pos.shape[0], Hkv, D, B, NB, bt.shape[1], kp.itemsize)
+        if rc != 0:
+            raise ValueError("oracle_append: position or table entry out of range")
+        return kp, vp
+
+    def copy_blocks(self, k_pool, v_pool, src, dst):
+        """New pools (copies) after block dst[i] <- block src[i] in both."""
+        kp = np.array(k_pool, copy=True, order="C")
+        vp = np.array(v_pool, copy=True, order="C")
+        s = _c(src, np.int32)
+        d = _c(dst, np.int32)
+        NB, Hkv, B, D = kp.shape
+        rc = self.lib.oracle_copy_blocks(_ptr(kp), _ptr(vp), _ptr(s), _ptr(d), s.shape[0], Hkv, D,
+                                         B, NB, kp.itemsize)
+        if rc != 0:
+            raise ValueError("oracle_copy_blocks: block id out of range")
+        return kp, vp
 
     def run_workload(self, w, num_threads: int = 0) -> np.ndarray:
         """paged_decode on a workload.Workload-like object."""

@@ -1,5 +1,7 @@
 """gfx950 paged decode attention: a C-ABI library (libpagedattn.so) and its
-thin Python binding.
+thin Python binding.  Besides the decode call the library writes the cache
+in its own layout: one appended token per sequence, and whole-block copies
+for copy-on-write sharing.
 
 ``_lib`` mirrors the C ABI (include/pagedattn.h) name for name; ``api``
 adds torch-tensor conveniences (descriptor from shapes, workspace and
@@ -23,9 +25,13 @@ from ._lib import (  # noqa: F401
     pa_k_elem_offset,
     pa_pool_bytes,
     pa_v_elem_offset,
+    pa_validate_append_host,
+    pa_validate_copy_host,
     pa_validate_host,
     pa_workspace_bytes,
     paged_attn_decode,
+    paged_kv_append,
+    paged_kv_copy_blocks,
     status_str,
 )
-from .api import decode, ensure_built, make_desc, new_workspace  # noqa: F401
+from .api import append, copy_blocks, decode, ensure_built, make_desc, new_workspace  # noqa: F401

@@ -23,7 +23,8 @@ PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
 EXPORTS = (
     "pa_status_str", "pa_dtype_size", "pa_blocks_for_len", "pa_pool_bytes", "pa_k_elem_offset",
     "pa_v_elem_offset", "pa_workspace_bytes", "pa_validate_host", "pa_check_desc",
-    "paged_attn_decode", "pa_decode_grid",
+    "paged_attn_decode", "pa_decode_grid", "paged_kv_append", "pa_validate_append_host",
+    "paged_kv_copy_blocks", "pa_validate_copy_host",
 )
 
 
@@ -79,6 +80,14 @@ def load() -> ctypes.CDLL:
             lib.paged_attn_decode.restype = ctypes.c_int32
             lib.pa_decode_grid.argtypes = [_DP]
             lib.pa_decode_grid.restype = ctypes.c_int32
+            lib.paged_kv_append.argtypes = [_P, _P, _P, _P, _P, _P, _DP, _P]
+            lib.paged_kv_append.restype = ctypes.c_int32
+            lib.pa_validate_append_host.argtypes = [_DP, _P, _P]
+            lib.pa_validate_append_host.restype = ctypes.c_int32
+            lib.paged_kv_copy_blocks.argtypes = [_P, _P, _P, _P, ctypes.c_int32, _DP, _P]
+            lib.paged_kv_copy_blocks.restype = ctypes.c_int32
+            lib.pa_validate_copy_host.argtypes = [_DP, _P, _P, ctypes.c_int32]
+            lib.pa_validate_copy_host.restype = ctypes.c_int32
             _lib = lib
     return _lib
 
@@ -149,3 +158,32 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, o
                                   _ptr(seq_lens), float(scale), _ptr(out), ctypes.byref(desc),
                                   _ptr(workspace), int(workspace_bytes), _ptr(stream))
     return _check(rc, "paged_attn_decode")
+
+
+def paged_kv_append(k_new, v_new, k_pool, v_pool, block_tables, positions, desc: PaDesc,
+                    stream=None) -> int:
+    rc = load().paged_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+                                _ptr(block_tables), _ptr(positions), ctypes.byref(desc),
+                                _ptr(stream))
+    return _check(rc, "paged_kv_append")
+
+
+def pa_validate_append_host(desc: PaDesc, block_tables_host, positions_host) -> int:
+    """block_tables_host / positions_host: contiguous int32 numpy arrays."""
+    return int(load().pa_validate_append_host(ctypes.byref(desc), block_tables_host.ctypes.data,
+                                              positions_host.ctypes.data))
+
+
+def paged_kv_copy_blocks(k_pool, v_pool, src_blocks, dst_blocks, num_pairs: int, desc: PaDesc,
+                         stream=None) -> int:
+    rc = load().paged_kv_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(src_blocks),
+                                     _ptr(dst_blocks), int(num_pairs), ctypes.byref(desc),
+                                     _ptr(stream))
+    return _check(rc, "paged_kv_copy_blocks")
+
+
+def pa_validate_copy_host(desc: PaDesc, src_host, dst_host, num_pairs: int) -> int:
+    """src_host / dst_host: contiguous int32 numpy arrays (or None when num_pairs is 0)."""
+    return int(load().pa_validate_copy_host(
+        ctypes.byref(desc), None if src_host is None else src_host.ctypes.data,
+        None if dst_host is None else dst_host.ctypes.data, int(num_pairs)))

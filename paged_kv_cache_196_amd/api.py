@@ -93,3 +93,65 @@ def decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, *,
                            workspace, workspace.numel() * workspace.element_size(),
                            st.cuda_stream)
     return out
+
+
+def _pool_desc(k_pool: torch.Tensor, v_pool: torch.Tensor, block_tables: torch.Tensor,
+               num_seqs: int) -> _lib.PaDesc:
+    """Descriptor for the cache-writing calls (they use the pool and table
+    shapes; the query-head count is set to the KV-head count)."""
+    for name, t in (("k_pool", k_pool), ("v_pool", v_pool), ("block_tables", block_tables)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if block_tables.dtype != torch.int32:
+        raise TypeError("block_tables must be int32")
+    if v_pool.dtype != k_pool.dtype:
+        raise TypeError("k_pool and v_pool must share a dtype")
+    NB, Hkv, B, D = k_pool.shape
+    if B % 16 != 0 or tuple(v_pool.shape) != (NB, Hkv, B // 16, D, 16):
+        raise ValueError("v_pool must be [num_blocks][num_kv_heads][block_size/16][head_dim][16]")
+    dt = pa_dtype_of(k_pool.dtype)
+    return _lib.PaDesc(num_seqs, Hkv, Hkv, D, B, NB, block_tables.shape[1], dt, _lib.PA_F32,
+                       _lib.PA_KERNEL_AUTO, 0)
+
+
+def append(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+           block_tables: torch.Tensor, positions: torch.Tensor, *,
+           stream: torch.cuda.Stream | None = None) -> None:
+    """Write one new token per sequence in place: k_new / v_new
+    [S][Hkv][D] go to logical slot positions[b] of sequence b (skipped
+    where positions[b] < 0) through its block table."""
+    S = positions.shape[0]
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("positions", positions)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if positions.dtype != torch.int32:
+        raise TypeError("positions must be int32")
+    desc = _pool_desc(k_pool, v_pool, block_tables, S)
+    want = (S, desc.num_kv_heads, desc.head_dim)
+    if tuple(k_new.shape) != want or tuple(v_new.shape) != want:
+        raise ValueError(f"k_new and v_new must be {list(want)}")
+    if k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype:
+        raise TypeError("k_new, v_new and the pools must share a dtype")
+    if block_tables.shape[0] != S:
+        raise ValueError("block_tables needs one row per sequence")
+    st = stream if stream is not None else torch.cuda.current_stream(k_pool.device)
+    _lib.paged_kv_append(k_new, v_new, k_pool, v_pool, block_tables, positions, desc,
+                         st.cuda_stream)
+
+
+def copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, src_blocks: torch.Tensor,
+                dst_blocks: torch.Tensor, *, stream: torch.cuda.Stream | None = None) -> None:
+    """Copy-on-write step: physical block dst_blocks[i] of both pools
+    becomes a copy of src_blocks[i] (int32 device tensors of one length)."""
+    n = src_blocks.shape[0]
+    if dst_blocks.shape[0] != n:
+        raise ValueError("src_blocks and dst_blocks differ in length")
+    for name, t in (("src_blocks", src_blocks), ("dst_blocks", dst_blocks)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.int32:
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    table = torch.zeros((1, 1), dtype=torch.int32, device=k_pool.device)
+    desc = _pool_desc(k_pool, v_pool, table, 1)
+    st = stream if stream is not None else torch.cuda.current_stream(k_pool.device)
+    _lib.paged_kv_copy_blocks(k_pool, v_pool, src_blocks, dst_blocks, n, desc, st.cuda_stream)

@@ -12,11 +12,13 @@
 
 #include <mutex>
 #include <string.h>
+#include <unordered_set>
 
 #include "pagedattn.h"
 #include "pa_device.h"
 #include "decode_mfma.h"
 #include "decode_valu.h"
+#include "kv_write.h"
 
 namespace pa {
 
@@ -297,6 +299,98 @@ int32_t paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
   if (v.launch(a, grid, prefix_lds(a.S), static_cast<hipStream_t>(stream)) != hipSuccess)
     return PA_ERR_LAUNCH;
   return PA_OK;
+}
+
+int32_t pa_validate_append_host(const pa_desc* d, const int32_t* bt, const int32_t* pos) {
+  const int32_t st = pa_check_desc(d);
+  if (st != PA_OK) return st;
+  if (d->num_seqs > 0 && (!bt || !pos)) return PA_ERR_NULL;
+  const int64_t cap = (int64_t)d->max_blocks_per_seq * d->block_size;
+  std::unordered_set<int64_t> seen;
+  for (int32_t b = 0; b < d->num_seqs; ++b) {
+    const int32_t t = pos[b];
+    if (t < 0) continue;
+    if (t >= cap) return PA_ERR_TABLE;
+    const int32_t id = bt[(int64_t)b * d->max_blocks_per_seq + t / d->block_size];
+    if (id < 0 || id >= d->num_blocks) return PA_ERR_TABLE;
+    if (!seen.insert((int64_t)id * d->block_size + t % d->block_size).second) return PA_ERR_TABLE;
+  }
+  return PA_OK;
+}
+
+int32_t paged_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                        const int32_t* bt, const int32_t* pos, const pa_desc* d, void* stream) {
+  const int32_t st = pa_check_desc(d);
+  if (st != PA_OK) return st;
+  if (d->num_seqs == 0) return PA_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool || !bt || !pos) return PA_ERR_NULL;
+  if (((uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_pool | (uintptr_t)v_pool) & 15u)
+    return PA_ERR_ALIGN;
+  if (!device_info().ok) return PA_ERR_DEVICE;
+  AppendArgs a;
+  a.kn = k_new;
+  a.vn = v_new;
+  a.kp = k_pool;
+  a.vp = v_pool;
+  a.bt = bt;
+  a.pos = pos;
+  a.S = d->num_seqs;
+  a.Hkv = d->num_kv_heads;
+  a.B = d->block_size;
+  a.mbs = d->max_blocks_per_seq;
+  const int grid = (int)(((int64_t)a.S * a.Hkv + kWaves - 1) / kWaves);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (pa_dtype_size(d->dtype) == 4)
+    hipLaunchKernelGGL(append_kernel<4>, dim3(grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(append_kernel<2>, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int32_t pa_validate_copy_host(const pa_desc* d, const int32_t* src, const int32_t* dst,
+                              int32_t n) {
+  const int32_t st = pa_check_desc(d);
+  if (st != PA_OK) return st;
+  if (n < 0) return PA_ERR_SHAPE;
+  if (n > 0 && (!src || !dst)) return PA_ERR_NULL;
+  std::unordered_set<int32_t> dsts, srcs;
+  for (int32_t i = 0; i < n; ++i) {
+    if (src[i] < 0 || src[i] >= d->num_blocks || dst[i] < 0 || dst[i] >= d->num_blocks)
+      return PA_ERR_TABLE;
+    if (!dsts.insert(dst[i]).second) return PA_ERR_TABLE;
+    srcs.insert(src[i]);
+  }
+  for (int32_t x : dsts)
+    if (srcs.count(x)) return PA_ERR_TABLE;
+  return PA_OK;
+}
+
+int32_t paged_kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst,
+                             int32_t n, const pa_desc* d, void* stream) {
+  const int32_t st = pa_check_desc(d);
+  if (st != PA_OK) return st;
+  if (n < 0) return PA_ERR_SHAPE;
+  if (n == 0) return PA_OK;
+  if (!k_pool || !v_pool || !src || !dst) return PA_ERR_NULL;
+  if (((uintptr_t)k_pool | (uintptr_t)v_pool) & 15u) return PA_ERR_ALIGN;
+  const DeviceInfo info = device_info();
+  if (!info.ok) return PA_ERR_DEVICE;
+  CopyArgs a;
+  a.kp = static_cast<char*>(k_pool);
+  a.vp = static_cast<char*>(v_pool);
+  a.src = src;
+  a.dst = dst;
+  a.block_bytes = (int64_t)d->num_kv_heads * d->block_size * d->head_dim * pa_dtype_size(d->dtype);
+  a.chunks = (int32_t)(a.block_bytes / kChunkBytes);  // head_dim 128, B in {16, 32}: exact
+  const int64_t total = (int64_t)n * 2 * a.chunks;
+  if (total >= ((int64_t)1 << 31)) return PA_ERR_UNSUPPORTED;
+  a.total = (int32_t)total;
+  int64_t grid = (total + kCopyUnroll - 1) / kCopyUnroll;
+  const int64_t cap = (int64_t)info.cus * 8;
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 }  // extern "C"

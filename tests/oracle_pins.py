@@ -450,4 +450,145 @@ def pin_empty_partial_is_merge_identity(O):
     assert ee[0] == -math.inf and ee[1] == 0.0 and not np.any(ee[2])
 
 
+# ------------------------------------------------ writing the cache
+# "PagedAttention: The Cache Was Storing Nothing", §2.2 (the table maps
+# logical to physical blocks; only the last block is partly filled) and
+# §2.3 (a shared block is copied when a sequence diverges and writes).
+
+def _append_case(seed, B, esize, S=3, H=2, D=16, lens=(9, 16, 3)):
+    """Logical rows as raw element bits (uint16 patterns for esize 2,
+    float32 values for esize 4) plus tables over a shuffled pool."""
+    rng = np.random.default_rng(seed)
+    lmax = max(lens)
+    if esize == 2:
+        rows = rng.integers(1, 65536, size=(2, S, H, lmax, D)).astype(np.float64)
+    else:
+        rows = rng.standard_normal((2, S, H, lmax, D)).astype(np.float32).astype(np.float64)
+    nb = sum(-(-L // B) for L in lens)
+    NB = nb + 3
+    bt = random_tables(rng, lens, B, NB, max(-(-L // B) for L in lens) + 1)
+    return rows[0], rows[1], bt, np.asarray(lens, np.int32), NB
+
+
+def _storage(x, esize):
+    return x.astype(np.uint16) if esize == 2 else x.astype(np.float32)
+
+
+def _append_all(O, Klog, Vlog, bt, lens, NB, B, esize, fill):
+    """Append every token of every sequence, one decode step at a time,
+    into pools that start filled with `fill`."""
+    S, H, lmax, D = Klog.shape
+    Gv = vgroup(B)
+    kp = _storage(np.full((NB, H, B, D), fill), esize)
+    vp = _storage(np.full((NB, H, B // Gv, D, Gv), fill), esize)
+    for t in range(lmax):
+        pos = np.where(t < lens, t, -1).astype(np.int32)
+        kp, vp = O.append(_storage(Klog[:, :, t, :], esize), _storage(Vlog[:, :, t, :], esize),
+                          kp, vp, bt, pos)
+    return kp, vp
+
+
+def pin_append_places_tokens_like_an_independent_scatter(O):
+    """Appending tokens 0..L-1 one step at a time builds, bit for bit, the
+    pools that numpy fancy indexing builds from the same logical rows
+    (16- and 32-bit elements; block sizes 4, 16, 32; every slot no token
+    owns keeps its fill)."""
+    for B in (4, 16, 32):
+        for esize in (2, 4):
+            Klog, Vlog, bt, lens, NB = _append_case(11 + B, B, esize)
+            fill = 0 if esize == 2 else np.nan
+            kp, vp = _append_all(O, Klog, Vlog, bt, lens, NB, B, esize, fill)
+            kw, vw = scatter(Klog, Vlog, bt, lens, NB, B, fill=fill)
+            assert np.array_equal(kp.view(np.uint8), _storage(kw, esize).view(np.uint8)), (B, esize)
+            assert np.array_equal(vp.view(np.uint8), _storage(vw, esize).view(np.uint8)), (B, esize)
+
+
+def pin_append_then_decode_matches_library_sdpa(O):
+    """Tokens appended one by one and then read back by the decode oracle
+    give torch's attention on the contiguous logical rows."""
+    B = 16
+    Klog, Vlog, bt, lens, NB = _append_case(5, B, 4, lens=(40, 17, 1))
+    kp, vp = _append_all(O, Klog, Vlog, bt, lens, NB, B, 4, np.nan)
+    rng = np.random.default_rng(6)
+    S, H, _, D = Klog.shape
+    q = rng.standard_normal((S, H, D)).astype(np.float32)
+    got = O.paged_decode(q, kp, vp, bt, lens, 0.25, num_kv_heads=H, block_size=B, dtype="f32")
+    for b in range(S):
+        for h in range(H):
+            L = int(lens[b])
+            want = sdpa(q[b, h].astype(np.float64), Klog[b, h, :L], Vlog[b, h, :L], 0.25)
+            assert np.max(np.abs(got[b, h] - want)) < 1e-12
+
+
+def pin_append_with_negative_positions_writes_nothing(O):
+    Klog, Vlog, bt, lens, NB = _append_case(7, 16, 2)
+    rng = np.random.default_rng(8)
+    kp = rng.integers(0, 65536, size=(NB, 2, 16, 16)).astype(np.uint16)
+    vp = rng.integers(0, 65536, size=(NB, 2, 1, 16, 16)).astype(np.uint16)
+    k2, v2 = O.append(_storage(Klog[:, :, 0, :], 2), _storage(Vlog[:, :, 0, :], 2), kp, vp, bt,
+                      np.full(3, -1, np.int32))
+    assert np.array_equal(k2, kp) and np.array_equal(v2, vp)
+
+
+def pin_append_out_of_range_is_an_error(O):
+    Klog, Vlog, bt, lens, NB = _append_case(9, 16, 4)
+    kp = np.zeros((NB, 2, 16, 16), np.float32)
+    vp = np.zeros((NB, 2, 1, 16, 16), np.float32)
+    for pos in ([bt.shape[1] * 16, -1, -1], [-1, 40, -1]):  # past the table row / unused entry
+        try:
+            O.append(_storage(Klog[:, :, 0, :], 4), _storage(Vlog[:, :, 0, :], 4), kp, vp, bt,
+                     np.asarray(pos, np.int32))
+        except ValueError:
+            continue
+        raise AssertionError(f"append at {pos} should be rejected")
+
+
+def pin_copy_blocks_matches_numpy_assignment(O):
+    """Block dst[i] of both pools becomes block src[i]; every other block
+    is untouched (numpy fancy assignment as the reference)."""
+    rng = np.random.default_rng(12)
+    for (NB, H, B, esize) in ((20, 2, 16, 2), (9, 3, 32, 4), (12, 1, 4, 2)):
+        Gv = vgroup(B)
+        dt = np.uint16 if esize == 2 else np.uint32
+        kp = rng.integers(0, 1 << (8 * esize), size=(NB, H, B, 8), dtype=np.uint64).astype(dt)
+        vp = rng.integers(0, 1 << (8 * esize), size=(NB, H, B // Gv, 8, Gv), dtype=np.uint64).astype(dt)
+        ids = rng.permutation(NB)
+        n = NB // 3
+        src, dst = ids[:n].astype(np.int32), ids[n: 2 * n].astype(np.int32)
+        k2, v2 = O.copy_blocks(kp, vp, src, dst)
+        kw, vw = kp.copy(), vp.copy()
+        kw[dst] = kp[src]
+        vw[dst] = vp[src]
+        assert np.array_equal(k2, kw) and np.array_equal(v2, vw), (NB, H, B, esize)
+
+
+def pin_copy_on_write_fork_keeps_the_original(O):
+    """Two sequences share every block; before the fork appends into the
+    shared last block, that block is copied and the fork's table entry
+    repointed.  Afterwards each sequence attends to its own new token and
+    the original is exactly what it would be without the fork."""
+    B, H, D, L = 16, 2, 16, 21
+    rng = np.random.default_rng(13)
+    Klog = rng.standard_normal((1, H, L + 1, D)).astype(np.float32).astype(np.float64)
+    Vlog = rng.standard_normal((1, H, L + 1, D)).astype(np.float32).astype(np.float64)
+    NB = 6
+    bt = np.asarray([[4, 1, -1]], np.int32)
+    kp, vp = scatter(Klog, Vlog, bt, [L], NB, B)
+    kp, vp = kp.astype(np.float32), vp.astype(np.float32)
+    # fork: sequence 1 shares blocks 4, 1; its last block (1) is copied to 3
+    kp, vp = O.copy_blocks(kp, vp, np.asarray([1], np.int32), np.asarray([3], np.int32))
+    tables = np.asarray([[4, 1, -1], [4, 3, -1]], np.int32)
+    new = rng.standard_normal((2, 2, H, D)).astype(np.float32)  # [k/v][seq][head][dim]
+    kp, vp = O.append(new[0], new[1], kp, vp, tables, np.asarray([L, L], np.int32))
+    q = rng.standard_normal((2, H, D)).astype(np.float32)
+    got = O.paged_decode(q, kp, vp, tables, np.asarray([L + 1, L + 1], np.int32), 0.3,
+                         num_kv_heads=H, block_size=B, dtype="f32")
+    for b in range(2):
+        for h in range(H):
+            K = np.concatenate([Klog[0, h, :L], new[0, b, h][None].astype(np.float64)])
+            V = np.concatenate([Vlog[0, h, :L], new[1, b, h][None].astype(np.float64)])
+            want = sdpa(q[b, h].astype(np.float64), K, V, 0.3)
+            assert np.max(np.abs(got[b, h] - want)) < 1e-12
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

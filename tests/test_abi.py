@@ -26,7 +26,7 @@ def _declared_functions():
     with open(os.path.join(ROOT, "include", "pagedattn.h")) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*[a-z_][\w\s\*]*?\b(pa_\w+|paged_attn_decode)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*[a-z_][\w\s\*]*?\b(pa_\w+|paged_\w+)\s*\(", text, re.M)))
 
 
 def test_every_declared_function_is_exported(lib):
@@ -184,6 +184,64 @@ def test_no_device_is_reported(lib):
                                pa.pa_workspace_bytes(d), None)
     assert rc == 9
     assert pa.pa_decode_grid(d) == -1
+
+
+def test_validate_append_host(lib):
+    w = workload.make(3, 3, batch=8, max_len=700)
+    d = pa.PaDesc(w.num_seqs, 32, 8, 128, 16, w.num_blocks, w.max_blocks_per_seq, pa.PA_BF16, pa.PA_F32, 0)
+    bt = np.ascontiguousarray(w.block_tables)
+    pos = np.ascontiguousarray(w.seq_lens - 1)  # overwrite each sequence's last token: in its table
+    assert pa.pa_validate_append_host(d, bt, pos) == 0
+    skip = pos.copy()
+    skip[::2] = -1
+    assert pa.pa_validate_append_host(d, bt, skip) == 0
+    nxt = np.ascontiguousarray(w.seq_lens)  # next slot: fails where it needs a new, unassigned block
+    needs_block = (w.seq_lens % 16) == 0
+    assert pa.pa_validate_append_host(d, bt, nxt) == (8 if needs_block.any() else 0)
+    past = pos.copy()
+    past[1] = w.max_blocks_per_seq * 16
+    assert pa.pa_validate_append_host(d, bt, past) == 8
+    bad = bt.copy()
+    bad[2, int(pos[2]) // 16] = w.num_blocks
+    assert pa.pa_validate_append_host(d, bad, pos) == 8
+    same = bt.copy()
+    same[1] = same[0]
+    dup = pos.copy()
+    dup[1] = dup[0]
+    assert pa.pa_validate_append_host(d, same, dup) == 8  # two sequences, one (block, slot)
+
+
+def test_validate_copy_host(lib):
+    d = _desc(num_blocks=10)
+    arr = lambda *v: np.asarray(v, np.int32)  # noqa: E731
+    assert pa.pa_validate_copy_host(d, arr(1, 2, 3), arr(4, 5, 6), 3) == 0
+    assert pa.pa_validate_copy_host(d, arr(1, 1), arr(4, 5), 2) == 0  # one source, two copies
+    assert pa.pa_validate_copy_host(d, arr(1, 2), arr(4, 4), 2) == 8  # destination twice
+    assert pa.pa_validate_copy_host(d, arr(1, 4), arr(4, 5), 2) == 8  # a destination is a source
+    assert pa.pa_validate_copy_host(d, arr(1), arr(10), 1) == 8
+    assert pa.pa_validate_copy_host(d, arr(-1), arr(3), 1) == 8
+    assert pa.pa_validate_copy_host(d, None, None, 0) == 0
+    assert pa.pa_validate_copy_host(d, None, None, 2) == 1
+    assert pa.pa_validate_copy_host(d, arr(1), arr(2), -1) == 2
+
+
+def test_cache_write_argument_errors_before_any_launch(lib):
+    d = _desc()
+    byref = pa._lib.ctypes.byref
+    P = 1 << 20  # fake aligned address; not dereferenced on these paths
+    assert lib.paged_kv_append(None, P, P, P, P, P, byref(d), None) == 1
+    assert lib.paged_kv_append(P, P, P + 2, P, P, P, byref(d), None) == 6
+    assert lib.paged_kv_append(P, P, P, P, P, P, byref(_desc(block_size=8)), None) == 4
+    assert lib.paged_kv_append(P, P, P, P, P, P, byref(_desc(num_seqs=0)), None) == 0
+    assert lib.paged_kv_copy_blocks(P, P, P, P, -1, byref(d), None) == 2
+    assert lib.paged_kv_copy_blocks(P, P, P, P, 0, byref(d), None) == 0
+    assert lib.paged_kv_copy_blocks(P, None, P, P, 3, byref(d), None) == 1
+    assert lib.paged_kv_copy_blocks(P, P + 8, P, P, 3, byref(d), None) == 6
+    assert lib.paged_kv_copy_blocks(P, P, P, P, 3, byref(_desc(dtype=7)), None) == 3
+    import torch
+    if not torch.cuda.is_available():
+        assert lib.paged_kv_append(P, P, P, P, P, P, byref(d), None) == 9
+        assert lib.paged_kv_copy_blocks(P, P, P, P, 3, byref(d), None) == 9
 
 
 def test_binding_refuses_to_run_without_the_library(tmp_path, monkeypatch):

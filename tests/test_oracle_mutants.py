@@ -23,8 +23,8 @@ MUTANTS = [
     ("slot_off_by_one", "const int64_t slot = t % B;", "const int64_t slot = (t + 1) % B;"),
     ("block_index_rounding", "const int64_t j = t / B;", "const int64_t j = (t + 1) / B;"),
     ("table_row_offset_missing", "block_tables[(int64_t)b * max_blocks_per_seq + j]", "block_tables[j]"),
-    ("kv_head_stride_missing", "const int64_t tile = (phys * H + g) * B * D;",
-     "const int64_t tile = (phys + g) * B * D;"),
+    ("kv_head_stride_missing", "const int64_t tile = (phys * H + g) * B * D; /* same tile base",
+     "const int64_t tile = (phys + g) * B * D; /* same tile base"),
     ("slack_slots_attended", "const int64_t L = seq_lens[b] > 0 ? seq_lens[b] : 0;",
      "const int64_t L = seq_lens[b] > 0 ? ((seq_lens[b] + block_size - 1) / block_size) * block_size : 0;"),
     ("q_element_size_swapped", "(dtype == ORC_F32 ? 4 : 2)", "(dtype == ORC_F32 ? 2 : 4)"),
@@ -38,6 +38,26 @@ MUTANTS = [
     ("f16_subnormal_scale", "v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
     ("f16_hidden_bit_missing", "v = ldexp((double)(0x400 | f), e - 25);", "v = ldexp((double)f, e - 25);"),
     ("bf16_wrong_half", "const uint32_t u = (uint32_t)b << 16;", "const uint32_t u = (uint32_t)b;"),
+    # writing the cache
+    ("append_slot_off_by_one", "const int64_t j = t / B, slot = t % B;",
+     "const int64_t j = t / B, slot = (t + 1) % B;"),
+    ("append_v_not_transposed", "const int64_t vdst = tile + (slot / G) * D * G + d * G + slot % G;",
+     "const int64_t vdst = tile + slot * D + d;"),
+    ("append_kv_head_stride_missing",
+     "const int64_t tile = (phys * H + g) * B * D;\n      const int64_t src",
+     "const int64_t tile = (phys + g) * B * D;\n      const int64_t src"),
+    ("append_source_rows_head_major", "const int64_t src = (b * H + g) * D;",
+     "const int64_t src = (g * num_seqs + b) * D;"),
+    ("append_table_row_offset_missing", "const int64_t phys = block_tables[b * max_blocks_per_seq + j];",
+     "const int64_t phys = block_tables[j];"),
+    ("copy_block_bytes_one_head", "const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * esize;",
+     "const int64_t block_bytes = (int64_t)block_size * head_dim * esize;"),
+    ("copy_direction_swapped",
+     "memmove((char*)k_pool + dst[i] * block_bytes, (const char*)k_pool + src[i] * block_bytes,",
+     "memmove((char*)k_pool + src[i] * block_bytes, (const char*)k_pool + dst[i] * block_bytes,"),
+    ("copy_v_pool_skipped",
+     "memmove((char*)v_pool + dst[i] * block_bytes, (const char*)v_pool + src[i] * block_bytes,\n            block_bytes);",
+     "(void)v_pool;"),
 ]
 
 
