@@ -253,6 +253,125 @@ def cpu_baseline(w, kv_bytes: int, budget_s: float) -> dict:
     }
 
 
+def _time_events(fn, flush, stream, reps: int, warmup: int = 3):
+    """Mean / median ms of `fn` between HIP events on `stream`, the cache
+    flush before every call outside the events."""
+    import torch
+    ms = []
+    for i in range(warmup + reps):
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        if i >= warmup:
+            ms.append(e0.elapsed_time(e1))
+    return statistics.mean(ms), statistics.median(ms)
+
+
+def _cpu_time(fn, budget_s: float = 2.0) -> float:
+    times = []
+    t_all = time.perf_counter()
+    while len(times) < 3 or (time.perf_counter() - t_all < budget_s and len(times) < 200):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return statistics.median(times)
+
+
+def cache_writes(w, kp, vp, dev, flush, stream, with_cpu: bool) -> dict:
+    """The two cache writes on the same pools: appending the next token of
+    every sequence (the step before the next decode call) and copying
+    random live blocks into every free block of the pool (copy-on-write at
+    scale).  Neither touches a slot the decode call reads (the appended
+    slot is at position L, the copies land in unreferenced blocks).  Each
+    is timed with HIP events like the decode call; the oracle's byte-level
+    routine is timed on the host copies, one thread."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_196_amd as pa
+    import workload as wl
+
+    rng = np.random.default_rng(w.seed + 1000)
+    B, S, H, D, es = w.block_size, w.num_seqs, w.num_kv_heads, w.head_dim, w.esize
+    tables = w.block_tables.copy()
+    used = np.zeros(w.num_blocks, bool)
+    used[tables[tables >= 0]] = True
+    free = list(rng.permutation(np.nonzero(~used)[0]))
+    pos = w.seq_lens.astype(np.int32).copy()
+    for b in range(S):
+        if pos[b] // B >= tables.shape[1]:
+            pos[b] = -1  # the table row is full: no next slot
+        elif pos[b] % B == 0:
+            tables[b, pos[b] // B] = free.pop()
+    dtype_code = {"f32": pa.PA_F32, "f16": pa.PA_F16, "bf16": pa.PA_BF16}[w.dtype]
+    desc = pa.PaDesc(S, H, H, D, B, w.num_blocks, tables.shape[1], dtype_code, pa.PA_F32, 0, 0)
+    if pa.pa_validate_append_host(desc, np.ascontiguousarray(tables), pos) != 0:
+        raise RuntimeError("append preconditions do not hold")
+    shape = (S, H, D)
+    kn = wl.round_to(rng.standard_normal(shape, dtype=np.float32), w.dtype).reshape(shape)
+    vn = wl.round_to(rng.standard_normal(shape, dtype=np.float32), w.dtype).reshape(shape)
+
+    def up(x):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    kn_d, vn_d = up(kn), up(vn)
+    tb_d = torch.from_numpy(tables).to(dev)
+    pos_d = torch.from_numpy(pos).to(dev)
+    sh = stream.cuda_stream
+    live = int((pos >= 0).sum())
+    app_bytes = 2 * 2 * live * H * D * es + 4 * S + 4 * live
+    a_mean, a_med = _time_events(
+        lambda: pa.paged_kv_append(kn_d, vn_d, kp, vp, tb_d, pos_d, desc, sh), flush, stream, 50)
+
+    n = len(free)
+    src = rng.choice(np.nonzero(used)[0], size=n).astype(np.int32)
+    dst = np.asarray(free, np.int32)
+    if pa.pa_validate_copy_host(desc, src, dst, n) != 0:
+        raise RuntimeError("copy preconditions do not hold")
+    src_d, dst_d = torch.from_numpy(src).to(dev), torch.from_numpy(dst).to(dev)
+    block_bytes = H * B * D * es
+    copy_bytes = 2 * 2 * n * block_bytes + 8 * n
+    c_mean, c_med = _time_events(
+        lambda: pa.paged_kv_copy_blocks(kp, vp, src_d, dst_d, n, desc, sh), flush, stream, 20)
+
+    res = {
+        "workload": w.name,
+        "append": {
+            "kernel": f"append_kernel<{es}>", "tokens": live,
+            "us_per_call": round(a_mean * 1e3, 2), "us_median": round(a_med * 1e3, 2),
+            "algorithmic_bytes": app_bytes,
+            "gbps": round(app_bytes / (a_mean * 1e-3) / 1e9, 2),
+            "frac_of_hbm_peak": round(app_bytes / (a_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS, 5),
+            "bound": "launch latency: one call moves well under 1 MB",
+        },
+        "copy_blocks": {
+            "kernel": "copy_blocks_kernel", "pairs": n, "block_bytes_per_pool": block_bytes,
+            "us_per_call": round(c_mean * 1e3, 2), "us_median": round(c_med * 1e3, 2),
+            "algorithmic_bytes": copy_bytes,
+            "gbps": round(copy_bytes / (c_mean * 1e-3) / 1e9, 2),
+            "roofline": {"bound": "hbm", "achieved": round(copy_bytes / (c_mean * 1e-3) / 1e9, 2),
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(copy_bytes / (c_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        },
+    }
+    if with_cpu:
+        import oracle
+        O = oracle.load()
+        hk, hv = np.ascontiguousarray(w.k_pool).copy(), np.ascontiguousarray(w.v_pool).copy()
+        t_app = _cpu_time(lambda: O.append(kn, vn, hk, hv, tables, pos, inplace=True))
+        t_cp = _cpu_time(lambda: O.copy_blocks(hk, hv, src, dst, inplace=True))
+        res["append"]["cpu_oracle"] = {"us_per_call": round(t_app * 1e6, 1), "cores": 1,
+                                       "kind": "oracle", "sample": "same call, host pools"}
+        res["copy_blocks"]["cpu_oracle"] = {"us_per_call": round(t_cp * 1e6, 1), "cores": 1,
+                                            "gbps": round(copy_bytes / t_cp / 1e9, 2),
+                                            "kind": "oracle", "sample": "same call, host pools"}
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -268,6 +387,8 @@ def main() -> int:
     ap.add_argument("--no-check", action="store_true", help="skip the oracle spot check")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-read-probe", action="store_true")
+    ap.add_argument("--no-cache-writes", action="store_true",
+                    help="skip timing the append / block-copy calls")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the calibration copy (for rocprofv3 counter scaling)")
     ap.add_argument("--summarize-counters", nargs=4, metavar="DIR",
@@ -439,6 +560,10 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, kv_unique, args.cpu_seconds)
+    if not args.no_cache_writes:
+        # after the decode timing and its check: these write (unread) pool slots
+        result["cache_writes"] = cache_writes(w, kp, vp, dev, flush, stream,
+                                              with_cpu=not args.no_cpu_baseline)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -178,12 +178,14 @@ class Oracle:
             raise ValueError(f"oracle_paged_decode failed with code {rc}")
         return out
 
-    def append(self, k_new, v_new, k_pool, v_pool, block_tables, positions):
-        """New pools (copies) after appending k_new / v_new [S][Hkv][D] at
-        logical slot positions[b] of every sequence (skipped where < 0).
-        Pools as in paged_decode (raw storage); the inputs are not modified."""
-        kp = np.array(k_pool, copy=True, order="C")
-        vp = np.array(v_pool, copy=True, order="C")
+    def append(self, k_new, v_new, k_pool, v_pool, block_tables, positions, inplace=False):
+        """Pools after appending k_new / v_new [S][Hkv][D] at logical slot
+        positions[b] of every sequence (skipped where < 0).  Pools as in
+        paged_decode (raw storage).  Copies unless inplace (then the given
+        C-contiguous pools are written and returned)."""
+        kp = k_pool if inplace else np.array(k_pool, copy=True, order="C")
+        vp = v_pool if inplace else np.array(v_pool, copy=True, order="C")
+        assert kp.flags.c_contiguous and vp.flags.c_contiguous
         kn = _c(k_new)
         vn = _c(v_new)
         bt = _c(block_tables, np.int32)
@@ -195,10 +197,12 @@ class Oracle:
             raise ValueError("oracle_append: position or table entry out of range")
         return kp, vp
 
-    def copy_blocks(self, k_pool, v_pool, src, dst):
-        """New pools (copies) after block dst[i] <- block src[i] in both."""
-        kp = np.array(k_pool, copy=True, order="C")
-        vp = np.array(v_pool, copy=True, order="C")
+    def copy_blocks(self, k_pool, v_pool, src, dst, inplace=False):
+        """Pools after block dst[i] <- block src[i] in both (copies unless
+        inplace)."""
+        kp = k_pool if inplace else np.array(k_pool, copy=True, order="C")
+        vp = v_pool if inplace else np.array(v_pool, copy=True, order="C")
+        assert kp.flags.c_contiguous and vp.flags.c_contiguous
         s = _c(src, np.int32)
         d = _c(dst, np.int32)
         NB, Hkv, B, D = kp.shape
