@@ -653,6 +653,20 @@ __device__ __forceinline__ int split_seen(const Args& a, const Piece& pc) {
   return counted(a.counters + pc.kfirst);
 }
 
+// Stage the batch's query groups in LDS (all threads; the caller
+// synchronises before they are read).
+template <class T, int G, class Smem>
+__device__ inline void stage_queries(const Args& a, Smem& sm, int npl) {
+  constexpr int kQChunks = G * kD * T::kEsize / 16;  // 16-byte chunks per query group
+  for (int x = threadIdx.x; x < npl * kQChunks; x += kThreads) {
+    const int p = x / kQChunks, k = x % kQChunks;
+    const Piece& pc = sm.plist[p];
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
+        ((int64_t)pc.b * a.Hq + (int64_t)pc.kvh * G) * kD * T::kEsize);
+    sm.q[p][k] = src[k];
+  }
+}
+
 template <class T, int B, int G, class Engine>
 __device__ inline void stream_batch(const Args& a, typename Engine::Smem& sm) {
   using Tile = typename Engine::Tile;
@@ -730,17 +744,26 @@ __device__ inline void stream_batch(const Args& a, typename Engine::Smem& sm) {
         Engine::template load_tile<kStreamPolicy>(a, kvh, tok % B, phys, bytes, t);
     };
     // Each tile register carries (piece, valid tokens) of its sub-tile.
+    // The first two positions and their table entries are resolved before
+    // any tile load, so both loads leave back to back, and the query
+    // groups are staged after them: the batch starts with two memory round
+    // trips instead of three.
+    const Cur c0 = c;
     int p0 = c.p, v0 = c.te - (c.tb + kSub * c.j);
-    Tile t0, t1;
-    load(c, row_phys(c), true, t0);
     advance(c);
     if (c.p < npl) last = c;
+    const Cur c1 = last;
+    const bool live1 = c.p < npl;
     int p1 = c.p, v1 = c.te - (c.tb + kSub * c.j);
-    load(last, row_phys(last), c.p < npl, t1);
     advance(c);
     if (c.p < npl) last = c;
+    const int ph0 = row_phys(c0), ph1 = row_phys(c1);
     int ph = row_phys(last);
-    __syncthreads();  // query groups staged (see run_decode)
+    Tile t0, t1;
+    load(c0, ph0, true, t0);
+    load(c1, ph1, live1, t1);
+    stage_queries<T, G>(a, sm, npl);
+    __syncthreads();  // query groups staged
     Engine::load_query(sm, 0, q);
     // Load the stream's next sub-tile into t and return its (piece, valid
     // tokens).
@@ -776,6 +799,7 @@ __device__ inline void stream_batch(const Args& a, typename Engine::Smem& sm) {
       enter(p0, false);
     }
   } else {
+    stage_queries<T, G>(a, sm, npl);
     __syncthreads();  // query groups staged
   }
   enter(npl, true);
@@ -862,20 +886,11 @@ __device__ inline void run_decode(const Args& a) {
     sm.early_seen = -1;
   }
   __syncthreads();
-  constexpr int kQChunks = G * kD * T::kEsize / 16;  // 16-byte chunks per query group
   while (true) {
     if (threadIdx.x < 64) list_batch<B>(a, sm, cum, lens_s, s, e, chunk, c);
     __syncthreads();
     const int npl = sm.npl;
     if (npl == 0) break;
-    // Stage the batch's query groups in LDS (issued before any tile load).
-    for (int x = threadIdx.x; x < npl * kQChunks; x += kThreads) {
-      const int p = x / kQChunks, k = x % kQChunks;
-      const Piece& pc = sm.plist[p];
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
-          ((int64_t)pc.b * a.Hq + (int64_t)pc.kvh * G) * kD * T::kEsize);
-      sm.q[p][k] = src[k];
-    }
     stream_batch<T, B, G, Engine>(a, sm);
     __syncthreads();
   }
