@@ -372,6 +372,56 @@ def cache_writes(w, kp, vp, dev, flush, stream, with_cpu: bool) -> dict:
     return res
 
 
+def eviction_scores(w, kp, vp, dev, flush, stream, with_cpu: bool) -> dict:
+    """Block-wise eviction scoring (paged_kv_block_scores) over the same
+    pools, every length cut to a whole number of blocks so that every
+    sequence chooses a block: the scan reads every full block's K and V of
+    every KV head once.  Timed with HIP events (two launches per call); the
+    oracle is timed on a bounded sample of the sequences."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_196_amd as pa
+
+    B, S, H, D, es = w.block_size, w.num_seqs, w.num_kv_heads, w.head_dim, w.esize
+    lens = (w.seq_lens // B * B).astype(np.int32)
+    full = lens // B
+    dtype_code = {"f32": pa.PA_F32, "f16": pa.PA_F16, "bf16": pa.PA_BF16}[w.dtype]
+    M = w.max_blocks_per_seq
+    desc = pa.PaDesc(S, H, H, D, B, w.num_blocks, M, dtype_code, pa.PA_F32, 0, 0)
+    if pa.pa_validate_host(desc, np.ascontiguousarray(w.block_tables), lens) != 0:
+        raise RuntimeError("score preconditions do not hold")
+    bt_d = torch.from_numpy(w.block_tables).to(dev)
+    lens_d = torch.from_numpy(lens).to(dev)
+    scores = torch.empty((S, M), dtype=torch.float32, device=dev)
+    evict = torch.empty(S, dtype=torch.int32, device=dev)
+    sh = stream.cuda_stream
+    kv = int(full.sum()) * H * B * D * es * 2
+    alg = kv + S * M * 4 + 4 * S + 4 * S + 4 * int(full.sum())
+    mean, med = _time_events(
+        lambda: pa.paged_kv_block_scores(kp, vp, bt_d, lens_d, scores, evict, desc, sh), flush,
+        stream, 20)
+    gbps = alg / (mean * 1e-3) / 1e9
+    res = {
+        "workload": w.name + " (lengths cut to whole blocks)",
+        "kernels": ["block_score_kernel", "evict_choice_kernel"],
+        "us_per_call": round(mean * 1e3, 2), "us_median": round(med * 1e3, 2),
+        "kv_bytes": kv, "algorithmic_bytes": alg, "gbps": round(gbps, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4)},
+    }
+    if with_cpu:
+        import oracle
+        O = oracle.load()
+        n = min(S, 4)
+        t = _cpu_time(lambda: O.block_scores(w.k_pool, w.v_pool, w.block_tables[:n], lens[:n],
+                                             dtype=w.dtype), budget_s=5.0)
+        kv_n = int(full[:n].sum()) * H * B * D * es * 2
+        res["cpu_oracle"] = {"gbps": round(kv_n / t / 1e9, 3), "seconds": round(t, 3), "cores": 1,
+                             "kind": "oracle", "sample": f"first {n} of {S} sequences, fp64 C"}
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -389,6 +439,8 @@ def main() -> int:
     ap.add_argument("--no-read-probe", action="store_true")
     ap.add_argument("--no-cache-writes", action="store_true",
                     help="skip timing the append / block-copy calls")
+    ap.add_argument("--no-eviction-scores", action="store_true",
+                    help="skip timing the block-wise eviction scoring")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the calibration copy (for rocprofv3 counter scaling)")
     ap.add_argument("--summarize-counters", nargs=4, metavar="DIR",
@@ -560,6 +612,9 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, kv_unique, args.cpu_seconds)
+    if not args.no_eviction_scores:
+        result["eviction_scores"] = eviction_scores(w, kp, vp, dev, flush, stream,
+                                                    with_cpu=not args.no_cpu_baseline)
     if not args.no_cache_writes:
         # after the decode timing and its check: these write (unread) pool slots
         result["cache_writes"] = cache_writes(w, kp, vp, dev, flush, stream,

@@ -251,6 +251,43 @@ int32_t paged_kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src_bloc
 int32_t pa_validate_copy_host(const pa_desc* desc, const int32_t* src_blocks_host,
                               const int32_t* dst_blocks_host, int32_t num_pairs);
 
+/* ------------------------------------------------------------------
+ * Block-wise eviction scoring ("PagedEviction: Structured Block-wise KV
+ * Cache Pruning for Efficient Large Language Model Inference", the review's
+ * "Core claim" and "What carries the argument"): a token's importance is
+ * the ratio of its value norm to its key norm, read from the cached rows,
+ * and a block's score is the mean over its tokens; during decode, when a
+ * sequence's most recent block has just filled, the block with the lowest
+ * score is the one to evict.
+ * ------------------------------------------------------------------ */
+
+/* For every sequence b (L = seq_lens[b]) and every full logical block
+ * j < L / block_size:
+ *
+ *   block_scores[b][j] = (1/B) * sum over the B tokens t of block j of
+ *                        ||V_b[t]||_2 / ||K_b[t]||_2
+ *
+ * where K_b[t] / V_b[t] is token t's whole key / value row of the layer:
+ * all num_kv_heads * head_dim elements (pages through the table as for the
+ * decode call).  Entries j >= L / block_size are set to NaN.
+ * evict[b] = the full block with the lowest score (the lowest j among
+ * equal scores) when L > 0 and L % block_size == 0, else -1.  Scores are
+ * accumulated in fp32.  The library only scores and chooses: dropping the
+ * block from the sequence's table is the caller's.  A token whose key and
+ * value rows are both all-zero scores NaN and the choice is then undefined.
+ *
+ *   block_scores  float [num_seqs][max_blocks_per_seq], device
+ *   evict         int32 [num_seqs], device
+ *
+ * Two kernel launches on `stream` (scores, then the choice).  Data-dependent
+ * preconditions as for paged_attn_decode (pa_validate_host).  Returns PA_OK,
+ * a descriptor error, PA_ERR_NULL, PA_ERR_ALIGN, PA_ERR_DEVICE or
+ * PA_ERR_LAUNCH. */
+int32_t paged_kv_block_scores(const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* seq_lens,
+                              float* block_scores, int32_t* evict, const pa_desc* desc,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,7 +1,8 @@
 /*
  * oracle.c — plain fp64 CPU oracle for single-token paged decode attention,
- * and the plain byte-level definition of the two cache writes around it
- * (appending a decode token, copy-on-write block copy; end of this file).
+ * the plain byte-level definition of the two cache writes around it
+ * (appending a decode token, copy-on-write block copy) and the block-wise
+ * eviction scores (end of this file).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or
  * calls this file: only the test suite, the smoke check and the CPU-baseline
@@ -312,6 +313,68 @@ int oracle_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, const int
             block_bytes);
     memmove((char*)v_pool + dst[i] * block_bytes, (const char*)v_pool + src[i] * block_bytes,
             block_bytes);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------
+ * Block-wise eviction scoring ("PagedEviction: Structured Block-wise KV
+ * Cache Pruning for Efficient Large Language Model Inference", the review's
+ * "Core claim" and "What carries the argument"): token importance
+ * S_t = ||V_t||_2 / ||K_t||_2 from the cached rows; a block's score is the
+ * mean of S_t over its tokens; in decode, when the most recent block of a
+ * sequence has just filled, the block with the lowest mean is evicted.
+ * Readings (the page is silent on them): a token's key / value row is its
+ * whole row of the layer, every KV head; every full block of the sequence
+ * is a candidate; the lowest logical index wins a tie.
+ * ------------------------------------------------------------------ */
+
+/* scores[b][j] (fp64, [num_seqs][max_blocks_per_seq]) for every full block
+ * j < L / B of every sequence, NaN elsewhere; evict[b] = the lowest-scoring
+ * full block when L > 0 and L % B == 0, else -1.  Returns 0, or -1 when a
+ * table entry that is read is out of range. */
+int oracle_block_scores(const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                        const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                        int32_t max_blocks_per_seq, int32_t dtype, double* scores,
+                        int32_t* evict) {
+  const int64_t D = head_dim, B = block_size, H = num_kv_heads, M = max_blocks_per_seq;
+  const int64_t G = (B % 16 == 0) ? 16 : B; /* tokens per transposed V group */
+  for (int64_t b = 0; b < num_seqs; ++b) {
+    const int64_t L = seq_lens[b] < 0 ? 0 : seq_lens[b];
+    const int64_t full = L / B;
+    for (int64_t j = 0; j < M; ++j) scores[b * M + j] = NAN;
+    for (int64_t j = 0; j < full; ++j) {
+      const int64_t phys = block_tables[b * M + j];
+      if (phys < 0 || phys >= num_blocks) return -1;
+      double ratio_sum = 0.0;
+      for (int64_t slot = 0; slot < B; ++slot) {
+        double kk = 0.0, vv = 0.0; /* squared norms of the token's rows, all heads */
+        for (int64_t g = 0; g < H; ++g) {
+          const int64_t base = (phys * H + g) * B * D;
+          for (int64_t d = 0; d < D; ++d) {
+            const double k = elem(k_pool, dtype, base + slot * D + d);
+            const double v = elem(v_pool, dtype, base + (slot / G) * D * G + d * G + slot % G);
+            kk += k * k;
+            vv += v * v;
+          }
+        }
+        ratio_sum += sqrt(vv) / sqrt(kk);
+      }
+      scores[b * M + j] = ratio_sum / (double)B;
+    }
+    evict[b] = -1;
+    if (L > 0 && L % B == 0) {
+      double best = INFINITY;
+      int64_t arg = 0;
+      for (int64_t j = 0; j < full; ++j) {
+        if (scores[b * M + j] < best) {
+          best = scores[b * M + j];
+          arg = j;
+        }
+      }
+      evict[b] = (int32_t)arg;
+    }
   }
   return 0;
 }

@@ -82,6 +82,9 @@ class Oracle:
         lib.oracle_append.restype = ctypes.c_int
         lib.oracle_copy_blocks.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32]
         lib.oracle_copy_blocks.restype = ctypes.c_int
+        lib.oracle_block_scores.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                            _I32, _P, _P]
+        lib.oracle_block_scores.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -211,6 +214,25 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_copy_blocks: block id out of range")
         return kp, vp
+
+    def block_scores(self, k_pool, v_pool, block_tables, seq_lens, *, dtype: str):
+        """(scores fp64 [S][max_blocks_per_seq] with NaN past the full
+        blocks, evict int32 [S]) of block-wise eviction scoring."""
+        kp = _c(k_pool)
+        vp = _c(v_pool)
+        bt = _c(block_tables, np.int32)
+        lens = _c(seq_lens, np.int32)
+        NB, Hkv, B, D = kp.shape
+        S, M = bt.shape
+        scores = np.empty((S, M), np.float64)
+        evict = np.empty(S, np.int32)
+        if dtype != "f32":
+            kp, vp = kp.view(np.uint16), vp.view(np.uint16)
+        rc = self.lib.oracle_block_scores(_ptr(kp), _ptr(vp), _ptr(bt), _ptr(lens), S, Hkv, D, B, NB,
+                                          M, DTYPE_CODES[dtype], _ptr(scores), _ptr(evict))
+        if rc != 0:
+            raise ValueError("oracle_block_scores: table entry out of range")
+        return scores, evict
 
     def run_workload(self, w, num_threads: int = 0) -> np.ndarray:
         """paged_decode on a workload.Workload-like object."""

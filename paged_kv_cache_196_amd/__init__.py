@@ -1,7 +1,7 @@
 """gfx950 paged decode attention: a C-ABI library (libpagedattn.so) and its
 thin Python binding.  Besides the decode call the library writes the cache
-in its own layout: one appended token per sequence, and whole-block copies
-for copy-on-write sharing.
+in its own layout (one appended token per sequence, whole-block copies for
+copy-on-write sharing) and scores blocks for block-wise eviction.
 
 ``_lib`` mirrors the C ABI (include/pagedattn.h) name for name; ``api``
 adds torch-tensor conveniences (descriptor from shapes, workspace and
@@ -31,7 +31,9 @@ from ._lib import (  # noqa: F401
     pa_workspace_bytes,
     paged_attn_decode,
     paged_kv_append,
+    paged_kv_block_scores,
     paged_kv_copy_blocks,
     status_str,
 )
-from .api import append, copy_blocks, decode, ensure_built, make_desc, new_workspace  # noqa: F401
+from .api import (  # noqa: F401
+    append, block_scores, copy_blocks, decode, ensure_built, make_desc, new_workspace)

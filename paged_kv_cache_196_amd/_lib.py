@@ -24,7 +24,7 @@ EXPORTS = (
     "pa_status_str", "pa_dtype_size", "pa_blocks_for_len", "pa_pool_bytes", "pa_k_elem_offset",
     "pa_v_elem_offset", "pa_workspace_bytes", "pa_validate_host", "pa_check_desc",
     "paged_attn_decode", "pa_decode_grid", "paged_kv_append", "pa_validate_append_host",
-    "paged_kv_copy_blocks", "pa_validate_copy_host",
+    "paged_kv_copy_blocks", "pa_validate_copy_host", "paged_kv_block_scores",
 )
 
 
@@ -88,6 +88,8 @@ def load() -> ctypes.CDLL:
             lib.paged_kv_copy_blocks.restype = ctypes.c_int32
             lib.pa_validate_copy_host.argtypes = [_DP, _P, _P, ctypes.c_int32]
             lib.pa_validate_copy_host.restype = ctypes.c_int32
+            lib.paged_kv_block_scores.argtypes = [_P, _P, _P, _P, _P, _P, _DP, _P]
+            lib.paged_kv_block_scores.restype = ctypes.c_int32
             _lib = lib
     return _lib
 
@@ -187,3 +189,11 @@ def pa_validate_copy_host(desc: PaDesc, src_host, dst_host, num_pairs: int) -> i
     return int(load().pa_validate_copy_host(
         ctypes.byref(desc), None if src_host is None else src_host.ctypes.data,
         None if dst_host is None else dst_host.ctypes.data, int(num_pairs)))
+
+
+def paged_kv_block_scores(k_pool, v_pool, block_tables, seq_lens, block_scores, evict,
+                          desc: PaDesc, stream=None) -> int:
+    rc = load().paged_kv_block_scores(_ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                                      _ptr(seq_lens), _ptr(block_scores), _ptr(evict),
+                                      ctypes.byref(desc), _ptr(stream))
+    return _check(rc, "paged_kv_block_scores")

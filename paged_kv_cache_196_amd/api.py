@@ -155,3 +155,22 @@ def copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, src_blocks: torch.Te
     desc = _pool_desc(k_pool, v_pool, table, 1)
     st = stream if stream is not None else torch.cuda.current_stream(k_pool.device)
     _lib.paged_kv_copy_blocks(k_pool, v_pool, src_blocks, dst_blocks, n, desc, st.cuda_stream)
+
+
+def block_scores(k_pool: torch.Tensor, v_pool: torch.Tensor, block_tables: torch.Tensor,
+                 seq_lens: torch.Tensor, *, stream: torch.cuda.Stream | None = None):
+    """Block-wise eviction scores: (scores float32 [S][max_blocks_per_seq],
+    NaN past each sequence's full blocks; evict int32 [S], the block to drop
+    for sequences whose last block just filled, else -1)."""
+    if not seq_lens.is_cuda or not seq_lens.is_contiguous() or seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be a contiguous int32 device tensor")
+    S = seq_lens.shape[0]
+    desc = _pool_desc(k_pool, v_pool, block_tables, S)
+    if block_tables.shape[0] != S:
+        raise ValueError("block_tables needs one row per sequence")
+    scores = torch.empty((S, block_tables.shape[1]), dtype=torch.float32, device=k_pool.device)
+    evict = torch.empty(S, dtype=torch.int32, device=k_pool.device)
+    st = stream if stream is not None else torch.cuda.current_stream(k_pool.device)
+    _lib.paged_kv_block_scores(k_pool, v_pool, block_tables, seq_lens, scores, evict, desc,
+                               st.cuda_stream)
+    return scores, evict

@@ -19,6 +19,7 @@
 #include "decode_mfma.h"
 #include "decode_valu.h"
 #include "kv_write.h"
+#include "evict_scan.h"
 
 namespace pa {
 
@@ -138,6 +139,16 @@ constexpr size_t kCounterBytes = sizeof(int) * kMaxGrid;
 size_t ws_bytes_for(const pa_desc* d) {
   const int64_t G = d->num_q_heads / d->num_kv_heads;
   return kCounterBytes + sizeof(float) * (size_t)(2 * kMaxGrid) * G * (kD + 2);
+}
+
+template <class T>
+hipError_t launch_scores(const ScoreArgs& a, int B, hipStream_t s) {
+  const dim3 grid((unsigned)((a.mbs + kWaves - 1) / kWaves), (unsigned)a.S);
+  if (B == 16)
+    hipLaunchKernelGGL((block_score_kernel<T, 16>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((block_score_kernel<T, 32>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace pa
@@ -390,6 +401,39 @@ int32_t paged_kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, con
   if (grid > cap) grid = cap;
   hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int32_t paged_kv_block_scores(const void* k_pool, const void* v_pool, const int32_t* bt,
+                              const int32_t* lens, float* scores, int32_t* evict,
+                              const pa_desc* d, void* stream) {
+  const int32_t st = pa_check_desc(d);
+  if (st != PA_OK) return st;
+  if (d->num_seqs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !bt || !lens || !scores || !evict) return PA_ERR_NULL;
+  if (((uintptr_t)k_pool | (uintptr_t)v_pool) & 15u) return PA_ERR_ALIGN;
+  if (((uintptr_t)scores | (uintptr_t)evict) & 3u) return PA_ERR_ALIGN;
+  if (!device_info().ok) return PA_ERR_DEVICE;
+  ScoreArgs a;
+  a.kp = k_pool;
+  a.vp = v_pool;
+  a.bt = bt;
+  a.lens = lens;
+  a.scores = scores;
+  a.evict = evict;
+  a.S = d->num_seqs;
+  a.Hkv = d->num_kv_heads;
+  a.mbs = d->max_blocks_per_seq;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (d->dtype) {
+    case PA_F32: e = launch_scores<F32>(a, d->block_size, s); break;
+    case PA_F16: e = launch_scores<F16>(a, d->block_size, s); break;
+    default: e = launch_scores<BF16>(a, d->block_size, s); break;
+  }
+  if (e != hipSuccess) return PA_ERR_LAUNCH;
+  hipLaunchKernelGGL(evict_choice_kernel, dim3((unsigned)((a.S + kWaves - 1) / kWaves)),
+                     dim3(kThreads), 0, s, a, (int)d->block_size);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -591,4 +591,97 @@ def pin_copy_on_write_fork_keeps_the_original(O):
             assert np.max(np.abs(got[b, h] - want)) < 1e-12
 
 
+# ------------------------------------------- block-wise eviction scoring
+# "PagedEviction: Structured Block-wise KV Cache Pruning ...": token
+# importance ||V_t|| / ||K_t|| from the cached rows, block score = mean over
+# the block, the lowest block evicted when the last block has just filled.
+
+def _score_case(seed, lens, B, H=3, D=8, cfac=None, grid=None, fill=np.nan):
+    """Logical K, V [S][H][Lmax][D] (fp64 values exact in float32), pools
+    of the library layout on a shuffled table, `fill` in every other slot."""
+    rng = np.random.default_rng(seed)
+    S, lmax = len(lens), max(max(lens), 1)
+    K = f32_normal(rng, (S, H, lmax, D), grid=grid)
+    V = f32_normal(rng, (S, H, lmax, D), grid=grid)
+    if cfac is not None:  # V = c_j * K inside block j
+        c = np.repeat(np.asarray(cfac, np.float64), B)[:lmax]
+        V = K * c[None, None, :, None]
+    nb = sum(-(-L // B) for L in lens)
+    NB = nb + 5
+    bt = random_tables(rng, lens, B, NB, max(-(-L // B) for L in lens) + 2)
+    kp, vp = scatter(K, V, bt, lens, NB, B, fill=fill)
+    return K, V, bt, np.asarray(lens, np.int32), kp.astype(np.float32), vp.astype(np.float32)
+
+
+def _numpy_scores(K, V, lens, B, M):
+    """Independent evaluation: np.linalg.norm over each token's whole row."""
+    S = K.shape[0]
+    sc = np.full((S, M), np.nan)
+    ev = np.full(S, -1, np.int32)
+    for b, L in enumerate(lens):
+        full = int(L) // B
+        if full:
+            kn = np.linalg.norm(K[b, :, : full * B, :].transpose(1, 0, 2).reshape(full * B, -1), axis=1)
+            vn = np.linalg.norm(V[b, :, : full * B, :].transpose(1, 0, 2).reshape(full * B, -1), axis=1)
+            sc[b, :full] = (vn / kn).reshape(full, B).mean(axis=1)
+        if L > 0 and L % B == 0:
+            ev[b] = int(np.argmin(sc[b, :full]))
+    return sc, ev
+
+
+def pin_block_scores_match_numpy_norms(O):
+    for B in (4, 16, 32):
+        lens = [3 * B, 2 * B + 1, 0, 5 * B, B - 1]
+        K, V, bt, L, kp, vp = _score_case(40 + B, lens, B)
+        got, ev = O.block_scores(kp, vp, bt, L, dtype="f32")
+        want, evw = _numpy_scores(K, V, lens, B, bt.shape[1])
+        assert np.array_equal(np.isnan(got), np.isnan(want)), B
+        ok = ~np.isnan(want)
+        assert np.max(np.abs(got[ok] - want[ok]) / want[ok]) < 1e-12, B
+        assert np.array_equal(ev, evw), (B, ev, evw)
+
+
+def pin_block_score_is_the_value_key_ratio_closed_form(O):
+    """V = c_j K inside block j: every token's ratio is |c_j|, so the block
+    score is |c_j| and the evicted block is the smallest |c_j|."""
+    B = 16
+    c = [1.5, -0.25, 0.75, 2.0, -1.0]
+    K, V, bt, L, kp, vp = _score_case(7, [5 * B], B, cfac=c, grid=6)
+    got, ev = O.block_scores(kp, vp, bt, L, dtype="f32")
+    assert np.max(np.abs(got[0, :5] - np.abs(c)) / np.abs(c)) < 1e-14
+    assert np.all(np.isnan(got[0, 5:]))
+    assert ev[0] == 1
+
+
+def pin_eviction_only_when_the_last_block_just_filled(O):
+    B = 16
+    lens = [2 * B, 2 * B + 3, 0, 1, B]
+    K, V, bt, L, kp, vp = _score_case(8, lens, B, fill=1.0)  # finite slack: a scored partial block shows
+    got, ev = O.block_scores(kp, vp, bt, L, dtype="f32")
+    assert ev[1] == -1 and ev[2] == -1 and ev[3] == -1
+    assert ev[0] in (0, 1) and ev[4] == 0
+    assert not np.isnan(got[1, :2]).any() and np.isnan(got[1, 2:]).all()  # partial block unscored
+    assert np.isnan(got[2]).all() and np.isnan(got[3]).all()
+
+
+def pin_equal_block_scores_pick_the_lowest_block(O):
+    B = 4
+    c = [2.0, 0.5, 1.0, 0.5, 0.5]
+    K, V, bt, L, kp, vp = _score_case(9, [5 * B], B, cfac=c, grid=6)
+    got, ev = O.block_scores(kp, vp, bt, L, dtype="f32")
+    assert ev[0] == 1
+
+
+def pin_block_scores_do_not_depend_on_physical_placement(O):
+    B = 16
+    lens = [4 * B, 3 * B + 5]
+    K, V, bt, L, kp, vp = _score_case(10, lens, B)
+    a, ea = O.block_scores(kp, vp, bt, L, dtype="f32")
+    rng = np.random.default_rng(11)
+    bt2 = random_tables(rng, lens, B, kp.shape[0], bt.shape[1])
+    kp2, vp2 = scatter(K, V, bt2, lens, kp.shape[0], B)
+    b, eb = O.block_scores(kp2.astype(np.float32), vp2.astype(np.float32), bt2, L, dtype="f32")
+    assert np.array_equal(a, b, equal_nan=True) and np.array_equal(ea, eb)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

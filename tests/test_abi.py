@@ -238,10 +238,16 @@ def test_cache_write_argument_errors_before_any_launch(lib):
     assert lib.paged_kv_copy_blocks(P, None, P, P, 3, byref(d), None) == 1
     assert lib.paged_kv_copy_blocks(P, P + 8, P, P, 3, byref(d), None) == 6
     assert lib.paged_kv_copy_blocks(P, P, P, P, 3, byref(_desc(dtype=7)), None) == 3
+    assert lib.paged_kv_block_scores(P, P, P, P, None, P, byref(d), None) == 1
+    assert lib.paged_kv_block_scores(P, P, P, P, P + 2, P, byref(d), None) == 6
+    assert lib.paged_kv_block_scores(P + 4, P, P, P, P, P, byref(d), None) == 6
+    assert lib.paged_kv_block_scores(P, P, P, P, P, P, byref(_desc(head_dim=64)), None) == 4
+    assert lib.paged_kv_block_scores(P, P, P, P, P, P, byref(_desc(num_seqs=0)), None) == 0
     import torch
     if not torch.cuda.is_available():
         assert lib.paged_kv_append(P, P, P, P, P, P, byref(d), None) == 9
         assert lib.paged_kv_copy_blocks(P, P, P, P, 3, byref(d), None) == 9
+        assert lib.paged_kv_block_scores(P, P, P, P, P, P, byref(d), None) == 9
 
 
 def test_binding_refuses_to_run_without_the_library(tmp_path, monkeypatch):

@@ -58,6 +58,20 @@ MUTANTS = [
     ("copy_v_pool_skipped",
      "memmove((char*)v_pool + dst[i] * block_bytes, (const char*)v_pool + src[i] * block_bytes,\n            block_bytes);",
      "(void)v_pool;"),
+    # block-wise eviction scoring
+    ("score_first_head_only", "for (int64_t g = 0; g < H; ++g) {\n          const int64_t base",
+     "for (int64_t g = 0; g < 1; ++g) {\n          const int64_t base"),
+    ("score_squared_norms", "ratio_sum += sqrt(vv) / sqrt(kk);", "ratio_sum += vv / kk;"),
+    ("score_ratio_inverted", "ratio_sum += sqrt(vv) / sqrt(kk);", "ratio_sum += sqrt(kk) / sqrt(vv);"),
+    ("score_sum_not_mean", "scores[b * M + j] = ratio_sum / (double)B;", "scores[b * M + j] = ratio_sum;"),
+    ("score_partial_block_scored", "const int64_t full = L / B;", "const int64_t full = (L + B - 1) / B;"),
+    ("score_v_read_token_major",
+     "const double v = elem(v_pool, dtype, base + (slot / G) * D * G + d * G + slot % G);",
+     "const double v = elem(v_pool, dtype, base + slot * D + d);"),
+    ("evict_without_full_last_block", "if (L > 0 && L % B == 0) {", "if (L > 0) {"),
+    ("evict_ties_pick_last", "if (scores[b * M + j] < best) {", "if (scores[b * M + j] <= best) {"),
+    ("evict_picks_highest", "if (scores[b * M + j] < best) {",
+     "if (best == INFINITY || scores[b * M + j] > best) {"),
 ]
 
 
