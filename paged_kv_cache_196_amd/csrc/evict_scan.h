@@ -13,7 +13,8 @@
 //
 // block_score_kernel: one wave per (sequence, full logical block).  It reads
 // the block's K and V tiles of every KV head (each one contiguous burst,
-// 16 bytes per lane per load), squares and sums in fp32:
+// 16 bytes per lane per load, streaming cache policy: read once), squares
+// and sums in fp32:
 //   K tile rows are token-major, so a load's 16-byte chunks of one row sit
 //   in consecutive lanes and a DPP row reduction (plus one xor-16 step for
 //   fp32 rows) gives the row's sum of squares;
@@ -84,16 +85,17 @@ __global__ __launch_bounds__(kThreads) void block_score_kernel(ScoreArgs a) {
     for (int e = 0; e < E; ++e) vv[s][e] = 0.f;
   }
   for (int h = 0; h < a.Hkv; ++h) {
-    const int64_t tile = ((int64_t)phys * a.Hkv + h) * B * kD * T::kEsize;  // bytes
-    const char* kt = static_cast<const char*>(a.kp) + tile;
-    const char* vt = static_cast<const char*>(a.vp) + tile;
+    // each tile is read once: streaming-policy buffer loads, resource = the tile
+    const int64_t tile = ((int64_t)phys * a.Hkv + uniform(h)) * B * kD * T::kEsize;  // bytes
+    const auto rk = tile_rsrc(a.kp, tile, B * kD * T::kEsize);
+    const auto rv = tile_rsrc(a.vp, tile, B * kD * T::kEsize);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       uint4 kc[NL], vc[NL];
 #pragma unroll
       for (int n = 0; n < NL; ++n) {
-        kc[n] = *reinterpret_cast<const uint4*>(kt + s * kSubBytes + (lane + 64 * n) * 16);
-        vc[n] = *reinterpret_cast<const uint4*>(vt + s * kSubBytes + (lane + 64 * n) * 16);
+        kc[n] = tile_load16<kStreamPolicy>(rk, s * (int)kSubBytes + (lane + 64 * n) * 16, 0);
+        vc[n] = tile_load16<kStreamPolicy>(rv, s * (int)kSubBytes + (lane + 64 * n) * 16, 0);
       }
 #pragma unroll
       for (int n = 0; n < NL; ++n) {

@@ -18,8 +18,9 @@
 // Block copy (§2.3 of the same page: a shared block is copied only when a
 // sequence diverges and writes into it).  A physical block of one pool is
 // one contiguous num_kv_heads * B * head_dim * esize range, a multiple of
-// 4 KiB; the copy moves it in 4 KiB chunks, 16 bytes per thread, with
-// four chunks' loads in flight per workgroup before their stores.
+// 4 KiB; the copy moves it in 4 KiB chunks, 16 bytes per thread (the
+// source with the non-temporal policy: it is read once), with four chunks'
+// loads in flight per workgroup before their stores.
 #pragma once
 
 #include "pa_device.h"
@@ -108,9 +109,9 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(CopyArgs a) {
       char* pool = rem < a.chunks ? a.kp : a.vp;
       const int64_t c = rem % a.chunks;
       const int64_t s = as_constant(a.src)[pair], d = as_constant(a.dst)[pair];
-      const int64_t off = c * kChunkBytes + threadIdx.x * 16;
-      v[u] = *reinterpret_cast<const uint4*>(pool + s * a.block_bytes + off);
-      to[u] = reinterpret_cast<uint4*>(pool + d * a.block_bytes + off);
+      const auto src = tile_rsrc(pool, s * a.block_bytes + c * kChunkBytes, kChunkBytes);
+      v[u] = tile_load16<kStreamPolicy>(src, threadIdx.x * 16, 0);
+      to[u] = reinterpret_cast<uint4*>(pool + d * a.block_bytes + c * kChunkBytes + threadIdx.x * 16);
     }
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u)
