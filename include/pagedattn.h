@@ -81,7 +81,8 @@ typedef enum pa_status {
   PA_ERR_ALIGN = 6,       /* q, pools or out not 16-byte aligned */
   PA_ERR_LAUNCH = 7,      /* the HIP launch reported an error */
   PA_ERR_TABLE = 8,       /* pa_validate_host: table id out of range or bad seq_len */
-  PA_ERR_DEVICE = 9       /* device query failed or the device is not gfx950 */
+  PA_ERR_DEVICE = 9,      /* device query failed or the device is not gfx950 */
+  PA_ERR_NOMEM = 10       /* block manager: not enough free physical blocks */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -287,6 +288,70 @@ int32_t paged_kv_block_scores(const void* k_pool, const void* v_pool,
                               const int32_t* block_tables, const int32_t* seq_lens,
                               float* block_scores, int32_t* evict, const pa_desc* desc,
                               void* stream);
+
+/* ------------------------------------------------------------------
+ * Host block manager (plain C++ on the host; touches no device memory).
+ * "PagedAttention: The Cache Was Storing Nothing", §2.2: the cache is cut
+ * into fixed-size blocks and every request's block table maps its logical
+ * blocks to physical ones; since every free block has the same size any
+ * free block will do, and only a request's last block is partly filled.
+ * §2.3: tables may point at the same physical blocks (shared prompts, beam
+ * search); a block is copied only when a sequence diverges and writes
+ * into it.  Ids come from a bump pointer (never-used blocks in id order)
+ * and a LIFO free list (released blocks, most recent first), O(1) each;
+ * every block counts the table entries that point at it.  Not thread-safe:
+ * calls on one manager must be serialised by the caller.
+ * ------------------------------------------------------------------ */
+
+typedef struct pa_block_manager pa_block_manager; /* opaque */
+
+/* A manager of num_blocks physical blocks of block_size tokens, all free.
+ * NULL if num_blocks <= 0, block_size <= 0 or out of memory.  Owned by the
+ * caller; release with pa_bm_destroy. */
+pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size);
+void pa_bm_destroy(pa_block_manager* bm);
+
+/* Free blocks, or -1 for NULL. */
+int32_t pa_bm_num_free(const pa_block_manager* bm);
+
+/* Table entries pointing at `block` (0 = free), -1 if out of range / NULL. */
+int32_t pa_bm_refcount(const pa_block_manager* bm, int32_t block);
+
+/* n fresh blocks (one reference each) into ids[0..n): all or nothing.
+ * PA_ERR_NOMEM (nothing taken) when fewer than n are free; PA_ERR_SHAPE for
+ * n < 0; PA_ERR_NULL for NULL arguments (ids may be NULL when n == 0). */
+int32_t pa_bm_alloc(pa_block_manager* bm, int32_t n, int32_t* ids);
+
+/* Drop one reference of each of ids[0..n), in order; a block whose count
+ * reaches 0 is free again (a finished sequence releases its table row; an
+ * evicted block is released alone).  PA_ERR_TABLE at the first id that is
+ * out of range or holds no reference (the ones before it are dropped). */
+int32_t pa_bm_release(pa_block_manager* bm, const int32_t* ids, int32_t n);
+
+/* Add one reference to each of ids[0..n) (another table now points at the
+ * block: a shared prefix, a forked beam).  PA_ERR_TABLE at the first id
+ * that is free or out of range (the ones before it stay shared). */
+int32_t pa_bm_share(pa_block_manager* bm, const int32_t* ids, int32_t n);
+
+/* The host side of one decode step: make logical slot L = seq_lens[b]
+ * writable for every sequence b, in order b = 0, 1, ...:
+ *   L % block_size == 0: a fresh block goes into block_tables[b][L / B];
+ *   otherwise, if block_tables[b][L / B] is shared (more than one
+ *   reference): copy-on-write -- a fresh block d replaces the entry, one
+ *   reference of the old block s is dropped, and the pair (s, d) is
+ *   appended to cow_src / cow_dst for paged_kv_copy_blocks;
+ *   positions[b] = L (for paged_kv_append).
+ * seq_lens[b] < 0 skips b (positions[b] = -1).  All arrays are HOST
+ * arrays: block_tables int32 [num_seqs][max_blocks_per_seq] (updated in
+ * place), cow_src / cow_dst of num_seqs entries; *num_cow receives the
+ * number of pairs.  All or nothing: PA_ERR_TABLE if some L / B >=
+ * max_blocks_per_seq or some written entry is not a live block,
+ * PA_ERR_NOMEM if the step needs more fresh blocks than are free; then
+ * nothing changes (*num_cow = 0). */
+int32_t pa_bm_prepare_append(pa_block_manager* bm, int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                             int32_t num_seqs, int32_t* positions, int32_t* cow_src,
+                             int32_t* cow_dst, int32_t* num_cow);
 
 #ifdef __cplusplus
 }

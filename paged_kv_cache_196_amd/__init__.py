@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     PA_KERNEL_MFMA,
     PA_KERNEL_VALU,
     LIB_PATH,
+    BlockManager,
     PaDesc,
     PagedAttnError,
     load,

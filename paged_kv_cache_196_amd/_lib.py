@@ -14,7 +14,7 @@ PA_OK = 0
 STATUS = {
     0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE", 4: "PA_ERR_UNSUPPORTED",
     5: "PA_ERR_WORKSPACE", 6: "PA_ERR_ALIGN", 7: "PA_ERR_LAUNCH", 8: "PA_ERR_TABLE",
-    9: "PA_ERR_DEVICE",
+    9: "PA_ERR_DEVICE", 10: "PA_ERR_NOMEM",
 }
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
@@ -24,7 +24,9 @@ EXPORTS = (
     "pa_status_str", "pa_dtype_size", "pa_blocks_for_len", "pa_pool_bytes", "pa_k_elem_offset",
     "pa_v_elem_offset", "pa_workspace_bytes", "pa_validate_host", "pa_check_desc",
     "paged_attn_decode", "pa_decode_grid", "paged_kv_append", "pa_validate_append_host",
-    "paged_kv_copy_blocks", "pa_validate_copy_host", "paged_kv_block_scores",
+    "paged_kv_copy_blocks", "pa_validate_copy_host", "paged_kv_block_scores", "pa_bm_create",
+    "pa_bm_destroy", "pa_bm_num_free", "pa_bm_refcount", "pa_bm_alloc", "pa_bm_release",
+    "pa_bm_share", "pa_bm_prepare_append",
 )
 
 
@@ -90,6 +92,23 @@ def load() -> ctypes.CDLL:
             lib.pa_validate_copy_host.restype = ctypes.c_int32
             lib.paged_kv_block_scores.argtypes = [_P, _P, _P, _P, _P, _P, _DP, _P]
             lib.paged_kv_block_scores.restype = ctypes.c_int32
+            lib.pa_bm_create.argtypes = [ctypes.c_int32, ctypes.c_int32]
+            lib.pa_bm_create.restype = _P
+            lib.pa_bm_destroy.argtypes = [_P]
+            lib.pa_bm_destroy.restype = None
+            lib.pa_bm_num_free.argtypes = [_P]
+            lib.pa_bm_num_free.restype = ctypes.c_int32
+            lib.pa_bm_refcount.argtypes = [_P, ctypes.c_int32]
+            lib.pa_bm_refcount.restype = ctypes.c_int32
+            for n in ("pa_bm_alloc",):
+                getattr(lib, n).argtypes = [_P, ctypes.c_int32, _P]
+                getattr(lib, n).restype = ctypes.c_int32
+            for n in ("pa_bm_release", "pa_bm_share"):
+                getattr(lib, n).argtypes = [_P, _P, ctypes.c_int32]
+                getattr(lib, n).restype = ctypes.c_int32
+            lib.pa_bm_prepare_append.argtypes = [_P, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, _P,
+                                                 _P, _P]
+            lib.pa_bm_prepare_append.restype = ctypes.c_int32
             _lib = lib
     return _lib
 
@@ -197,3 +216,64 @@ def paged_kv_block_scores(k_pool, v_pool, block_tables, seq_lens, block_scores, 
                                       _ptr(seq_lens), _ptr(block_scores), _ptr(evict),
                                       ctypes.byref(desc), _ptr(stream))
     return _check(rc, "paged_kv_block_scores")
+
+
+class BlockManager:
+    """The library's host block manager (pa_bm_*): marshalling only.  Arrays
+    are contiguous int32 numpy arrays; methods return the pa_status code."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self._lib = load()
+        self.h = self._lib.pa_bm_create(int(num_blocks), int(block_size))
+        if not self.h:
+            raise ValueError("pa_bm_create failed")
+        self.block_size = int(block_size)
+
+    def close(self):
+        if self.h:
+            self._lib.pa_bm_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 - interpreter teardown
+            pass
+
+    def num_free(self) -> int:
+        return int(self._lib.pa_bm_num_free(self.h))
+
+    def refcount(self, block: int) -> int:
+        return int(self._lib.pa_bm_refcount(self.h, int(block)))
+
+    def alloc(self, n: int):
+        import numpy as np
+        ids = np.zeros(max(n, 1), np.int32)
+        rc = int(self._lib.pa_bm_alloc(self.h, int(n), ids.ctypes.data))
+        return rc, (ids[:n] if rc == PA_OK else ids[:0])
+
+    def release(self, ids) -> int:
+        import numpy as np
+        a = np.ascontiguousarray(ids, np.int32)
+        return int(self._lib.pa_bm_release(self.h, a.ctypes.data if a.size else None, a.size))
+
+    def share(self, ids) -> int:
+        import numpy as np
+        a = np.ascontiguousarray(ids, np.int32)
+        return int(self._lib.pa_bm_share(self.h, a.ctypes.data if a.size else None, a.size))
+
+    def prepare_append(self, block_tables, seq_lens):
+        """block_tables: int32 [S][M] numpy array, updated in place.
+        Returns (status, positions, cow_src, cow_dst)."""
+        import numpy as np
+        assert block_tables.dtype == np.int32 and block_tables.flags.c_contiguous
+        lens = np.ascontiguousarray(seq_lens, np.int32)
+        S, M = block_tables.shape
+        pos = np.full(max(S, 1), -1, np.int32)
+        src = np.zeros(max(S, 1), np.int32)
+        dst = np.zeros(max(S, 1), np.int32)
+        n = ctypes.c_int32(0)
+        rc = int(self._lib.pa_bm_prepare_append(self.h, block_tables.ctypes.data, M, lens.ctypes.data,
+                                                S, pos.ctypes.data, src.ctypes.data, dst.ctypes.data,
+                                                ctypes.byref(n)))
+        return rc, pos[:S], src[: n.value], dst[: n.value]

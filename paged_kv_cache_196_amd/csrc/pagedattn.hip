@@ -12,6 +12,7 @@
 
 #include <mutex>
 #include <string.h>
+#include <unordered_map>
 #include <unordered_set>
 
 #include "pagedattn.h"
@@ -20,6 +21,7 @@
 #include "decode_valu.h"
 #include "kv_write.h"
 #include "evict_scan.h"
+#include "block_manager.h"
 
 namespace pa {
 
@@ -169,6 +171,7 @@ const char* pa_status_str(int32_t s) {
     case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: kernel launch failed";
     case PA_ERR_TABLE: return "PA_ERR_TABLE: block table entry or sequence length out of range";
     case PA_ERR_DEVICE: return "PA_ERR_DEVICE: no gfx950 device current";
+    case PA_ERR_NOMEM: return "PA_ERR_NOMEM: not enough free physical blocks";
     default: return "unknown pa_status";
   }
 }
@@ -435,6 +438,104 @@ int32_t paged_kv_block_scores(const void* k_pool, const void* v_pool, const int3
   hipLaunchKernelGGL(evict_choice_kernel, dim3((unsigned)((a.S + kWaves - 1) / kWaves)),
                      dim3(kThreads), 0, s, a, (int)d->block_size);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+struct pa_block_manager {
+  pa::BlockManager m;
+};
+
+pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size) {
+  if (num_blocks <= 0 || block_size <= 0) return nullptr;
+  try {
+    return new pa_block_manager{pa::BlockManager(num_blocks, block_size)};
+  } catch (...) {
+    return nullptr;
+  }
+}
+
+void pa_bm_destroy(pa_block_manager* bm) { delete bm; }
+
+int32_t pa_bm_num_free(const pa_block_manager* bm) { return bm ? bm->m.num_free() : -1; }
+
+int32_t pa_bm_refcount(const pa_block_manager* bm, int32_t block) {
+  return bm ? bm->m.refcount(block) : -1;
+}
+
+int32_t pa_bm_alloc(pa_block_manager* bm, int32_t n, int32_t* ids) {
+  if (!bm || (n > 0 && !ids)) return PA_ERR_NULL;
+  if (n < 0) return PA_ERR_SHAPE;
+  if (bm->m.num_free() < n) return PA_ERR_NOMEM;
+  for (int32_t i = 0; i < n; ++i) ids[i] = bm->m.take();
+  return PA_OK;
+}
+
+int32_t pa_bm_release(pa_block_manager* bm, const int32_t* ids, int32_t n) {
+  if (!bm || (n > 0 && !ids)) return PA_ERR_NULL;
+  if (n < 0) return PA_ERR_SHAPE;
+  for (int32_t i = 0; i < n; ++i)
+    if (!bm->m.drop(ids[i])) return PA_ERR_TABLE;
+  return PA_OK;
+}
+
+int32_t pa_bm_share(pa_block_manager* bm, const int32_t* ids, int32_t n) {
+  if (!bm || (n > 0 && !ids)) return PA_ERR_NULL;
+  if (n < 0) return PA_ERR_SHAPE;
+  for (int32_t i = 0; i < n; ++i)
+    if (!bm->m.share(ids[i])) return PA_ERR_TABLE;
+  return PA_OK;
+}
+
+int32_t pa_bm_prepare_append(pa_block_manager* bm, int32_t* bt, int32_t mbs, const int32_t* lens,
+                             int32_t num_seqs, int32_t* pos, int32_t* cow_src, int32_t* cow_dst,
+                             int32_t* num_cow) {
+  if (!bm || !num_cow) return PA_ERR_NULL;
+  *num_cow = 0;
+  if (num_seqs < 0 || mbs <= 0) return PA_ERR_SHAPE;
+  if (num_seqs > 0 && (!bt || !lens || !pos || !cow_src || !cow_dst)) return PA_ERR_NULL;
+  const int32_t B = bm->m.block_size();
+  // Pass 1: validate every sequence and count the fresh blocks the step
+  // needs (a copy of a block shared only within this batch is needed once:
+  // after the first writer copies it, the next one owns it alone).
+  std::unordered_map<int32_t, int32_t> drops;
+  int64_t need = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int32_t L = lens[b];
+    if (L < 0) continue;
+    if (L / B >= mbs) return PA_ERR_TABLE;
+    if (L % B == 0) {
+      ++need;
+      continue;
+    }
+    const int32_t e = bt[(int64_t)b * mbs + L / B];
+    const int32_t rc = bm->m.refcount(e) - (drops.count(e) ? drops[e] : 0);
+    if (rc <= 0) return PA_ERR_TABLE;
+    if (rc > 1) {
+      ++need;
+      ++drops[e];
+    }
+  }
+  if (need > bm->m.num_free()) return PA_ERR_NOMEM;
+  // Pass 2: apply (cannot fail).
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int32_t L = lens[b];
+    if (L < 0) {
+      pos[b] = -1;
+      continue;
+    }
+    int32_t* entry = bt + (int64_t)b * mbs + L / B;
+    if (L % B == 0) {
+      *entry = bm->m.take();
+    } else if (bm->m.refcount(*entry) > 1) {
+      const int32_t id = bm->m.take();
+      cow_src[*num_cow] = *entry;
+      cow_dst[*num_cow] = id;
+      ++*num_cow;
+      bm->m.drop(*entry);
+      *entry = id;
+    }
+    pos[b] = L;
+  }
+  return PA_OK;
 }
 
 }  // extern "C"

@@ -186,3 +186,77 @@ def test_fork_append_decode_loop(O, dtype):
     assert err <= TOL[dtype]
     # twins differ only by the new token: their outputs must differ
     assert not np.array_equal(ref[:S], ref[S:])
+
+
+def test_block_manager_drives_fork_append_evict_decode(O):
+    """One serving step end to end through the library: the host block
+    manager allocates every sequence's blocks and forks each one (its twin
+    shares all blocks), prepares the next token's slot (fresh blocks at
+    block boundaries, copy-on-write pairs for shared partly filled blocks);
+    the GPU copies and appends and decodes; the scan chooses a block to
+    evict for every sequence whose last block just filled, the manager
+    releases it and the tables are compacted; the GPU decodes again.  Each
+    decode is compared with the fp64 oracle on the oracle's own pools."""
+    B, Hq, Hkv, NB = 16, 8, 2, 400
+    lens0 = [5, 15, 16, 47, 100, 129]
+    S = len(lens0)
+    bm = pa.BlockManager(NB, B)
+    M = 16
+    bt = np.full((2 * S, M), -1, np.int32)
+    for b, L in enumerate(lens0):
+        st, ids = bm.alloc(-(-L // B))
+        assert st == 0
+        bt[b, : ids.size] = ids
+        assert bm.share(ids) == 0
+        bt[S + b] = bt[b]
+    lens = np.asarray(lens0 + lens0, np.int32)
+    w = workload.build(name="bm", dtype="bf16", seq_lens=lens, num_q_heads=Hq, num_kv_heads=Hkv,
+                       head_dim=128, block_size=B, seed=31, tables=[list(r[r >= 0]) for r in bt],
+                       num_blocks=NB, max_blocks_per_seq=M)
+    bt = np.ascontiguousarray(w.block_tables)
+    st, pos, src, dst = bm.prepare_append(bt, lens)
+    assert st == 0 and list(pos) == list(lens)
+    assert len(src) == sum(1 for L in lens0 if L % B)  # one copy per shared, partly filled block
+    d = _desc(w)
+    assert pa.pa_validate_copy_host(d, src, dst, len(src)) == 0
+    assert pa.pa_validate_append_host(d, bt, pos) == 0
+    rng = np.random.default_rng(32)
+    kn, vn = _new_rows(w, rng)
+    k, v = device_tensor(w.k_pool, "bf16"), device_tensor(w.v_pool, "bf16")
+    _log("[kv_write] block manager: copy, append, decode")
+    pa.copy_blocks(k, v, torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda())
+    pa.append(device_tensor(kn, "bf16"), device_tensor(vn, "bf16"), k, v, torch.from_numpy(bt).cuda(),
+              torch.from_numpy(pos).cuda())
+    kw, vw = O.copy_blocks(w.k_pool, w.v_pool, src, dst)
+    kw, vw = O.append(kn, vn, kw, vw, bt, pos)
+    lens1 = lens + 1
+    scale = np.float64(np.float32(w.scale))
+    q = device_tensor(w.q, "bf16")
+    out = pa.decode(q, k, v, torch.from_numpy(bt).cuda(), torch.from_numpy(lens1).cuda(), float(w.scale))
+    ref = O.paged_decode(w.q, kw, vw, bt, lens1, scale, num_kv_heads=Hkv, block_size=B, dtype="bf16")
+    assert max_err(out, ref) <= TOL["bf16"]
+    # eviction for the sequences whose last block just filled
+    sc, ev = pa.block_scores(k, v, torch.from_numpy(bt).cuda(), torch.from_numpy(lens1).cuda())
+    ev = ev.cpu().numpy()
+    wsc, wev = O.block_scores(kw, vw, bt, lens1, dtype="bf16")
+    due = [b for b in range(2 * S) if lens1[b] % B == 0]
+    assert due and all(ev[b] >= 0 for b in due) and all(ev[b] == -1 for b in range(2 * S) if b not in due)
+    for b in due:
+        if ev[b] != wev[b]:  # only a near-tie of the two lowest fp64 scores allows another choice
+            w2 = np.sort(wsc[b, : lens1[b] // B])
+            assert w2[1] - w2[0] <= 2e-4 * w2[0], (b, ev[b], wev[b])
+        j = int(ev[b])
+        assert bm.release([bt[b, j]]) == 0
+        row = [int(x) for x in bt[b, : lens1[b] // B]]
+        del row[j]
+        bt[b] = -1
+        bt[b, : len(row)] = row
+        lens1[b] -= B
+    out2 = pa.decode(q, k, v, torch.from_numpy(bt).cuda(), torch.from_numpy(lens1).cuda(), float(w.scale))
+    ref2 = O.paged_decode(w.q, kw, vw, bt, lens1, scale, num_kv_heads=Hkv, block_size=B, dtype="bf16")
+    err = max_err(out2, ref2)
+    _log(f"[kv_write] block manager loop: decode after eviction max_abs_err={err:.3e}")
+    assert err <= TOL["bf16"]
+    live = set(int(x) for x in bt[bt >= 0].ravel())
+    assert bm.num_free() == NB - len(live)
+    bm.close()
