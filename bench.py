@@ -422,6 +422,80 @@ def eviction_scores(w, kp, vp, dev, flush, stream, with_cpu: bool) -> dict:
     return res
 
 
+def block_manager_timing(w, with_cpu: bool, steps: int = 50) -> dict:
+    """Host block manager (pa_bm_*) latencies: allocating and releasing a
+    large batch of single blocks (per block, one call each way), and the
+    append preparation of one decode step for the workload's batch (tables
+    built by the manager without sharing, `steps` consecutive steps, mean
+    per step, the C entry point called directly with preallocated arrays).
+    The plain model in oracle/ is timed on the same steps."""
+    import ctypes
+
+    import numpy as np
+
+    import paged_kv_cache_196_amd as pa
+
+    B, S = w.block_size, w.num_seqs
+    NB = max(w.num_blocks, int((-(-w.seq_lens.astype(np.int64) // B)).sum()) + S * (steps // B + 2))
+    bm = pa.BlockManager(NB, B)
+    n = min(NB, 1 << 16)
+    ta, tr = [], []
+    for _ in range(20):
+        t0 = time.perf_counter()
+        st, ids = bm.alloc(n)
+        t1 = time.perf_counter()
+        st2 = bm.release(ids)
+        t2 = time.perf_counter()
+        if st or st2:
+            raise RuntimeError("block manager alloc / release failed")
+        ta.append(t1 - t0)
+        tr.append(t2 - t1)
+    lens0 = w.seq_lens.astype(np.int32)
+    M = int(-(-(int(lens0.max()) + steps) // B)) + 1
+
+    def fresh(model=None):
+        tables = np.full((S, M), -1, np.int32)
+        for b, L in enumerate(lens0):
+            k = -(-int(L) // B)
+            st, ids = (model.alloc(k) if model is not None else bm.alloc(k))
+            tables[b, :k] = ids
+        return tables
+
+    tables = fresh()
+    lens = lens0.copy()
+    pos, src, dst = (np.zeros(S, np.int32) for _ in range(3))
+    ncow = ctypes.c_int32(0)
+    fn = pa.load().pa_bm_prepare_append
+    args = (bm.h, tables.ctypes.data, M, lens.ctypes.data, S, pos.ctypes.data, src.ctypes.data,
+            dst.ctypes.data, ctypes.byref(ncow))
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        if fn(*args):
+            raise RuntimeError("prepare_append failed")
+        lens += 1
+    t_step = (time.perf_counter() - t0) / steps
+    bm.close()
+    res = {
+        "bound": "host (no device work)",
+        "alloc_ns_per_block": round(statistics.median(ta) / n * 1e9, 2),
+        "release_ns_per_block": round(statistics.median(tr) / n * 1e9, 2),
+        "blocks_per_call": n,
+        "prepare_append_us_per_step": round(t_step * 1e6, 2),
+        "sequences": S,
+    }
+    if with_cpu:
+        from oracle.block_manager import BlockManagerModel
+        m = BlockManagerModel(NB, B)
+        mt = [list(r) for r in fresh(m)]
+        ml = [int(x) for x in lens0]
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            st, pos, cows = m.prepare_append(mt, ml)
+            ml = [x + 1 for x in ml]
+        res["model_prepare_append_us_per_step"] = round((time.perf_counter() - t0) / steps * 1e6, 1)
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -612,6 +686,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, kv_unique, args.cpu_seconds)
+    result["block_manager"] = block_manager_timing(w, with_cpu=not args.no_cpu_baseline)
     if not args.no_eviction_scores:
         result["eviction_scores"] = eviction_scores(w, kp, vp, dev, flush, stream,
                                                     with_cpu=not args.no_cpu_baseline)
