@@ -108,6 +108,25 @@ def test_all_sequences_empty():
         assert torch.count_nonzero(out).item() == 0
 
 
+@pytest.mark.parametrize("kern", ["mfma", "valu"])
+def test_max_batch_many_pieces_per_chunk(O, kern):
+    """The largest batch the library takes (8192 sequences: the length
+    prefix in LDS at capacity) with lengths 0..100, one in ten empty: the
+    length scan runs 32 passes with carries, empty sequences sit between the
+    pieces, and every chunk meets ~57 (sequence, KV head) pairs, so its
+    pieces are listed and streamed in more than one batch."""
+    rng = np.random.default_rng(8192)
+    lens = rng.integers(0, 101, size=8192)
+    lens[rng.random(8192) < 0.1] = 0
+    w = workload.build(name="maxbatch", dtype="bf16", seq_lens=lens, num_q_heads=16, num_kv_heads=4,
+                       head_dim=128, block_size=16, seed=77)
+    _log(f"[parity] max batch 8192 kernel={kern}")
+    ref = O.run_workload(w)
+    err = max_err(Uploaded(w).run(kern), ref)
+    _log(f"[parity] max batch kernel={kern} max_abs_err={err:.3e}")
+    assert err <= TOL["bf16"], err
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_output_in_input_dtype(O, dtype):
     """out_dtype = input dtype: the fp32 result rounded once (RNE), so the
