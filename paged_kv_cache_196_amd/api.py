@@ -95,24 +95,32 @@ def decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, *,
     return out
 
 
-def _pool_desc(k_pool: torch.Tensor, v_pool: torch.Tensor, block_tables: torch.Tensor,
-               num_seqs: int) -> _lib.PaDesc:
-    """Descriptor for the cache-writing calls (they use the pool and table
-    shapes; the query-head count is set to the KV-head count)."""
-    for name, t in (("k_pool", k_pool), ("v_pool", v_pool), ("block_tables", block_tables)):
+def _check_table(block_tables: torch.Tensor, num_seqs: int) -> None:
+    if not block_tables.is_cuda or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be a contiguous device tensor")
+    if block_tables.dtype != torch.int32:
+        raise TypeError("block_tables must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != num_seqs:
+        raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq]")
+
+
+def _pool_desc(k_pool: torch.Tensor, v_pool: torch.Tensor, num_seqs: int,
+               max_blocks_per_seq: int) -> _lib.PaDesc:
+    """Descriptor for the calls that work on the pools alone (they use the
+    pool shape and the table width; the query-head count is set to the
+    KV-head count)."""
+    for name, t in (("k_pool", k_pool), ("v_pool", v_pool)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if block_tables.dtype != torch.int32:
-        raise TypeError("block_tables must be int32")
     if v_pool.dtype != k_pool.dtype:
         raise TypeError("k_pool and v_pool must share a dtype")
     NB, Hkv, B, D = k_pool.shape
     if B % 16 != 0 or tuple(v_pool.shape) != (NB, Hkv, B // 16, D, 16):
         raise ValueError("v_pool must be [num_blocks][num_kv_heads][block_size/16][head_dim][16]")
     dt = pa_dtype_of(k_pool.dtype)
-    return _lib.PaDesc(num_seqs, Hkv, Hkv, D, B, NB, block_tables.shape[1], dt, _lib.PA_F32,
+    return _lib.PaDesc(num_seqs, Hkv, Hkv, D, B, NB, max_blocks_per_seq, dt, _lib.PA_F32,
                        _lib.PA_KERNEL_AUTO, 0)
 
 
@@ -128,14 +136,13 @@ def append(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor, v_poo
             raise ValueError(f"{name} must be a contiguous device tensor")
     if positions.dtype != torch.int32:
         raise TypeError("positions must be int32")
-    desc = _pool_desc(k_pool, v_pool, block_tables, S)
+    _check_table(block_tables, S)
+    desc = _pool_desc(k_pool, v_pool, S, block_tables.shape[1])
     want = (S, desc.num_kv_heads, desc.head_dim)
     if tuple(k_new.shape) != want or tuple(v_new.shape) != want:
         raise ValueError(f"k_new and v_new must be {list(want)}")
     if k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype:
         raise TypeError("k_new, v_new and the pools must share a dtype")
-    if block_tables.shape[0] != S:
-        raise ValueError("block_tables needs one row per sequence")
     st = stream if stream is not None else torch.cuda.current_stream(k_pool.device)
     _lib.paged_kv_append(k_new, v_new, k_pool, v_pool, block_tables, positions, desc,
                          st.cuda_stream)
@@ -151,8 +158,7 @@ def copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, src_blocks: torch.Te
     for name, t in (("src_blocks", src_blocks), ("dst_blocks", dst_blocks)):
         if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.int32:
             raise ValueError(f"{name} must be a contiguous int32 device tensor")
-    table = torch.zeros((1, 1), dtype=torch.int32, device=k_pool.device)
-    desc = _pool_desc(k_pool, v_pool, table, 1)
+    desc = _pool_desc(k_pool, v_pool, 1, 1)
     st = stream if stream is not None else torch.cuda.current_stream(k_pool.device)
     _lib.paged_kv_copy_blocks(k_pool, v_pool, src_blocks, dst_blocks, n, desc, st.cuda_stream)
 
@@ -165,9 +171,8 @@ def block_scores(k_pool: torch.Tensor, v_pool: torch.Tensor, block_tables: torch
     if not seq_lens.is_cuda or not seq_lens.is_contiguous() or seq_lens.dtype != torch.int32:
         raise ValueError("seq_lens must be a contiguous int32 device tensor")
     S = seq_lens.shape[0]
-    desc = _pool_desc(k_pool, v_pool, block_tables, S)
-    if block_tables.shape[0] != S:
-        raise ValueError("block_tables needs one row per sequence")
+    _check_table(block_tables, S)
+    desc = _pool_desc(k_pool, v_pool, S, block_tables.shape[1])
     scores = torch.empty((S, block_tables.shape[1]), dtype=torch.float32, device=k_pool.device)
     evict = torch.empty(S, dtype=torch.int32, device=k_pool.device)
     st = stream if stream is not None else torch.cuda.current_stream(k_pool.device)
