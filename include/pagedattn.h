@@ -76,7 +76,9 @@ typedef enum pa_status {
   PA_ERR_NULL = 1,        /* a required pointer is NULL */
   PA_ERR_SHAPE = 2,       /* a size is <= 0 (cached_prefix_blocks < 0), or num_q_heads % num_kv_heads != 0 */
   PA_ERR_DTYPE = 3,       /* unknown dtype, or out_dtype neither PA_F32 nor dtype */
-  PA_ERR_UNSUPPORTED = 4, /* valid but not built: head_dim, block_size, group size, kernel/dtype pair */
+  PA_ERR_UNSUPPORTED = 4, /* valid but not built: head_dim, block_size, group size, kernel/dtype pair,
+                             or the decode workgroup's LDS (length prefix of a very large batch plus
+                             the group-16 staging) does not fit a CU */
   PA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than pa_workspace_bytes() */
   PA_ERR_ALIGN = 6,       /* q, pools or out not 16-byte aligned */
   PA_ERR_LAUNCH = 7,      /* the HIP launch reported an error */
@@ -182,7 +184,8 @@ int32_t paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Number of decode workgroups a launch uses for this descriptor on the
- * current device (the split-K granularity), or -1 on error. */
+ * current device (the split-K granularity: CUs x resident workgroups per
+ * CU), or -1 on error or when the workgroup's LDS does not fit a CU. */
 int32_t pa_decode_grid(const pa_desc* desc);
 
 /* ------------------------------------------------------------------

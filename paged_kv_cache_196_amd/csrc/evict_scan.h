@@ -53,11 +53,11 @@ __device__ __forceinline__ float chunk_sumsq(const uint4& c) {
   return s;
 }
 
-// Grid: (ceil(mbs / kWaves), S) workgroups of kThreads; wave -> block
-// j = blockIdx.x * kWaves + wave of sequence blockIdx.y.  Entries of blocks
+// Grid: (ceil(mbs / kAuxWaves), S) workgroups of kAuxThreads; wave -> block
+// j = blockIdx.x * kAuxWaves + wave of sequence blockIdx.y.  Entries of blocks
 // that are not full (j >= L / B) are set to NaN.
 template <class T, int B>
-__global__ __launch_bounds__(kThreads) void block_score_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kAuxThreads) void block_score_kernel(ScoreArgs a) {
   constexpr int E = 16 / T::kEsize;         // elements per 16-byte chunk
   constexpr int CPR = kD * T::kEsize / 16;  // chunks per key row: 16 or 32
   constexpr int TPL = 64 / CPR;             // key rows per wave load: 4 or 2
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void block_score_kernel(ScoreArgs a) {
   constexpr int64_t kSubBytes = (int64_t)kSub * kD * T::kEsize;
   const int lane = threadIdx.x & 63;
   const int b = blockIdx.y;
-  const int j = uniform(blockIdx.x * kWaves + (threadIdx.x >> 6));
+  const int j = uniform(blockIdx.x * kAuxWaves + (threadIdx.x >> 6));
   if (j >= a.mbs) return;
   const int L = as_constant(a.lens)[b];
   float* out = a.scores + (int64_t)b * a.mbs + j;
@@ -149,11 +149,11 @@ __global__ __launch_bounds__(kThreads) void block_score_kernel(ScoreArgs a) {
   if (lane == 0) *out = total / (float)B;
 }
 
-// Grid: ceil(S / kWaves) workgroups; wave -> sequence.  evict[b] = arg-min
+// Grid: ceil(S / kAuxWaves) workgroups; wave -> sequence.  evict[b] = arg-min
 // of scores[b][0 .. L/B) when L > 0 and L % B == 0, else -1.
-__global__ __launch_bounds__(kThreads) void evict_choice_kernel(ScoreArgs a, int B) {
+__global__ __launch_bounds__(kAuxThreads) void evict_choice_kernel(ScoreArgs a, int B) {
   const int lane = threadIdx.x & 63;
-  const int b = uniform(blockIdx.x * kWaves + (threadIdx.x >> 6));
+  const int b = uniform(blockIdx.x * kAuxWaves + (threadIdx.x >> 6));
   if (b >= a.S) return;
   const int L = as_constant(a.lens)[b];
   if (L <= 0 || L % B != 0) {

@@ -44,15 +44,15 @@ struct Bits<2> { using T = uint16_t; using Pair = uint32_t; };
 template <>
 struct Bits<4> { using T = uint32_t; using Pair = uint2; };
 
-// Grid: ceil(S * Hkv / kWaves) workgroups of kThreads; wave = one
+// Grid: ceil(S * Hkv / kAuxWaves) workgroups of kAuxThreads; wave = one
 // (sequence, KV head).  Lane l moves dims 2l and 2l + 1.
 template <int kEsize>
-__global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
+__global__ __launch_bounds__(kAuxThreads) void append_kernel(AppendArgs a) {
   using E = typename Bits<kEsize>::T;
   using E2 = typename Bits<kEsize>::Pair;
   static_assert(kD == 128, "two dims per lane");
   const int lane = threadIdx.x & 63;
-  const int i = uniform(blockIdx.x * kWaves + (threadIdx.x >> 6));
+  const int i = uniform(blockIdx.x * kAuxWaves + (threadIdx.x >> 6));
   if (i >= a.S * a.Hkv) return;
   const int b = i / a.Hkv, kvh = i % a.Hkv;
   const int t = as_constant(a.pos)[b];
@@ -95,7 +95,7 @@ constexpr int kCopyUnroll = 4;  // chunks per workgroup pass
 // Work item w = ((pair * 2) + pool) * chunks + c.  Grid-stride over passes
 // of kCopyUnroll consecutive items; item indices are wave-uniform, so the
 // id lookups are scalar loads.
-__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(CopyArgs a) {
+__global__ __launch_bounds__(kAuxThreads) void copy_blocks_kernel(CopyArgs a) {
   const int per_pair = 2 * a.chunks;
   for (int w0 = blockIdx.x * kCopyUnroll; w0 < a.total; w0 += gridDim.x * kCopyUnroll) {
     uint4 v[kCopyUnroll];

@@ -10,8 +10,10 @@
 namespace pa {
 
 constexpr int kD = 128;          // head_dim the kernels are built for
-constexpr int kWaves = 4;        // waves per workgroup
+constexpr int kWaves = 8;        // waves per decode workgroup (one workgroup per CU)
 constexpr int kThreads = 64 * kWaves;
+constexpr int kAuxWaves = 4;     // waves per workgroup of the cache-write and scan kernels
+constexpr int kAuxThreads = 64 * kAuxWaves;
 constexpr int kSub = 16;         // tokens per sub-tile (unit of the streaming loop)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxGrid = 2048;   // upper bound on decode workgroups (sizes the workspace)

@@ -145,11 +145,11 @@ size_t ws_bytes_for(const pa_desc* d) {
 
 template <class T>
 hipError_t launch_scores(const ScoreArgs& a, int B, hipStream_t s) {
-  const dim3 grid((unsigned)((a.mbs + kWaves - 1) / kWaves), (unsigned)a.S);
+  const dim3 grid((unsigned)((a.mbs + kAuxWaves - 1) / kAuxWaves), (unsigned)a.S);
   if (B == 16)
-    hipLaunchKernelGGL((block_score_kernel<T, 16>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((block_score_kernel<T, 16>), grid, dim3(kAuxThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((block_score_kernel<T, 32>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((block_score_kernel<T, 32>), grid, dim3(kAuxThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -261,7 +261,8 @@ int32_t pa_decode_grid(const pa_desc* d) {
   if (!info.ok) return -1;
   const Variant v = pick(d);
   const int per_cu = v.occ(prefix_lds(d->num_seqs));
-  int grid = info.cus * (per_cu > 0 ? per_cu : 1);
+  if (per_cu <= 0) return -1;  // the workgroup's LDS does not fit a CU
+  int grid = info.cus * per_cu;
   if (grid > kMaxGrid) grid = kMaxGrid;
   return grid;
 }
@@ -278,8 +279,9 @@ static int32_t prepare(const void* q, const void* k_pool, const void* v_pool, co
   if (!q || !k_pool || !v_pool || !bt || !lens || !out) return PA_ERR_NULL;
   if (((uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool | (uintptr_t)out) & 15u) return PA_ERR_ALIGN;
   if (!ws || ws_bytes < pa_workspace_bytes(d) || ((uintptr_t)ws & 15u)) return PA_ERR_WORKSPACE;
+  if (!device_info().ok) return PA_ERR_DEVICE;
   const int g = pa_decode_grid(d);
-  if (g <= 0) return PA_ERR_DEVICE;
+  if (g <= 0) return PA_ERR_UNSUPPORTED;  // LDS of this batch size and group does not fit
   const int G = d->num_q_heads / d->num_kv_heads;
   a->q = q;
   a->kp = k_pool;
@@ -352,12 +354,12 @@ int32_t paged_kv_append(const void* k_new, const void* v_new, void* k_pool, void
   a.Hkv = d->num_kv_heads;
   a.B = d->block_size;
   a.mbs = d->max_blocks_per_seq;
-  const int grid = (int)(((int64_t)a.S * a.Hkv + kWaves - 1) / kWaves);
+  const int grid = (int)(((int64_t)a.S * a.Hkv + kAuxWaves - 1) / kAuxWaves);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (pa_dtype_size(d->dtype) == 4)
-    hipLaunchKernelGGL(append_kernel<4>, dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(append_kernel<4>, dim3(grid), dim3(kAuxThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(append_kernel<2>, dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(append_kernel<2>, dim3(grid), dim3(kAuxThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
@@ -402,7 +404,7 @@ int32_t paged_kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, con
   int64_t grid = (total + kCopyUnroll - 1) / kCopyUnroll;
   const int64_t cap = (int64_t)info.cus * 8;
   if (grid > cap) grid = cap;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)grid), dim3(kAuxThreads), 0,
                      static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
@@ -435,8 +437,8 @@ int32_t paged_kv_block_scores(const void* k_pool, const void* v_pool, const int3
     default: e = launch_scores<BF16>(a, d->block_size, s); break;
   }
   if (e != hipSuccess) return PA_ERR_LAUNCH;
-  hipLaunchKernelGGL(evict_choice_kernel, dim3((unsigned)((a.S + kWaves - 1) / kWaves)),
-                     dim3(kThreads), 0, s, a, (int)d->block_size);
+  hipLaunchKernelGGL(evict_choice_kernel, dim3((unsigned)((a.S + kAuxWaves - 1) / kAuxWaves)),
+                     dim3(kAuxThreads), 0, s, a, (int)d->block_size);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
