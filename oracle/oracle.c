@@ -378,3 +378,84 @@ int oracle_block_scores(const void* k_pool, const void* v_pool, const int32_t* b
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------
+ * Paged prefill: many query rows per sequence, causal.
+ *
+ * "FlashAttention vs PagedAttention", "How prefill and decode change the
+ * diagnosis": prefill scores many prompt positions at once against a cache
+ * whose length differs from the number of queries.  "Paging the KV cache
+ * with a fused mask" ("What carries the argument", and its list of
+ * assumptions: masking a query to its own keys leaves exact attention
+ * unchanged) maps every query to its own sequence's pages.
+ * Readings (the pages print no convention):
+ *  - sequence b contributes n_b = q_start[b+1] - q_start[b] query rows,
+ *    rows q_start[b] .. q_start[b+1]-1 of q and out; they are its NEWEST
+ *    n_b tokens, already in the cache, so row i sits at position
+ *    p = L_b - n_b + i (chunked prefill: L_b - n_b earlier tokens are
+ *    cached from before);
+ *  - causal: row i attends tokens 0 .. p of the table, nothing later;
+ *  - n_b = 1 is single-token decode, n_b = L_b a whole prompt.
+ * Each row is plain softmax attention over its p + 1 gathered tokens.
+ * Returns 0, -1 on a table error, -2 on bad sizes (including n_b < 0 or
+ * n_b > L_b), -3 on allocation failure.
+ * ------------------------------------------------------------------ */
+int oracle_paged_prefill(const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* block_tables, const int32_t* seq_lens,
+                         const int32_t* q_start, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t num_blocks, int32_t max_blocks_per_seq, int32_t dtype,
+                         double scale, double* out, int32_t num_threads) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      block_size <= 0 || num_q_heads % num_kv_heads != 0)
+    return -2;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t n = (int64_t)q_start[b + 1] - q_start[b];
+    if (n < 0 || seq_lens[b] < 0 || n > seq_lens[b]) return -2;
+  }
+  const int64_t D = head_dim;
+  const int64_t G = num_q_heads / num_kv_heads;
+  const size_t qsize = dtype == ORC_F32 ? 4 : 2;
+  const int64_t units = (int64_t)num_seqs * num_kv_heads;
+  int status = 0;
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+#else
+  (void)num_threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < units; ++u) {
+    const int32_t b = (int32_t)(u / num_kv_heads);
+    const int32_t g = (int32_t)(u % num_kv_heads);
+    const int64_t Lb = seq_lens[b];
+    const int64_t n = (int64_t)q_start[b + 1] - q_start[b];
+    const int64_t rows = Lb > 0 ? Lb : 1;
+    double* K = (double*)malloc(sizeof(double) * rows * D);
+    double* V = (double*)malloc(sizeof(double) * rows * D);
+    double* s = (double*)malloc(sizeof(double) * rows);
+    double* qrow = (double*)malloc(sizeof(double) * D);
+    if (!K || !V || !s || !qrow) {
+#pragma omp atomic write
+      status = -3;
+    } else if (oracle_gather(k_pool, v_pool, block_tables, b, g, Lb, num_kv_heads, head_dim,
+                             block_size, num_blocks, max_blocks_per_seq, dtype, K, V) != 0) {
+#pragma omp atomic write
+      status = -1;
+    } else {
+      for (int64_t i = 0; i < n; ++i) {
+        const int64_t row = q_start[b] + i;  /* row of q and out */
+        const int64_t p = Lb - n + i;        /* its position in the sequence */
+        for (int64_t k = 0; k < G; ++k) {
+          const int64_t off = (row * num_q_heads + g * G + k) * D;
+          oracle_to_f64((const char*)q + off * qsize, dtype, D, qrow);
+          oracle_attention(qrow, K, V, p + 1, D, scale, out + off, s);  /* tokens 0 .. p */
+        }
+      }
+    }
+    free(K);
+    free(V);
+    free(s);
+    free(qrow);
+  }
+  return status;
+}

@@ -85,6 +85,9 @@ class Oracle:
         lib.oracle_block_scores.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                             _I32, _P, _P]
         lib.oracle_block_scores.restype = ctypes.c_int
+        lib.oracle_paged_prefill.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                             _I32, _I32, _I32, _D, _P, _I32]
+        lib.oracle_paged_prefill.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         self.lib = lib
@@ -233,6 +236,36 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_block_scores: table entry out of range")
         return scores, evict
+
+    def paged_prefill(self, q, k_pool, v_pool, block_tables, seq_lens, q_start, scale, *,
+                      num_kv_heads: int, block_size: int, dtype: str,
+                      num_threads: int = 0) -> np.ndarray:
+        """fp64 out[total_q][Hq][D] of causal paged prefill.
+
+        q: [total_q][Hq][D]; rows q_start[b] .. q_start[b+1]-1 are the
+        newest q_start[b+1]-q_start[b] tokens of sequence b (already in the
+        pools), row i of them at position seq_lens[b] - n_b + i, attending
+        tokens 0 .. that position.  Pools, tables, dtype and scale as for
+        paged_decode.
+        """
+        q = _c(q)
+        k_pool = _c(k_pool)
+        v_pool = _c(v_pool)
+        bt = _c(block_tables, np.int32)
+        lens = _c(seq_lens, np.int32)
+        qs = _c(q_start, np.int32)
+        T, Hq, D = q.shape
+        S = lens.shape[0]
+        if qs.shape[0] != S + 1 or qs[-1] != T:
+            raise ValueError("q_start must hold num_seqs + 1 offsets ending at the row count")
+        out = np.zeros((T, Hq, D), np.float64)
+        rc = self.lib.oracle_paged_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(bt), _ptr(lens),
+                                           _ptr(qs), S, Hq, num_kv_heads, D, block_size,
+                                           k_pool.shape[0], bt.shape[1], DTYPE_CODES[dtype],
+                                           float(scale), _ptr(out), int(num_threads))
+        if rc != 0:
+            raise ValueError(f"oracle_paged_prefill failed with code {rc}")
+        return out
 
     def run_workload(self, w, num_threads: int = 0) -> np.ndarray:
         """paged_decode on a workload.Workload-like object."""

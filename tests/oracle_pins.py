@@ -684,4 +684,81 @@ def pin_block_scores_do_not_depend_on_physical_placement(O):
     assert np.array_equal(a, b, equal_nan=True) and np.array_equal(ea, eb)
 
 
+# ------------------------------------------------------------ paged prefill
+# Readings: the n_b query rows of sequence b are its newest tokens (row i at
+# position L_b - n_b + i) and each attends tokens 0 .. its position.
+
+def _prefill_case(seed, lens=(9, 16, 5), nq=(9, 4, 1), Hq=4, Hkv=2, D=16, B=4):
+    rng = np.random.default_rng(seed)
+    S, Lmax = len(lens), max(lens)
+    Klog = f32_normal(rng, (S, Hkv, Lmax, D))
+    Vlog = f32_normal(rng, (S, Hkv, Lmax, D))
+    NB = sum(-(-L // B) for L in lens) + 3
+    bt = random_tables(rng, lens, B, NB, -(-Lmax // B) + 1)
+    kp, vp = scatter(Klog, Vlog, bt, lens, NB, B, fill=0.0)
+    qs = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    q = f32_normal(rng, (int(qs[-1]), Hq, D))
+    scale = 1.0 / math.sqrt(D)
+    return dict(q=q, kp=kp, vp=vp, bt=bt, lens=np.asarray(lens, np.int32), qs=qs,
+                Klog=Klog, Vlog=Vlog, Hkv=Hkv, B=B, scale=scale)
+
+
+def _prefill(O, c):
+    return O.paged_prefill(c["q"].astype(np.float32), c["kp"].astype(np.float32),
+                           c["vp"].astype(np.float32), c["bt"], c["lens"], c["qs"], c["scale"],
+                           num_kv_heads=c["Hkv"], block_size=c["B"], dtype="f32")
+
+
+def pin_prefill_matches_library_sdpa_with_bottom_right_causal_mask(O):
+    c = _prefill_case(11)
+    out = _prefill(O, c)
+    Hq = c["q"].shape[1]
+    G = Hq // c["Hkv"]
+    for b, L in enumerate(c["lens"]):
+        r0, r1 = int(c["qs"][b]), int(c["qs"][b + 1])
+        n = r1 - r0
+        pos = L - n + np.arange(n)
+        mask = torch.from_numpy(np.arange(L)[None, :] <= pos[:, None])
+        for h in range(Hq):
+            qt = torch.from_numpy(c["q"][r0:r1, h])[None, None]
+            K = torch.from_numpy(c["Klog"][b, h // G, :L])[None, None]
+            V = torch.from_numpy(c["Vlog"][b, h // G, :L])[None, None]
+            ref = torch.nn.functional.scaled_dot_product_attention(qt, K, V, attn_mask=mask,
+                                                                   scale=c["scale"])[0, 0].numpy()
+            assert np.allclose(out[r0:r1, h], ref, rtol=0, atol=1e-12), (b, h)
+
+
+def pin_prefill_row_equals_decode_at_its_position(O):
+    c = _prefill_case(12, lens=(13, 7, 20), nq=(5, 7, 3))
+    out = _prefill(O, c)
+    for b, L in enumerate(c["lens"]):
+        r0, r1 = int(c["qs"][b]), int(c["qs"][b + 1])
+        for i in range(r1 - r0):
+            lens = np.zeros_like(c["lens"])
+            lens[b] = L - (r1 - r0) + i + 1          # the sequence as it stood at that row
+            q = np.zeros((len(c["lens"]),) + c["q"].shape[1:])
+            q[b] = c["q"][r0 + i]
+            ref = decode_f64(O, q, c["kp"], c["vp"], c["bt"], lens, c["scale"], c["Hkv"], c["B"])
+            assert np.allclose(out[r0 + i], ref[b], rtol=0, atol=1e-13), (b, i)
+
+
+def pin_prefill_first_prompt_row_is_value_row_zero(O):
+    c = _prefill_case(13, lens=(6, 11), nq=(6, 11))
+    out = _prefill(O, c)
+    G = c["q"].shape[1] // c["Hkv"]
+    for b in range(2):
+        r0 = int(c["qs"][b])
+        for h in range(c["q"].shape[1]):
+            assert np.array_equal(out[r0, h], c["Vlog"][b, h // G, 0]), (b, h)
+
+
+def pin_prefill_more_rows_than_tokens_is_an_error(O):
+    c = _prefill_case(14, lens=(3, 5), nq=(4, 1))
+    try:
+        _prefill(O, c)
+    except ValueError:
+        return
+    raise AssertionError("4 query rows over 3 cached tokens were accepted")
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -72,6 +72,16 @@ MUTANTS = [
     ("evict_ties_pick_last", "if (scores[b * M + j] < best) {", "if (scores[b * M + j] <= best) {"),
     ("evict_picks_highest", "if (scores[b * M + j] < best) {",
      "if (best == INFINITY || scores[b * M + j] > best) {"),
+    # paged prefill
+    ("prefill_not_causal", "oracle_attention(qrow, K, V, p + 1, D, scale, out + off, s);",
+     "oracle_attention(qrow, K, V, Lb, D, scale, out + off, s);"),
+    ("prefill_position_off_by_one", "const int64_t p = Lb - n + i; ", "const int64_t p = Lb - n + i - 1; "),
+    ("prefill_causal_top_left", "const int64_t p = Lb - n + i; ", "const int64_t p = i; "),
+    ("prefill_rows_from_zero", "const int64_t row = q_start[b] + i;", "const int64_t row = i;"),
+    ("prefill_head_mapping_strided", "const int64_t off = (row * num_q_heads + g * G + k) * D;",
+     "const int64_t off = (row * num_q_heads + k * num_kv_heads + g) * D;"),
+    ("prefill_rows_beyond_cache_accepted", "if (n < 0 || seq_lens[b] < 0 || n > seq_lens[b]) return -2;",
+     "if (n < 0 || seq_lens[b] < 0) return -2;"),
 ]
 
 
