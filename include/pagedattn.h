@@ -189,6 +189,44 @@ int32_t paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
 int32_t pa_decode_grid(const pa_desc* desc);
 
 /* ------------------------------------------------------------------
+ * Paged prefill: many query rows per sequence, causal.
+ * ------------------------------------------------------------------ */
+
+/* Causal prefill attention over the paged cache, one kernel launch on
+ * `stream` ("FlashAttention vs PagedAttention", "How prefill and decode
+ * change the diagnosis": prefill scores many prompt positions against a
+ * cache whose length differs from the query count; "Paging the KV cache
+ * with a fused mask", "What carries the argument": every query reads
+ * exactly its own sequence's pages).
+ *
+ * q, out: [total_q][num_q_heads][head_dim], total_q = q_start[num_seqs].
+ * q_start: int32 [num_seqs + 1] row offsets, q_start[0] = 0.  Sequence b
+ * owns rows q_start[b] .. q_start[b+1]-1: its NEWEST n_b = q_start[b+1] -
+ * q_start[b] tokens, whose K/V are already in the pools (written with
+ * paged_kv_append or by the caller); row i sits at position
+ * seq_lens[b] - n_b + i and attends tokens 0 .. that position (the causal
+ * mask aligned to the end of the sequence).  n_b = seq_lens[b] is a whole
+ * prompt, smaller n_b a chunk of one; n_b = 0 leaves the sequence out.
+ * max_q_len >= every n_b (launch size; rows beyond it are not computed).
+ * Pools, block_tables, seq_lens, scale, dtype, out_dtype: as for
+ * paged_attn_decode.  No workspace.  Matrix cores only: fp16 / bf16 with
+ * kernel AUTO or MFMA, else PA_ERR_UNSUPPORTED.  Data-dependent
+ * preconditions are checked by pa_validate_prefill_host, not on the device;
+ * a sequence with n_b > seq_lens[b] is skipped by the kernel. */
+int32_t paged_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_tables, const int32_t* seq_lens,
+                           const int32_t* q_start, int32_t max_q_len, float scale, void* out,
+                           const pa_desc* desc, void* stream);
+
+/* pa_validate_host on host copies, then: q_start[0] == 0 and
+ * 0 <= q_start[b+1] - q_start[b] <= min(max_q_len, seq_lens[b]).  PA_OK, a
+ * descriptor error, PA_ERR_NULL, PA_ERR_SHAPE (max_q_len < 0) or
+ * PA_ERR_TABLE. */
+int32_t pa_validate_prefill_host(const pa_desc* desc, const int32_t* block_tables_host,
+                                 const int32_t* seq_lens_host, const int32_t* q_start_host,
+                                 int32_t max_q_len);
+
+/* ------------------------------------------------------------------
  * Writing the cache: the steps around the decode call on the same layout.
  * ------------------------------------------------------------------ */
 

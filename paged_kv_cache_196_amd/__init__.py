@@ -29,12 +29,14 @@ from ._lib import (  # noqa: F401
     pa_validate_append_host,
     pa_validate_copy_host,
     pa_validate_host,
+    pa_validate_prefill_host,
     pa_workspace_bytes,
     paged_attn_decode,
+    paged_attn_prefill,
     paged_kv_append,
     paged_kv_block_scores,
     paged_kv_copy_blocks,
     status_str,
 )
 from .api import (  # noqa: F401
-    append, block_scores, copy_blocks, decode, ensure_built, make_desc, new_workspace)
+    append, block_scores, copy_blocks, decode, ensure_built, make_desc, new_workspace, prefill)

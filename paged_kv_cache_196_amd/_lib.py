@@ -26,7 +26,7 @@ EXPORTS = (
     "paged_attn_decode", "pa_decode_grid", "paged_kv_append", "pa_validate_append_host",
     "paged_kv_copy_blocks", "pa_validate_copy_host", "paged_kv_block_scores", "pa_bm_create",
     "pa_bm_destroy", "pa_bm_num_free", "pa_bm_refcount", "pa_bm_alloc", "pa_bm_release",
-    "pa_bm_share", "pa_bm_prepare_append",
+    "pa_bm_share", "pa_bm_prepare_append", "paged_attn_prefill", "pa_validate_prefill_host",
 )
 
 
@@ -92,6 +92,11 @@ def load() -> ctypes.CDLL:
             lib.pa_validate_copy_host.restype = ctypes.c_int32
             lib.paged_kv_block_scores.argtypes = [_P, _P, _P, _P, _P, _P, _DP, _P]
             lib.paged_kv_block_scores.restype = ctypes.c_int32
+            lib.paged_attn_prefill.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_float,
+                                               _P, _DP, _P]
+            lib.paged_attn_prefill.restype = ctypes.c_int32
+            lib.pa_validate_prefill_host.argtypes = [_DP, _P, _P, _P, ctypes.c_int32]
+            lib.pa_validate_prefill_host.restype = ctypes.c_int32
             lib.pa_bm_create.argtypes = [ctypes.c_int32, ctypes.c_int32]
             lib.pa_bm_create.restype = _P
             lib.pa_bm_destroy.argtypes = [_P]
@@ -169,6 +174,14 @@ def pa_validate_host(desc: PaDesc, block_tables_host, seq_lens_host) -> int:
                                        seq_lens_host.ctypes.data))
 
 
+def pa_validate_prefill_host(desc: PaDesc, block_tables_host, seq_lens_host, q_start_host,
+                             max_q_len: int) -> int:
+    """Host copies as contiguous int32 numpy arrays; q_start_host [S + 1]."""
+    return int(load().pa_validate_prefill_host(ctypes.byref(desc), block_tables_host.ctypes.data,
+                                               seq_lens_host.ctypes.data, q_start_host.ctypes.data,
+                                               int(max_q_len)))
+
+
 def pa_decode_grid(desc: PaDesc) -> int:
     return int(load().pa_decode_grid(ctypes.byref(desc)))
 
@@ -179,6 +192,14 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, o
                                   _ptr(seq_lens), float(scale), _ptr(out), ctypes.byref(desc),
                                   _ptr(workspace), int(workspace_bytes), _ptr(stream))
     return _check(rc, "paged_attn_decode")
+
+
+def paged_attn_prefill(q, k_pool, v_pool, block_tables, seq_lens, q_start, max_q_len: int,
+                       scale: float, out, desc: PaDesc, stream=None) -> int:
+    rc = load().paged_attn_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                                   _ptr(seq_lens), _ptr(q_start), int(max_q_len), float(scale),
+                                   _ptr(out), ctypes.byref(desc), _ptr(stream))
+    return _check(rc, "paged_attn_prefill")
 
 
 def paged_kv_append(k_new, v_new, k_pool, v_pool, block_tables, positions, desc: PaDesc,

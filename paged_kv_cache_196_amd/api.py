@@ -95,6 +95,51 @@ def decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, *,
     return out
 
 
+def prefill(q, k_pool, v_pool, block_tables, seq_lens, q_start, scale: float, *,
+            max_q_len: int | None = None, out: torch.Tensor | None = None,
+            out_dtype: torch.dtype | None = torch.float32, kernel: int = _lib.PA_KERNEL_AUTO,
+            stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """Causal paged prefill on device tensors; returns out [total_q][Hq][D].
+
+    q [total_q][Hq][D]; q_start int32 [S + 1] row offsets: sequence b owns
+    rows q_start[b] .. q_start[b+1]-1, its newest tokens (already in the
+    pools), row i at position seq_lens[b] - n_b + i attending tokens 0 ..
+    that position.  max_q_len: the largest n_b (read from q_start on the
+    host when not given, which synchronises).  Pools and tables as for
+    decode(); fp16 / bf16 only."""
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool),
+                    ("block_tables", block_tables), ("seq_lens", seq_lens), ("q_start", q_start)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32 or q_start.dtype != torch.int32:
+        raise TypeError("block_tables, seq_lens and q_start must be int32")
+    if k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+        raise TypeError("q, k_pool and v_pool must share a dtype")
+    S = seq_lens.shape[0]
+    if q_start.shape != (S + 1,):
+        raise ValueError("q_start must be [num_seqs + 1]")
+    NB, Hkv, B, D = k_pool.shape
+    if B % 16 != 0 or tuple(v_pool.shape) != (NB, Hkv, B // 16, D, 16):
+        raise ValueError("v_pool must be [num_blocks][num_kv_heads][block_size/16][head_dim][16]")
+    _check_table(block_tables, S)
+    T, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError("q and k_pool head_dim differ")
+    if max_q_len is None:
+        max_q_len = int((q_start[1:] - q_start[:-1]).max().item()) if S else 0
+    dt = pa_dtype_of(q.dtype)
+    odt = dt if out_dtype is None else pa_dtype_of(out_dtype)
+    desc = _lib.PaDesc(S, Hq, Hkv, D, B, NB, block_tables.shape[1], dt, odt, kernel, 0)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    _lib.paged_attn_prefill(q, k_pool, v_pool, block_tables, seq_lens, q_start, max_q_len, scale,
+                            out, desc, st.cuda_stream)
+    return out
+
+
 def _check_table(block_tables: torch.Tensor, num_seqs: int) -> None:
     if not block_tables.is_cuda or not block_tables.is_contiguous():
         raise ValueError("block_tables must be a contiguous device tensor")

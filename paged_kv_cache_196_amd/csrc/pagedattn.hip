@@ -21,6 +21,7 @@
 #include "decode_valu.h"
 #include "kv_write.h"
 #include "evict_scan.h"
+#include "prefill_mfma.h"
 #include "block_manager.h"
 
 namespace pa {
@@ -151,6 +152,34 @@ hipError_t launch_scores(const ScoreArgs& a, int B, hipStream_t s) {
   else
     hipLaunchKernelGGL((block_score_kernel<T, 32>), grid, dim3(kAuxThreads), 0, s, a);
   return hipGetLastError();
+}
+
+using PrefillFn = void (*)(const PrefillArgs&, dim3, hipStream_t);
+
+template <class T, int B, int G>
+void launch_prefill(const PrefillArgs& a, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((prefill_kernel<T, B, G>), grid, dim3(kAuxThreads), 0, s, a);
+}
+
+template <class T, int B>
+PrefillFn prefill_for_group(int G) {
+  switch (G) {
+    case 1: return launch_prefill<T, B, 1>;
+    case 2: return launch_prefill<T, B, 2>;
+    case 4: return launch_prefill<T, B, 4>;
+    case 8: return launch_prefill<T, B, 8>;
+    case 16: return launch_prefill<T, B, 16>;
+    default: return nullptr;
+  }
+}
+
+// Prefill variant of a descriptor: matrix cores only (fp16 / bf16).
+PrefillFn pick_prefill(const pa_desc* d) {
+  if (d->kernel == PA_KERNEL_VALU || d->dtype == PA_F32) return nullptr;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  const bool bf = d->dtype == PA_BF16;
+  if (d->block_size == 16) return bf ? prefill_for_group<BF16, 16>(G) : prefill_for_group<F16, 16>(G);
+  return bf ? prefill_for_group<BF16, 32>(G) : prefill_for_group<F16, 32>(G);
 }
 
 }  // namespace pa
@@ -538,6 +567,58 @@ int32_t pa_bm_prepare_append(pa_block_manager* bm, int32_t* bt, int32_t mbs, con
     pos[b] = L;
   }
   return PA_OK;
+}
+
+int32_t pa_validate_prefill_host(const pa_desc* d, const int32_t* bt, const int32_t* lens,
+                                 const int32_t* q_start, int32_t max_q_len) {
+  const int32_t st = pa_validate_host(d, bt, lens);
+  if (st != PA_OK) return st;
+  if (!q_start) return PA_ERR_NULL;
+  if (max_q_len < 0) return PA_ERR_SHAPE;
+  if (q_start[0] != 0) return PA_ERR_TABLE;
+  for (int32_t b = 0; b < d->num_seqs; ++b) {
+    const int64_t n = (int64_t)q_start[b + 1] - q_start[b];
+    if (n < 0 || n > max_q_len || n > lens[b]) return PA_ERR_TABLE;
+  }
+  return PA_OK;
+}
+
+int32_t paged_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* bt, const int32_t* lens, const int32_t* q_start,
+                           int32_t max_q_len, float scale, void* out, const pa_desc* d,
+                           void* stream) {
+  const int32_t st = pa_check_desc(d);
+  if (st != PA_OK) return st;
+  if (max_q_len < 0) return PA_ERR_SHAPE;
+  const PrefillFn launch = pick_prefill(d);
+  if (!launch) return PA_ERR_UNSUPPORTED;
+  if (d->num_seqs == 0 || max_q_len == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !bt || !lens || !q_start || !out) return PA_ERR_NULL;
+  if (((uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool | (uintptr_t)out) & 15u) return PA_ERR_ALIGN;
+  if (!device_info().ok) return PA_ERR_DEVICE;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  const int R = kSub / G;
+  const int64_t tiles = (max_q_len + R - 1) / R;
+  const int64_t items = tiles * d->num_kv_heads;
+  if (items >= ((int64_t)1 << 31) - kAuxWaves) return PA_ERR_UNSUPPORTED;
+  PrefillArgs a;
+  a.q = q;
+  a.kp = k_pool;
+  a.vp = v_pool;
+  a.bt = bt;
+  a.lens = lens;
+  a.qs = q_start;
+  a.out = out;
+  a.scale_log2 = scale * kLog2e;
+  a.S = d->num_seqs;
+  a.Hq = d->num_q_heads;
+  a.Hkv = d->num_kv_heads;
+  a.mbs = d->max_blocks_per_seq;
+  a.tiles = (int32_t)tiles;
+  a.out_f32 = d->out_dtype == PA_F32 ? 1 : 0;
+  const dim3 grid((unsigned)((items + kAuxWaves - 1) / kAuxWaves), (unsigned)d->num_seqs);
+  launch(a, grid, static_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -255,3 +255,46 @@ def test_binding_refuses_to_run_without_the_library(tmp_path, monkeypatch):
     monkeypatch.setattr(pa._lib, "_lib", None)
     with pytest.raises(ImportError):
         pa._lib.load()
+
+
+def test_validate_prefill_host(lib):
+    w = workload.make(3, 3, batch=8, max_len=700)
+    d = pa.PaDesc(w.num_seqs, 32, 8, 128, 16, w.num_blocks, w.max_blocks_per_seq, pa.PA_BF16, pa.PA_F32, 0)
+    bt = np.ascontiguousarray(w.block_tables)
+    lens = np.ascontiguousarray(w.seq_lens)
+    n = np.minimum(lens, 37).astype(np.int32)
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    assert pa.pa_validate_prefill_host(d, bt, lens, qs, int(n.max())) == 0
+    assert pa.pa_validate_prefill_host(d, bt, lens, qs, int(n.max()) - 1) == 8  # a chunk beyond max_q_len
+    assert pa.pa_validate_prefill_host(d, bt, lens, qs, -1) == 2
+    bad = qs.copy()
+    bad[0] = 1
+    assert pa.pa_validate_prefill_host(d, bt, lens, bad, 10 ** 6) == 8
+    bad = qs.copy()
+    bad[2] = bad[1] - 1                                                           # negative row count
+    assert pa.pa_validate_prefill_host(d, bt, lens, bad, 10 ** 6) == 8
+    short = lens.copy()
+    short[0] = n[0] - 1                                                           # more rows than tokens
+    assert pa.pa_validate_prefill_host(d, bt, short, qs, 10 ** 6) == 8
+    bad = bt.copy()
+    bad[1, 0] = -5
+    assert pa.pa_validate_prefill_host(d, bad, lens, qs, 10 ** 6) == 8
+
+
+def test_prefill_argument_errors_before_any_launch(lib):
+    d = _desc()
+    byref = pa._lib.ctypes.byref
+    P = 1 << 20  # fake aligned address; not dereferenced on these paths
+    args = [P, P, P, P, P, P, 64, 0.1, P]
+    assert lib.paged_attn_prefill(None, *args[1:], byref(d), None) == 1
+    assert lib.paged_attn_prefill(*args[:5], None, *args[6:], byref(d), None) == 1
+    assert lib.paged_attn_prefill(P + 2, *args[1:], byref(d), None) == 6
+    assert lib.paged_attn_prefill(*args[:6], -1, *args[7:], byref(d), None) == 2
+    assert lib.paged_attn_prefill(*args, byref(_desc(dtype=pa.PA_F32)), None) == 4
+    assert lib.paged_attn_prefill(*args, byref(_desc(kernel=pa.PA_KERNEL_VALU)), None) == 4
+    assert lib.paged_attn_prefill(*args, byref(_desc(head_dim=64)), None) == 4
+    assert lib.paged_attn_prefill(*args, byref(_desc(num_seqs=0)), None) == 0
+    assert lib.paged_attn_prefill(*args[:6], 0, *args[7:], byref(d), None) == 0
+    import torch
+    if not torch.cuda.is_available():
+        assert lib.paged_attn_prefill(*args, byref(d), None) == 9

@@ -1,0 +1,128 @@
+"""GPU parity of causal paged prefill (paged_attn_prefill through the C
+ABI) against the fp64 oracle.  Bar: max |out - oracle| <= 2e-3 (fp16 /
+bf16 inputs, fp32 accumulation).
+
+Rows are each sequence's newest n_b tokens, row i at position L - n_b + i,
+attending tokens 0 .. that position.  Small cases compare every output with
+the oracle's prefill; the full-size GQA prompt batch compares sampled rows
+with the oracle's decode at each row's position (a pinned equivalence)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_196_amd as pa
+import workload
+from tests.gpu_util import TOL, device_tensor, max_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def O():
+    oracle.build(force=False)
+    return oracle.load()
+
+
+def _run(w, q, qs, out_dtype=torch.float32, kernel=pa.PA_KERNEL_AUTO):
+    qd = device_tensor(q, w.dtype)
+    out = pa.prefill(qd, device_tensor(w.k_pool, w.dtype), device_tensor(w.v_pool, w.dtype),
+                     torch.from_numpy(w.block_tables).cuda(), torch.from_numpy(w.seq_lens).cuda(),
+                     torch.from_numpy(qs).cuda(), float(w.scale), out_dtype=out_dtype, kernel=kernel)
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle(O, w, q, qs):
+    return O.paged_prefill(q, w.k_pool, w.v_pool, w.block_tables, w.seq_lens, qs,
+                           np.float64(np.float32(w.scale)), num_kv_heads=w.num_kv_heads,
+                           block_size=w.block_size, dtype=w.dtype)
+
+
+LENS = [1, 2, 15, 16, 17, 33, 64, 65, 129, 300, 511]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("B", [16, 32])
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+def test_prefill_ragged(O, dtype, B, G):
+    """Whole prompts, chunks, single rows and empty query sets over lengths
+    around block and sub-tile boundaries, for each group size."""
+    rng = np.random.default_rng(2000 + B + G)
+    lens = list(LENS) + [40, 200]
+    rng.shuffle(lens)
+    w = workload.build(name="prefill-edges", dtype=dtype, seq_lens=lens, num_q_heads=2 * G,
+                       num_kv_heads=2, head_dim=128, block_size=B, seed=int(rng.integers(1 << 30)))
+    kinds = rng.integers(0, 4, size=len(lens))
+    q_lens = [L if k == 0 else (1 if k == 1 else (0 if k == 2 else int(rng.integers(1, L + 1))))
+              for L, k in zip(lens, kinds)]
+    q_lens[0] = lens[0]  # at least one whole prompt
+    q, qs = workload.prefill_queries(w, q_lens, seed=B * 100 + G)
+    _log(f"[prefill] {dtype} B={B} G={G} rows={int(qs[-1])}")
+    ref = _oracle(O, w, q, qs)
+    err = max_err(_run(w, q, qs), ref)
+    _log(f"[prefill] {dtype} B={B} G={G} max_abs_err={err:.3e}")
+    assert err <= TOL[dtype], (dtype, B, G, err)
+
+
+def test_prefill_output_in_input_type_and_forced_kernel(O):
+    w = workload.make(3, 21, batch=3, max_len=700)
+    q, qs = workload.prefill_queries(w, [int(L) for L in w.seq_lens], seed=3)
+    ref = _oracle(O, w, q, qs)
+    got = _run(w, q, qs, out_dtype=torch.bfloat16, kernel=pa.PA_KERNEL_MFMA)
+    assert got.dtype == torch.bfloat16
+    # bf16 output adds at most half an ulp of |out| <= max |v| to the bar
+    bound = TOL["bf16"] + float(np.abs(ref).max()) * 2.0 ** -8
+    assert max_err(got, ref) <= bound
+    with pytest.raises(pa.PagedAttnError):
+        _run(w, q, qs, kernel=pa.PA_KERNEL_VALU)
+
+
+def test_prefill_first_row_is_value_row_and_single_row_is_decode(O):
+    """Row 0 of a whole prompt attends token 0 alone (out = its value row);
+    a single-row prefill equals the decode kernel on the same query."""
+    w = workload.make(3, 22, batch=4, max_len=900)
+    q, qs = workload.prefill_queries(w, [int(L) for L in w.seq_lens], seed=4)
+    got = _run(w, q, qs).double().cpu().numpy()
+    K, V = O.gather(w.k_pool, w.v_pool, w.block_tables, 0, 0, 1, num_kv_heads=w.num_kv_heads,
+                    head_dim=w.head_dim, block_size=w.block_size, dtype=w.dtype)
+    for h in range(w.group):  # the query heads of KV head 0
+        assert np.array_equal(got[0, h], V[0]), h
+    ones, qs1 = workload.prefill_queries(w, [1] * w.num_seqs, seed=5)
+    pre = _run(w, ones, qs1)
+    dec = pa.decode(device_tensor(ones, w.dtype), device_tensor(w.k_pool, w.dtype),
+                    device_tensor(w.v_pool, w.dtype), torch.from_numpy(w.block_tables).cuda(),
+                    torch.from_numpy(w.seq_lens).cuda(), float(w.scale))
+    torch.cuda.synchronize()
+    assert torch.max(torch.abs(pre - dec)).item() <= 1e-4
+
+
+def test_prefill_gqa_prompt_batch_full_size_sampled(O):
+    """The benchmarked prefill workload (8 whole prompts of 2048 tokens, GQA
+    32/8, bf16, B = 16): sampled rows against the oracle's decode at each
+    row's position."""
+    w, q, qs = workload.prefill_workload()
+    got = _run(w, q, qs).double().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(7)
+    worst = 0.0
+    for b in range(w.num_seqs):
+        n = int(qs[b + 1] - qs[b])
+        L = int(w.seq_lens[b])
+        for i in sorted(set(rng.integers(0, n, size=6).tolist()) | {0, n - 1}):
+            lens = np.zeros(w.num_seqs, np.int32)
+            lens[b] = L - n + i + 1
+            qq = np.zeros((w.num_seqs, w.num_q_heads, w.head_dim), q.dtype)
+            qq[b] = q[qs[b] + i]
+            ref = O.paged_decode(qq, w.k_pool, w.v_pool, w.block_tables, lens,
+                                 np.float64(np.float32(w.scale)), num_kv_heads=w.num_kv_heads,
+                                 block_size=w.block_size, dtype=w.dtype)[b]
+            worst = max(worst, float(np.max(np.abs(got[qs[b] + i] - ref))))
+    _log(f"[prefill] full size sampled max_abs_err={worst:.3e}")
+    assert worst <= TOL["bf16"]

@@ -299,3 +299,31 @@ def kv_bytes(w: Workload, unique: bool = False) -> int:
         v[-1] = int(w.seq_lens[b]) - (n - 1) * B
         np.maximum.at(valid, w.block_tables[b, :n].astype(np.int64), v)
     return int(valid.sum()) * per_token
+
+
+def prefill_queries(w: Workload, q_lens, seed: int):
+    """Query rows for a prefill over workload w's cache: sequence b gets
+    q_lens[b] rows (its newest q_lens[b] tokens, 0 <= q_lens[b] <=
+    seq_lens[b]).  Values N(0, 1), rounded once to w.dtype like the decode
+    queries.  Returns (q storage [sum q_lens][Hq][D], q_start int32 [S + 1])."""
+    q_lens = np.asarray(q_lens, np.int64)
+    assert q_lens.shape == (w.num_seqs,)
+    assert np.all(q_lens >= 0) and np.all(q_lens <= w.seq_lens)
+    q_start = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7])))
+    x = rng.standard_normal((int(q_start[-1]), w.num_q_heads, w.head_dim), dtype=np.float32)
+    return round_to(x, w.dtype), q_start
+
+
+PREFILL_NAME = "prefill GQA 32/8 heads, 8 whole prompts x 2048 tokens, bf16, B=16"
+
+
+def prefill_workload(seed: int = 6, num_prompts: int = 8, prompt_len: int = 2048):
+    """Prompt prefill over the paged cache with the GQA batch's head shapes:
+    num_prompts whole prompts of prompt_len tokens, their K/V already in
+    shuffled physical blocks, every token a query row.  Returns
+    (w, q storage [num_prompts * prompt_len][32][128], q_start)."""
+    w = build(name=PREFILL_NAME, dtype="bf16", seq_lens=[prompt_len] * num_prompts,
+              num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, seed=seed)
+    q, q_start = prefill_queries(w, [prompt_len] * num_prompts, seed)
+    return w, q, q_start
