@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix, published
 METRIC = "paged decode attention: achieved KV GB/s (% of HBM peak) and tokens/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 CSRC = os.path.join(ROOT, "paged_kv_cache_196_amd", "csrc")
@@ -422,6 +423,60 @@ def eviction_scores(w, kp, vp, dev, flush, stream, with_cpu: bool) -> dict:
     return res
 
 
+def prefill_timing(dev, flush, stream, with_cpu: bool) -> dict:
+    """Causal paged prefill (paged_attn_prefill) of 8 whole prompts of 2048
+    tokens with the GQA batch's head shapes (32 query / 8 KV heads, D 128,
+    bf16, B 16, shuffled blocks), bf16 output.  Algorithmic flops: 4 * D per
+    (query row, query head, attended key): 2 D for q.k and 2 D for the
+    weighted value sum; row i of a whole prompt attends i + 1 keys.  Timed
+    with HIP events; the oracle is timed on a bounded sample (the last 32
+    rows of the first prompt)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_196_amd as pa
+    import workload
+    from tests.gpu_util import device_tensor
+
+    w, q, qs = workload.prefill_workload()
+    n = np.diff(qs).astype(np.int64)
+    L = w.seq_lens.astype(np.int64)
+    keys = int(sum(((Lb - nb + 1) + Lb) * nb // 2 for Lb, nb in zip(L, n)))  # sum of (p + 1)
+    flops = 4 * w.head_dim * w.num_q_heads * keys
+    args = [device_tensor(q, w.dtype), device_tensor(w.k_pool, w.dtype),
+            device_tensor(w.v_pool, w.dtype), torch.from_numpy(w.block_tables).to(dev),
+            torch.from_numpy(w.seq_lens).to(dev), torch.from_numpy(qs).to(dev)]
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    max_q = int(n.max())
+    mean, med = _time_events(
+        lambda: pa.prefill(*args, float(w.scale), max_q_len=max_q, out=out,
+                           out_dtype=torch.bfloat16, stream=stream), flush, stream, 10)
+    tflops = flops / (mean * 1e-3) / 1e12
+    res = {
+        "workload": w.name, "kernel": "prefill_kernel", "query_rows": int(qs[-1]),
+        "us_per_call": round(mean * 1e3, 2), "us_median": round(med * 1e3, 2),
+        "algorithmic_flops": flops, "tflops": round(tflops, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+    }
+    if with_cpu:
+        import oracle
+        O = oracle.load()
+        rows = 32
+        Lb = int(L[0])
+        qs_s = np.array([0, rows], np.int32)
+        q_s = np.ascontiguousarray(q[qs[1] - rows: qs[1]])
+        t = _cpu_time(lambda: O.paged_prefill(q_s, w.k_pool, w.v_pool, w.block_tables[:1],
+                                              w.seq_lens[:1], qs_s, np.float64(np.float32(w.scale)),
+                                              num_kv_heads=w.num_kv_heads, block_size=w.block_size,
+                                              dtype=w.dtype, num_threads=1), budget_s=5.0)
+        f_s = 4 * w.head_dim * w.num_q_heads * sum(Lb - rows + 1 + i for i in range(rows))
+        res["cpu_oracle"] = {"tflops": round(f_s / t / 1e12, 5), "seconds": round(t, 3), "cores": 1,
+                             "kind": "oracle",
+                             "sample": f"last {rows} rows of the first prompt, fp64 C, one thread"}
+    return res
+
+
 def block_manager_timing(w, with_cpu: bool, steps: int = 50) -> dict:
     """Host block manager (pa_bm_*) latencies: allocating and releasing a
     large batch of single blocks (per block, one call each way), and the
@@ -515,6 +570,8 @@ def main() -> int:
                     help="skip timing the append / block-copy calls")
     ap.add_argument("--no-eviction-scores", action="store_true",
                     help="skip timing the block-wise eviction scoring")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip timing the causal paged prefill")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the calibration copy (for rocprofv3 counter scaling)")
     ap.add_argument("--summarize-counters", nargs=4, metavar="DIR",
@@ -694,6 +751,8 @@ def main() -> int:
         # after the decode timing and its check: these write (unread) pool slots
         result["cache_writes"] = cache_writes(w, kp, vp, dev, flush, stream,
                                               with_cpu=not args.no_cpu_baseline)
+    if not args.no_prefill:
+        result["prefill"] = prefill_timing(dev, flush, stream, with_cpu=not args.no_cpu_baseline)
     print(json.dumps(result), flush=True)
     return 0
 
