@@ -597,8 +597,8 @@ int32_t paged_attn_prefill(const void* q, const void* k_pool, const void* v_pool
   if (((uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool | (uintptr_t)out) & 15u) return PA_ERR_ALIGN;
   if (!device_info().ok) return PA_ERR_DEVICE;
   const int G = d->num_q_heads / d->num_kv_heads;
-  const int R = kSub / G;
-  const int64_t tiles = (max_q_len + R - 1) / R;
+  const int rows_per_wave = kSub / G * kPrefillTiles;
+  const int64_t tiles = (max_q_len + rows_per_wave - 1) / rows_per_wave;
   const int64_t items = tiles * d->num_kv_heads;
   if (items >= ((int64_t)1 << 31) - kAuxWaves) return PA_ERR_UNSUPPORTED;
   PrefillArgs a;
