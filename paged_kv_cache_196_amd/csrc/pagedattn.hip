@@ -599,7 +599,7 @@ int32_t paged_attn_prefill(const void* q, const void* k_pool, const void* v_pool
   const int G = d->num_q_heads / d->num_kv_heads;
   const int rows_per_wave = kSub / G * kPrefillTiles;
   const int64_t tiles = (max_q_len + rows_per_wave - 1) / rows_per_wave;
-  const int64_t items = tiles * d->num_kv_heads;
+  const int64_t items = tiles * d->num_kv_heads * d->num_seqs;
   if (items >= ((int64_t)1 << 31) - kAuxWaves) return PA_ERR_UNSUPPORTED;
   PrefillArgs a;
   a.q = q;
@@ -616,7 +616,7 @@ int32_t paged_attn_prefill(const void* q, const void* k_pool, const void* v_pool
   a.mbs = d->max_blocks_per_seq;
   a.tiles = (int32_t)tiles;
   a.out_f32 = d->out_dtype == PA_F32 ? 1 : 0;
-  const dim3 grid((unsigned)((items + kAuxWaves - 1) / kAuxWaves), (unsigned)d->num_seqs);
+  const dim3 grid((unsigned)((items + kAuxWaves - 1) / kAuxWaves));
   launch(a, grid, static_cast<hipStream_t>(stream));
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }

@@ -25,7 +25,7 @@
 // (operand layouts and the hi + lo split of P as in the decode engine), with
 // a running max and sum per column.  The waves of one (b, KV head) read the
 // same K/V tiles, through L2 (cached load policy).  Waves with later rows
-// (longer) are issued first.
+// (longer) are issued first, across the whole batch.
 #pragma once
 
 #include "decode_mfma.h"
@@ -47,8 +47,10 @@ struct PrefillArgs {
 
 constexpr int kPrefillTiles = 3;  // 16-column tiles per wave: they share every K/V load (3: two waves per SIMD)
 
-// Grid: (ceil(tiles * Hkv / kAuxWaves), S) workgroups of kAuxThreads; `tiles`
-// counts groups of kPrefillTiles column tiles.
+// Grid: ceil(tiles * S * Hkv / kAuxWaves) workgroups of kAuxThreads; `tiles`
+// counts groups of kPrefillTiles column tiles.  Items run (column group,
+// sequence, KV head) with the column group slowest and reversed, so the
+// longest rows of the whole batch are issued first and the shortest last.
 template <class T, int B, int G>
 __global__ __launch_bounds__(kAuxThreads) void prefill_kernel(PrefillArgs a) {
   using M = MfmaEngine<T, B, G>;
@@ -58,10 +60,10 @@ __global__ __launch_bounds__(kAuxThreads) void prefill_kernel(PrefillArgs a) {
   constexpr int R = kSub / G;  // query rows per column tile
   constexpr int kTileBytes = B * kD * 2;
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
-  const int b = blockIdx.y;
   const int item = uniform(blockIdx.x * kAuxWaves + (threadIdx.x >> 6));
-  if (item >= a.tiles * a.Hkv) return;
-  const int ct0 = (a.tiles - 1 - item / a.Hkv) * NT;  // first column tile; longest rows first
+  if (item >= a.tiles * a.S * a.Hkv) return;
+  const int ct0 = (a.tiles - 1 - item / (a.S * a.Hkv)) * NT;  // longest rows of the whole batch first
+  const int b = (item / a.Hkv) % a.S;
   const int kvh = item % a.Hkv;
   const int q0 = as_constant(a.qs)[b];
   const int n = as_constant(a.qs)[b + 1] - q0;
