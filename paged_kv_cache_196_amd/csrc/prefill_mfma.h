@@ -142,14 +142,17 @@ __global__ __launch_bounds__(kAuxThreads) void prefill_kernel(PrefillArgs a) {
       // Token 0 is in sub-tile 0 and every column attends it, so m is
       // finite from the first sub-tile on.
       const float mn = fmaxf(m[t], bm);
-      const float alpha = fast_exp2(m[t] - mn);
-      lsum[t] *= alpha;
+      if (wave_any(mn > m[t])) {
+        // some column's max grew: rescale (alpha = 1 where it did not)
+        const float alpha = fast_exp2(m[t] - mn);
+        lsum[t] *= alpha;
 #pragma unroll
-      for (int x = 0; x < 8; ++x) acc[t][x] *= alpha;
-      m[t] = mn;
+        for (int x = 0; x < 8; ++x) acc[t][x] *= alpha;
+        m[t] = mn;
+      }
       float p[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(xr[r] - mn);
+      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(xr[r] - m[t]);
       lsum[t] += (p[0] + p[1]) + (p[2] + p[3]);
       Op4 phi, plo;
 #pragma unroll
