@@ -1,19 +1,27 @@
-"""Compile the gfx950 library in-tree: csrc/pagedattn.hip -> libpagedattn.so.
+"""Compile the gfx950 library in-tree: csrc/*.hip -> libpagedattn.so.
+
+Every translation unit (the C ABI, the decode kernels per element type and
+engine, the prefill kernels per element type, the cache-write and scan
+kernels) is compiled to an object in parallel, then linked.
 
     python -m paged_kv_cache_196_amd.build
 """
 from __future__ import annotations
 
+import glob
 import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "pagedattn.hip")
+CSRC = os.path.join(PKG, "csrc")
+SOURCES = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpagedattn.so")
+OBJ_DIR = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 
 
@@ -22,30 +30,55 @@ def hipcc() -> str:
     return path
 
 
-def command(out: str = LIB, extra=()) -> list:
-    return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # packed fp32 VALU forms are kept out of the generated code
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # MFMA accumulators in ordinary VGPRs: the online softmax rescales
-        # them every sub-tile, which would otherwise shuttle them out of AGPRs
-        "-mllvm", "-amdgpu-mfma-vgpr-form",
-        "-I", INCLUDE, "-I", os.path.join(PKG, "csrc"),
-        *extra, SRC, "-o", out,
-    ]
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # packed fp32 VALU forms are kept out of the generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the online softmax rescales
+    # them every sub-tile, which would otherwise shuttle them out of AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
+    "-I", INCLUDE, "-I", CSRC,
+]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def compile_command(src: str, obj: str, extra=()) -> list:
+    return [hipcc(), *FLAGS, *extra, "-c", src, "-o", obj]
+
+
+def link_command(objs, out: str) -> list:
+    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out]
+
+
+def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = [ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln]
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
-    if verbose and errs:
-        print("\n".join(errs), file=sys.stderr)
+    return r.returncode, errs
+
+
+def build(verbose: bool = False, extra=(), jobs: int | None = None) -> str:
+    """Compile every source and link the library; return its path.
+    extra: additional hipcc flags for the compile steps (e.g. remarks)."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    objs = [os.path.join(OBJ_DIR, os.path.basename(s)[:-4] + ".o") for s in SOURCES]
+    cmds = [compile_command(s, o, extra) for s, o in zip(SOURCES, objs)]
+    if verbose:
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    jobs = jobs or min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(_run, cmds))
+    failed = [(c, e) for c, (rc, e) in zip(cmds, results) if rc != 0]
+    if failed:
+        raise RuntimeError("hipcc failed:\n" + "\n\n".join(
+            " ".join(c) + "\n" + "\n".join(e) for c, e in failed))
+    if verbose:
+        for c, (_, e) in zip(cmds, results):
+            if e:
+                print("\n".join(e), file=sys.stderr)
+    tmp = LIB + f".tmp{os.getpid()}"
+    rc, errs = _run(link_command(objs, tmp))
+    if rc != 0:
+        raise RuntimeError("link failed:\n" + "\n".join(errs))
     os.replace(tmp, LIB)
     return LIB
 

@@ -28,19 +28,11 @@
 // (lowest score, then lowest block index).
 #pragma once
 
+#include "kernel_args.h"
 #include "pa_device.h"
 
 namespace pa {
 
-struct ScoreArgs {
-  const void* kp;
-  const void* vp;
-  const int32_t* bt;
-  const int32_t* lens;
-  float* scores;   // [S][mbs]
-  int32_t* evict;  // [S]
-  int32_t S, Hkv, mbs;
-};
 
 // Sum of squares of the elements of one 16-byte chunk.
 template <class T>

@@ -23,19 +23,11 @@
 // loads in flight per workgroup before their stores.
 #pragma once
 
+#include "kernel_args.h"
 #include "pa_device.h"
 
 namespace pa {
 
-struct AppendArgs {
-  const void* kn;  // [S][Hkv][kD] new keys
-  const void* vn;  // [S][Hkv][kD] new values
-  void* kp;
-  void* vp;
-  const int32_t* bt;
-  const int32_t* pos;  // [S] logical slot of the new token (< 0: none)
-  int32_t S, Hkv, B, mbs;
-};
 
 template <int kEsize>
 struct Bits;
@@ -79,18 +71,6 @@ __global__ __launch_bounds__(kAuxThreads) void append_kernel(AppendArgs a) {
   vt[(2 * lane + 1) * kSub] = hi;
 }
 
-struct CopyArgs {
-  char* kp;
-  char* vp;
-  const int32_t* src;
-  const int32_t* dst;
-  int64_t block_bytes;  // one block of one pool
-  int32_t chunks;       // 4 KiB chunks per block of one pool
-  int32_t total;        // num_pairs * 2 pools * chunks
-};
-
-constexpr int kChunkBytes = 4096;
-constexpr int kCopyUnroll = 4;  // chunks per workgroup pass
 
 // Work item w = ((pair * 2) + pool) * chunks + c.  Grid-stride over passes
 // of kCopyUnroll consecutive items; item indices are wave-uniform, so the

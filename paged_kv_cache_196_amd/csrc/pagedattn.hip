@@ -1,13 +1,14 @@
-// pagedattn.hip — gfx950 paged decode attention: kernels instantiation and
-// the C ABI declared in include/pagedattn.h.
+// pagedattn.hip — the C ABI declared in include/pagedattn.h: descriptor
+// checks, dispatch to the kernel variants (compiled in their own
+// translation units, see dispatch.h) and the host block manager.
 //
-// One call is one kernel launch on the caller's stream: the decode kernel
-// (matrix-core or vector-ALU engine) with a grid of one resident wave of
-// workgroups.  Each workgroup rebuilds the block-count prefix in LDS, walks
-// its equal share of the flattened (sequence, KV head, logical block) units
-// and writes `out` for every (sequence, KV head) it holds whole; the pieces
-// of a (sequence, KV head) split across workgroups meet in the workspace,
-// where the last one to finish folds them.
+// One decode call is one kernel launch on the caller's stream: the decode
+// kernel (matrix-core or vector-ALU engine) with a grid of one resident
+// wave of workgroups.  Each workgroup rebuilds the block-count prefix in
+// LDS, walks its equal share of the flattened (sequence, KV head, logical
+// block) units and writes `out` for every (sequence, KV head) it holds
+// whole; the pieces of a (sequence, KV head) split across workgroups meet
+// in the workspace, where the last one to finish folds them.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -16,77 +17,12 @@
 #include <unordered_set>
 
 #include "pagedattn.h"
-#include "pa_device.h"
-#include "decode_mfma.h"
-#include "decode_valu.h"
-#include "kv_write.h"
-#include "evict_scan.h"
-#include "prefill_mfma.h"
 #include "block_manager.h"
+#include "dispatch.h"
+#include "kernel_args.h"
+#include "pa_device.h"
 
 namespace pa {
-
-template <class T, int B, int G, bool kMfma>
-__global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
-  if constexpr (kMfma)
-    run_decode<T, B, G, MfmaEngine<T, B, G>>(a);
-  else
-    run_decode<T, B, G, ValuEngine<T, B, G>>(a);
-}
-
-// ------------------------------------------------------------ dispatch
-
-using LaunchFn = hipError_t (*)(const Args&, int grid, size_t lds, hipStream_t);
-using OccFn = int (*)(size_t lds);
-
-template <class T, int B, int G, bool M>
-hipError_t launch_decode(const Args& a, int grid, size_t lds, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<T, B, G, M>), dim3(grid), dim3(kThreads), lds, st, a);
-  return hipGetLastError();
-}
-
-template <class T, int B, int G, bool M>
-int occupancy(size_t lds) {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<T, B, G, M>, kThreads, lds) !=
-      hipSuccess)
-    return 0;
-  return n;
-}
-
-struct Variant {
-  LaunchFn launch = nullptr;
-  OccFn occ = nullptr;
-};
-
-template <class T, int B, int G, bool M>
-Variant make_variant() {
-  Variant v;
-  v.launch = &launch_decode<T, B, G, M>;
-  v.occ = &occupancy<T, B, G, M>;
-  return v;
-}
-
-template <class T, int B, bool M>
-Variant pick_group(int G) {
-  switch (G) {
-    case 1: return make_variant<T, B, 1, M>();
-    case 2: return make_variant<T, B, 2, M>();
-    case 4: return make_variant<T, B, 4, M>();
-    case 8: return make_variant<T, B, 8, M>();
-    case 16:
-      if constexpr (M) return make_variant<T, B, 16, M>();
-      return Variant{};
-    default: return Variant{};
-  }
-}
-
-template <class T, bool M>
-Variant pick_block(int B, int G) {
-  if (B == 16) return pick_group<T, 16, M>(G);
-  if (B == 32) return pick_group<T, 32, M>(G);
-  return Variant{};
-}
 
 inline bool use_mfma(const pa_desc* d) {
   if (d->kernel == PA_KERNEL_MFMA) return true;
@@ -96,11 +32,12 @@ inline bool use_mfma(const pa_desc* d) {
 
 Variant pick(const pa_desc* d) {
   const int G = d->num_q_heads / d->num_kv_heads;
+  const int B = d->block_size;
   const bool mf = use_mfma(d);
   switch (d->dtype) {
-    case PA_F32: return mf ? Variant{} : pick_block<F32, false>(d->block_size, G);
-    case PA_F16: return mf ? pick_block<F16, true>(d->block_size, G) : pick_block<F16, false>(d->block_size, G);
-    case PA_BF16: return mf ? pick_block<BF16, true>(d->block_size, G) : pick_block<BF16, false>(d->block_size, G);
+    case PA_F32: return mf ? Variant{} : decode_variant_f32_valu(B, G);
+    case PA_F16: return mf ? decode_variant_f16_mfma(B, G) : decode_variant_f16_valu(B, G);
+    case PA_BF16: return mf ? decode_variant_bf16_mfma(B, G) : decode_variant_bf16_valu(B, G);
     default: return Variant{};
   }
 }
@@ -135,51 +72,29 @@ DeviceInfo device_info() {
 // and a copy of the lengths (S ints).
 size_t prefix_lds(int S) { return (size_t)(2 * S + 1) * sizeof(int); }
 
-// Workspace: [kMaxGrid] int32 split counters, then the partials
-// ws_o [2*kMaxGrid][G][kD] and ws_ml [2*kMaxGrid][G][2] (fp32).
-constexpr size_t kCounterBytes = sizeof(int) * kMaxGrid;
 
-size_t ws_bytes_for(const pa_desc* d) {
-  const int64_t G = d->num_q_heads / d->num_kv_heads;
-  return kCounterBytes + sizeof(float) * (size_t)(2 * kMaxGrid) * G * (kD + 2);
+// Workspace layout for `slots` partial slots (two per workgroup) and
+// `counters` split counters: counters first (padded to 256 bytes), then
+// the weighted-V partials [slots][G][kD] and the (max, sum) pairs
+// [slots][G][2], all fp32.
+size_t ws_layout_bytes(int counters, int slots, int G) {
+  const size_t cnt = ((size_t)counters * sizeof(int) + 255) & ~(size_t)255;
+  return cnt + sizeof(float) * (size_t)slots * G * (kD + 2);
 }
 
-template <class T>
-hipError_t launch_scores(const ScoreArgs& a, int B, hipStream_t s) {
-  const dim3 grid((unsigned)((a.mbs + kAuxWaves - 1) / kAuxWaves), (unsigned)a.S);
-  if (B == 16)
-    hipLaunchKernelGGL((block_score_kernel<T, 16>), grid, dim3(kAuxThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((block_score_kernel<T, 32>), grid, dim3(kAuxThreads), 0, s, a);
-  return hipGetLastError();
-}
-
-using PrefillFn = void (*)(const PrefillArgs&, dim3, hipStream_t);
-
-template <class T, int B, int G>
-void launch_prefill(const PrefillArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_kernel<T, B, G>), grid, dim3(kAuxThreads), 0, s, a);
-}
-
-template <class T, int B>
-PrefillFn prefill_for_group(int G) {
-  switch (G) {
-    case 1: return launch_prefill<T, B, 1>;
-    case 2: return launch_prefill<T, B, 2>;
-    case 4: return launch_prefill<T, B, 4>;
-    case 8: return launch_prefill<T, B, 8>;
-    case 16: return launch_prefill<T, B, 16>;
-    default: return nullptr;
-  }
+void bind_workspace(Args* a, void* ws, int counters, int slots, int G) {
+  const size_t cnt = ((size_t)counters * sizeof(int) + 255) & ~(size_t)255;
+  a->counters = static_cast<int*>(ws);
+  a->ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + cnt);
+  a->ws_ml = a->ws_o + (size_t)slots * G * kD;
 }
 
 // Prefill variant of a descriptor: matrix cores only (fp16 / bf16).
 PrefillFn pick_prefill(const pa_desc* d) {
   if (d->kernel == PA_KERNEL_VALU || d->dtype == PA_F32) return nullptr;
   const int G = d->num_q_heads / d->num_kv_heads;
-  const bool bf = d->dtype == PA_BF16;
-  if (d->block_size == 16) return bf ? prefill_for_group<BF16, 16>(G) : prefill_for_group<F16, 16>(G);
-  return bf ? prefill_for_group<BF16, 32>(G) : prefill_for_group<F16, 32>(G);
+  return d->dtype == PA_BF16 ? prefill_variant_bf16(d->block_size, G)
+                             : prefill_variant_f16(d->block_size, G);
 }
 
 }  // namespace pa
@@ -265,7 +180,7 @@ int64_t pa_v_elem_offset(const pa_desc* d, int32_t block, int32_t kv_head, int32
 
 size_t pa_workspace_bytes(const pa_desc* d) {
   if (pa_check_desc(d) != PA_OK) return 0;
-  return ws_bytes_for(d);
+  return ws_layout_bytes(kMaxGrid, 2 * kMaxGrid, d->num_q_heads / d->num_kv_heads);
 }
 
 int32_t pa_validate_host(const pa_desc* d, const int32_t* bt, const int32_t* lens) {
@@ -296,31 +211,30 @@ int32_t pa_decode_grid(const pa_desc* d) {
   return grid;
 }
 
+// Checks the call (a caller workspace too when check_ws) and fills every
+// field of the kernel arguments except the workspace pointers
+// (bind_workspace).  Argument errors come before any device query.
+// *grid = 0: nothing to launch.
 static int32_t prepare(const void* q, const void* k_pool, const void* v_pool, const int32_t* bt,
                        const int32_t* lens, float scale, void* out, const pa_desc* d,
-                       void* ws, size_t ws_bytes, Args* a, int* grid) {
+                       bool check_ws, const void* ws, size_t ws_bytes, Args* a, int* grid) {
   const int32_t st = pa_check_desc(d);
   if (st != PA_OK) return st;
-  if (d->num_seqs == 0) {
-    *grid = 0;
-    return PA_OK;
-  }
+  *grid = 0;
+  if (d->num_seqs == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !bt || !lens || !out) return PA_ERR_NULL;
   if (((uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool | (uintptr_t)out) & 15u) return PA_ERR_ALIGN;
-  if (!ws || ws_bytes < pa_workspace_bytes(d) || ((uintptr_t)ws & 15u)) return PA_ERR_WORKSPACE;
+  if (check_ws && (!ws || ws_bytes < pa_workspace_bytes(d) || ((uintptr_t)ws & 15u)))
+    return PA_ERR_WORKSPACE;
   if (!device_info().ok) return PA_ERR_DEVICE;
   const int g = pa_decode_grid(d);
   if (g <= 0) return PA_ERR_UNSUPPORTED;  // LDS of this batch size and group does not fit
-  const int G = d->num_q_heads / d->num_kv_heads;
   a->q = q;
   a->kp = k_pool;
   a->vp = v_pool;
   a->bt = bt;
   a->lens = lens;
   a->out = out;
-  a->counters = static_cast<int*>(ws);
-  a->ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
-  a->ws_ml = a->ws_o + (size_t)(2 * kMaxGrid) * G * kD;
   a->scale_log2 = scale * kLog2e;
   a->S = d->num_seqs;
   a->Hq = d->num_q_heads;
@@ -338,8 +252,10 @@ int32_t paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
                           const pa_desc* d, void* ws, size_t ws_bytes, void* stream) {
   Args a;
   int grid = 0;
-  const int32_t st = prepare(q, k_pool, v_pool, bt, lens, scale, out, d, ws, ws_bytes, &a, &grid);
+  const int32_t st = prepare(q, k_pool, v_pool, bt, lens, scale, out, d, true, ws, ws_bytes, &a,
+                             &grid);
   if (st != PA_OK || grid == 0) return st;
+  bind_workspace(&a, ws, kMaxGrid, 2 * kMaxGrid, d->num_q_heads / d->num_kv_heads);
   const Variant v = pick(d);
   if (v.launch(a, grid, prefix_lds(a.S), static_cast<hipStream_t>(stream)) != hipSuccess)
     return PA_ERR_LAUNCH;
@@ -385,11 +301,8 @@ int32_t paged_kv_append(const void* k_new, const void* v_new, void* k_pool, void
   a.mbs = d->max_blocks_per_seq;
   const int grid = (int)(((int64_t)a.S * a.Hkv + kAuxWaves - 1) / kAuxWaves);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (pa_dtype_size(d->dtype) == 4)
-    hipLaunchKernelGGL(append_kernel<4>, dim3(grid), dim3(kAuxThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(append_kernel<2>, dim3(grid), dim3(kAuxThreads), 0, s, a);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+  return launch_append(a, (int)pa_dtype_size(d->dtype), grid, s) == hipSuccess ? PA_OK
+                                                                              : PA_ERR_LAUNCH;
 }
 
 int32_t pa_validate_copy_host(const pa_desc* d, const int32_t* src, const int32_t* dst,
@@ -433,9 +346,9 @@ int32_t paged_kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, con
   int64_t grid = (total + kCopyUnroll - 1) / kCopyUnroll;
   const int64_t cap = (int64_t)info.cus * 8;
   if (grid > cap) grid = cap;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)grid), dim3(kAuxThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+  return launch_copy_blocks(a, (int)grid, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PA_OK
+             : PA_ERR_LAUNCH;
 }
 
 int32_t paged_kv_block_scores(const void* k_pool, const void* v_pool, const int32_t* bt,
@@ -458,17 +371,10 @@ int32_t paged_kv_block_scores(const void* k_pool, const void* v_pool, const int3
   a.S = d->num_seqs;
   a.Hkv = d->num_kv_heads;
   a.mbs = d->max_blocks_per_seq;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  switch (d->dtype) {
-    case PA_F32: e = launch_scores<F32>(a, d->block_size, s); break;
-    case PA_F16: e = launch_scores<F16>(a, d->block_size, s); break;
-    default: e = launch_scores<BF16>(a, d->block_size, s); break;
-  }
-  if (e != hipSuccess) return PA_ERR_LAUNCH;
-  hipLaunchKernelGGL(evict_choice_kernel, dim3((unsigned)((a.S + kAuxWaves - 1) / kAuxWaves)),
-                     dim3(kAuxThreads), 0, s, a, (int)d->block_size);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+  return launch_block_scores(a, d->dtype, d->block_size, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? PA_OK
+             : PA_ERR_LAUNCH;
 }
 
 struct pa_block_manager {

@@ -29,23 +29,11 @@
 #pragma once
 
 #include "decode_mfma.h"
+#include "kernel_args.h"
 #include "pa_device.h"
 
 namespace pa {
 
-struct PrefillArgs {
-  const void* q;       // [total_q][Hq][kD]
-  const void* kp;
-  const void* vp;
-  const int32_t* bt;   // [S][mbs]
-  const int32_t* lens; // [S]
-  const int32_t* qs;   // [S + 1] row offsets
-  void* out;           // [total_q][Hq][kD]
-  float scale_log2;
-  int32_t S, Hq, Hkv, mbs, tiles, out_f32;  // tiles: column tiles per (sequence, KV head)
-};
-
-constexpr int kPrefillTiles = 3;  // 16-column tiles per wave: they share every K/V load (3: two waves per SIMD)
 
 // Grid: ceil(tiles * S * Hkv / kAuxWaves) workgroups of kAuxThreads; `tiles`
 // counts groups of kPrefillTiles column tiles.  Items run (column group,
