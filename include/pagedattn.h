@@ -49,7 +49,9 @@
  *
  * Ownership and threading.  The caller allocates every buffer (including
  * the workspace) and owns the stream.  The library allocates nothing, keeps
- * no pointer after a call returns and holds no state between calls.  Calls
+ * no pointer after a call returns and holds no state between calls, except
+ * the static scratch of paged_attn_decode_noalloc (one array per GPU,
+ * allocated with the library's code object).  Calls
  * are asynchronous on `stream` (a hipStream_t; NULL = the null stream).
  * Calls that share a workspace must be ordered on one stream.  `out` must
  * not alias any input.
@@ -84,7 +86,8 @@ typedef enum pa_status {
   PA_ERR_LAUNCH = 7,      /* the HIP launch reported an error */
   PA_ERR_TABLE = 8,       /* pa_validate_host: table id out of range or bad seq_len */
   PA_ERR_DEVICE = 9,      /* device query failed or the device is not gfx950 */
-  PA_ERR_NOMEM = 10       /* block manager: not enough free physical blocks */
+  PA_ERR_NOMEM = 10,      /* block manager: not enough free physical blocks */
+  PA_ERR_SCRATCH = 11     /* paged_attn_decode_noalloc: the call needs more than its static scratch */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -182,6 +185,31 @@ int32_t paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
                           const int32_t* block_tables, const int32_t* seq_lens,
                           float scale, void* out, const pa_desc* desc,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* paged_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid allocation, harnesses without an allocator).  It allocates
+ * nothing: the split counters and partials live in a static 8 MiB device
+ * array inside the library, one per GPU, held until the process ends.  The
+ * caller still provides q, the pools, the tables, the lengths and out, in
+ * the layouts above; results are those of paged_attn_decode (same kernels,
+ * same fold order).
+ *
+ * Two launches on `stream`: a small kernel that zeroes the split counters,
+ * then the decode kernel.  Every call on one GPU shares that GPU's array,
+ * which keeps the last call's contents: calls that overlap on one GPU (on
+ * different streams, or from different host threads without ordering)
+ * race and may produce wrong results; order them on one stream.
+ *
+ * The call needs 4 * grid bytes of counters (rounded up to 256) plus
+ * 2 * grid * G * (head_dim + 2) * 4 bytes of partials, grid =
+ * pa_decode_grid(desc), G = num_q_heads / num_kv_heads: 1.06 MB at G = 4
+ * and 4.26 MB at G = 16 on a 256-CU gfx950.  A call that needs more than
+ * 8 MiB returns PA_ERR_SCRATCH and launches nothing.  Other errors as for
+ * paged_attn_decode (no PA_ERR_WORKSPACE). */
+int32_t paged_attn_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_tables, const int32_t* seq_lens,
+                                  float scale, void* out, const pa_desc* desc, void* stream);
 
 /* Number of decode workgroups a launch uses for this descriptor on the
  * current device (the split-K granularity: CUs x resident workgroups per

@@ -32,6 +32,7 @@ from ._lib import (  # noqa: F401
     pa_validate_prefill_host,
     pa_workspace_bytes,
     paged_attn_decode,
+    paged_attn_decode_noalloc,
     paged_attn_prefill,
     paged_kv_append,
     paged_kv_block_scores,

@@ -14,7 +14,7 @@ PA_OK = 0
 STATUS = {
     0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_DTYPE", 4: "PA_ERR_UNSUPPORTED",
     5: "PA_ERR_WORKSPACE", 6: "PA_ERR_ALIGN", 7: "PA_ERR_LAUNCH", 8: "PA_ERR_TABLE",
-    9: "PA_ERR_DEVICE", 10: "PA_ERR_NOMEM",
+    9: "PA_ERR_DEVICE", 10: "PA_ERR_NOMEM", 11: "PA_ERR_SCRATCH",
 }
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 PA_KERNEL_AUTO, PA_KERNEL_VALU, PA_KERNEL_MFMA = 0, 1, 2
@@ -27,6 +27,7 @@ EXPORTS = (
     "paged_kv_copy_blocks", "pa_validate_copy_host", "paged_kv_block_scores", "pa_bm_create",
     "pa_bm_destroy", "pa_bm_num_free", "pa_bm_refcount", "pa_bm_alloc", "pa_bm_release",
     "pa_bm_share", "pa_bm_prepare_append", "paged_attn_prefill", "pa_validate_prefill_host",
+    "paged_attn_decode_noalloc",
 )
 
 
@@ -80,6 +81,8 @@ def load() -> ctypes.CDLL:
             lib.paged_attn_decode.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, _P, _DP, _P,
                                               ctypes.c_size_t, _P]
             lib.paged_attn_decode.restype = ctypes.c_int32
+            lib.paged_attn_decode_noalloc.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, _P, _DP, _P]
+            lib.paged_attn_decode_noalloc.restype = ctypes.c_int32
             lib.pa_decode_grid.argtypes = [_DP]
             lib.pa_decode_grid.restype = ctypes.c_int32
             lib.paged_kv_append.argtypes = [_P, _P, _P, _P, _P, _P, _DP, _P]
@@ -192,6 +195,14 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, o
                                   _ptr(seq_lens), float(scale), _ptr(out), ctypes.byref(desc),
                                   _ptr(workspace), int(workspace_bytes), _ptr(stream))
     return _check(rc, "paged_attn_decode")
+
+
+def paged_attn_decode_noalloc(q, k_pool, v_pool, block_tables, seq_lens, scale: float, out,
+                              desc: PaDesc, stream=None) -> int:
+    rc = load().paged_attn_decode_noalloc(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                                          _ptr(seq_lens), float(scale), _ptr(out),
+                                          ctypes.byref(desc), _ptr(stream))
+    return _check(rc, "paged_attn_decode_noalloc")
 
 
 def paged_attn_prefill(q, k_pool, v_pool, block_tables, seq_lens, q_start, max_q_len: int,

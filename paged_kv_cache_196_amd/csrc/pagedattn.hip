@@ -72,6 +72,35 @@ DeviceInfo device_info() {
 // and a copy of the lengths (S ints).
 size_t prefix_lds(int S) { return (size_t)(2 * S + 1) * sizeof(int); }
 
+// ------------------------------------------- allocation-free decode scratch
+//
+// paged_attn_decode_noalloc keeps its workspace (split counters and
+// partials) in this file-scope device array instead of a caller buffer:
+// one copy per GPU, alive until the process ends.  Host code never passes
+// the array's name to a kernel (on the host it is only a stand-in for the
+// symbol); it uses the device address hipGetSymbolAddress returns, looked
+// up once per device with that device current.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of this device's scratch, nullptr if the lookup failed.
+void* scratch_ptr() {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+__global__ void clear_ints_kernel(int* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
 
 // Workspace layout for `slots` partial slots (two per workgroup) and
 // `counters` split counters: counters first (padded to 256 bytes), then
@@ -116,6 +145,9 @@ const char* pa_status_str(int32_t s) {
     case PA_ERR_TABLE: return "PA_ERR_TABLE: block table entry or sequence length out of range";
     case PA_ERR_DEVICE: return "PA_ERR_DEVICE: no gfx950 device current";
     case PA_ERR_NOMEM: return "PA_ERR_NOMEM: not enough free physical blocks";
+    case PA_ERR_SCRATCH:
+      return "PA_ERR_SCRATCH: the call needs more than the 8 MiB static scratch of "
+             "paged_attn_decode_noalloc";
     default: return "unknown pa_status";
   }
 }
@@ -259,6 +291,29 @@ int32_t paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
   const Variant v = pick(d);
   if (v.launch(a, grid, prefix_lds(a.S), static_cast<hipStream_t>(stream)) != hipSuccess)
     return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+int32_t paged_attn_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* bt, const int32_t* lens, float scale, void* out,
+                                  const pa_desc* d, void* stream) {
+  Args a;
+  int grid = 0;
+  const int32_t st = prepare(q, k_pool, v_pool, bt, lens, scale, out, d, false, nullptr, 0, &a,
+                             &grid);
+  if (st != PA_OK || grid == 0) return st;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (ws_layout_bytes(grid, 2 * grid, G) > kScratchBytes) return PA_ERR_SCRATCH;
+  void* ws = scratch_ptr();
+  if (!ws) return PA_ERR_DEVICE;
+  bind_workspace(&a, ws, grid, 2 * grid, G);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // the split counters must start at zero: a fill kernel (no memset node,
+  // so the pair of launches can also be captured into a graph)
+  hipLaunchKernelGGL(clear_ints_kernel, dim3(1), dim3(256), 0, s, a.counters, grid);
+  if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
+  const Variant v = pick(d);
+  if (v.launch(a, grid, prefix_lds(a.S), s) != hipSuccess) return PA_ERR_LAUNCH;
   return PA_OK;
 }
 

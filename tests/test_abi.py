@@ -298,3 +298,24 @@ def test_prefill_argument_errors_before_any_launch(lib):
     import torch
     if not torch.cuda.is_available():
         assert lib.paged_attn_prefill(*args, byref(d), None) == 9
+
+
+def test_noalloc_argument_errors_before_any_launch(lib):
+    """The allocation-free decode checks its arguments like the workspace
+    entry point, and without a GPU reports PA_ERR_DEVICE after them."""
+    d = _desc()
+    P = 1 << 20
+    f = lib.paged_attn_decode_noalloc
+    assert f(None, P, P, P, P, 0.1, P, pa._lib.ctypes.byref(d), None) == 1
+    assert f(P, P, P, None, P, 0.1, P, pa._lib.ctypes.byref(d), None) == 1
+    assert f(P + 8, P, P, P, P, 0.1, P, pa._lib.ctypes.byref(d), None) == 6
+    assert f(P, P, P, P, P, 0.1, P + 2, pa._lib.ctypes.byref(d), None) == 6
+    bad = _desc()
+    bad.num_kv_heads = 3
+    assert f(P, P, P, P, P, 0.1, P, pa._lib.ctypes.byref(bad), None) == 2
+    empty = _desc()
+    empty.num_seqs = 0
+    assert f(None, None, None, None, None, 0.1, None, pa._lib.ctypes.byref(empty), None) == 0
+    import torch
+    if not torch.cuda.is_available():
+        assert f(P, P, P, P, P, 0.1, P, pa._lib.ctypes.byref(d), None) == 9
