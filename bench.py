@@ -13,9 +13,12 @@ inside the next timed kernel (measured: ~25% lower read bandwidth).
 
     python bench.py [--steps K] [--warmup W] [--workload N]
 
-prints one JSON line.  Default workload: GQA decode, batch 64, 32 query /
-8 KV heads, head_dim 128, bf16, 16-token blocks, L ~ U{512..8192},
-shuffled physical blocks (workload 3 of workload.py).
+prints one JSON line.  Default workload: large-batch serving decode, batch
+256, 32 query / 8 KV heads, head_dim 128, bf16, 16-token blocks, lognormal
+lengths (median 1000), groups of 8 sequences sharing a 512-token prefix
+(workload 5 of workload.py), through paged_attn_decode_shared; the GQA
+batch (workload 3) and the long-context batch (workload 4) follow as
+sub-entries with their own roofline.
 """
 from __future__ import annotations
 
@@ -63,19 +66,24 @@ def algorithmic_bytes(w, unique_kv: int) -> dict:
     return parts
 
 
-def read_traffic(src_hash: str, kernel_name: str, workload_name: str):
-    """HBM bytes per decode launch from the committed rocprofv3 counter runs,
-    or None when they were taken on other kernel sources or another
-    workload."""
+def _traffic_entries() -> list:
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
-    if t.get("source_hash") != src_hash or t.get("kernel") != kernel_name or \
-            t.get("workload") != workload_name:
-        return None
-    return t.get("hbm_bytes_per_launch")
+        return []
+    return t.get("entries", []) if isinstance(t, dict) else []
+
+
+def read_traffic(src_hash: str, kernel_name: str, workload_name: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter runs,
+    or None when none were taken on these kernel sources for this kernel
+    and workload."""
+    for t in _traffic_entries():
+        if t.get("source_hash") == src_hash and t.get("kernel") == kernel_name and \
+                t.get("workload") == workload_name:
+            return t.get("hbm_bytes_per_launch")
+    return None
 
 
 COPY_BYTES = 512 << 20  # calibration copy: reads and writes this many bytes per launch
@@ -115,17 +123,19 @@ def _mean_counter(rows, counter: str, name_part: str) -> float:
     return sum(vals) / len(vals)
 
 
-def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, workload_id, kernel):
+def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, workload_id, kernel,
+                       shared: bool):
     """Turns four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE, each on
     this benchmark and on the calibration copy) into HBM bytes per decode
-    launch, scaled by the copy's known bytes, and writes TRAFFIC_FILE."""
+    launch, scaled by the copy's known bytes, and stores the entry for this
+    (kernel, workload) in TRAFFIC_FILE."""
     import workload as wl
     w = wl.make(workload_id)
-    use_mfma = kernel == "mfma" or (kernel == "auto" and w.dtype != "f32")
-    kname = f"decode_kernel<{w.dtype},B{w.block_size},G{w.group},{'mfma' if use_mfma else 'valu'}>"
+    kname = decode_kernel_name(w, kernel, shared)
+    part = "decode_shared_kernel" if kname.startswith("decode_shared") else "decode_kernel"
     kib = 1024.0
-    dec_fetch = _mean_counter(_counter_rows(fetch_dir), "FETCH_SIZE", "decode_kernel") * kib
-    dec_write = _mean_counter(_counter_rows(write_dir), "WRITE_SIZE", "decode_kernel") * kib
+    dec_fetch = _mean_counter(_counter_rows(fetch_dir), "FETCH_SIZE", part) * kib
+    dec_write = _mean_counter(_counter_rows(write_dir), "WRITE_SIZE", part) * kib
     cp_fetch = _mean_counter(_counter_rows(copy_fetch_dir), "FETCH_SIZE", "Mul") * kib
     cp_write = _mean_counter(_counter_rows(copy_write_dir), "WRITE_SIZE", "Mul") * kib
     f_fetch = COPY_BYTES / cp_fetch
@@ -147,11 +157,23 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, wor
         "algorithmic_bytes_per_launch": alg["total"],
         "traffic_over_algorithmic": round(hbm / alg["total"], 4),
     }
+    entries = [e for e in _traffic_entries()
+               if not (e.get("kernel") == kname and e.get("workload") == w.name)]
+    entries.append(out)
     with open(TRAFFIC_FILE, "w") as f:
-        json.dump(out, f, indent=1)
+        json.dump({"entries": entries}, f, indent=1)
         f.write("\n")
     print(json.dumps(out), flush=True)
     return 0
+
+
+def decode_kernel_name(w, kernel: str, shared: bool) -> str:
+    """Name of the decode kernel a call on workload w runs (as reported in
+    the bench line and matched against counter runs)."""
+    use_mfma = kernel == "mfma" or (kernel == "auto" and w.dtype != "f32")
+    if shared and use_mfma and w.num_groups > 0 and w.group in (1, 2, 4, 8):
+        return f"decode_shared_kernel<{w.dtype},B{w.block_size},G{w.group}>"
+    return f"decode_kernel<{w.dtype},B{w.block_size},G{w.group},{'mfma' if use_mfma else 'valu'}>"
 
 
 PROBE_SRC = os.path.join(ROOT, "bench_read_probe.hip")
@@ -436,7 +458,7 @@ def prefill_timing(dev, flush, stream, with_cpu: bool) -> dict:
 
     import paged_kv_cache_196_amd as pa
     import workload
-    from tests.gpu_util import device_tensor
+    from workload import to_device as device_tensor
 
     w, q, qs = workload.prefill_workload()
     n = np.diff(qs).astype(np.int64)
@@ -450,7 +472,8 @@ def prefill_timing(dev, flush, stream, with_cpu: bool) -> dict:
     max_q = int(n.max())
     mean, med = _time_events(
         lambda: pa.prefill(*args, float(w.scale), max_q_len=max_q, out=out,
-                           out_dtype=torch.bfloat16, stream=stream), flush, stream, 10)
+                           out_dtype=torch.bfloat16, stream=stream, check_rows=False),
+        flush, stream, 10)
     tflops = flops / (mean * 1e-3) / 1e12
     res = {
         "workload": w.name, "kernel": "prefill_kernel", "query_rows": int(qs[-1]),
@@ -551,19 +574,130 @@ def block_manager_timing(w, with_cpu: bool, steps: int = 50) -> dict:
     return res
 
 
+def decode_leg(w, args, dev, flush, stream, O, shared: bool, steps: int, warmup: int) -> dict:
+    """Upload workload w, check every output against the oracle, then time
+    `steps` decode calls (after `warmup`) between HIP events on the launch
+    stream, the read-only flush before every call outside the events.  With
+    shared=True a workload with prefix groups goes through
+    paged_attn_decode_shared (every shared block read once per group)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_196_amd as pa
+    import workload
+
+    kv_logical = workload.kv_bytes(w)
+    kv_unique = workload.kv_bytes(w, unique=True)
+    alg = algorithmic_bytes(w, kv_unique)
+    q, kp, vp = (workload.to_device(x, w.dtype, dev) for x in (w.q, w.k_pool, w.v_pool))
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    lens = torch.from_numpy(w.seq_lens).to(dev)
+    kern = {"auto": pa.PA_KERNEL_AUTO, "valu": pa.PA_KERNEL_VALU, "mfma": pa.PA_KERNEL_MFMA}[args.kernel]
+    use_groups = shared and w.num_groups > 0
+    hint = 0 if (use_groups or args.no_prefix_hint) else w.shared_prefix_blocks
+    desc = pa.make_desc(q, kp, bt, out_dtype=torch.float32, kernel=kern, cached_prefix_blocks=hint)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    sh = stream.cuda_stream
+    scale = float(w.scale)
+    kname = decode_kernel_name(w, args.kernel, use_groups)
+    if use_groups:
+        gs = torch.from_numpy(w.group_start).to(dev)
+        gsh = torch.from_numpy(w.group_shared).to(dev)
+        ws = pa.new_shared_workspace(desc, dev)
+        grid = pa.pa_decode_shared_grid(desc, w.num_groups)
+
+        def call():
+            pa.paged_attn_decode_shared(q, kp, vp, bt, lens, gs, gsh, w.num_groups, scale, out,
+                                        desc, ws, ws.numel(), sh)
+    else:
+        ws = pa.new_workspace(desc, dev)
+        grid = pa.pa_decode_grid(desc)
+
+        def call():
+            pa.paged_attn_decode(q, kp, vp, bt, lens, scale, out, desc, ws, ws.numel(), sh)
+
+    max_err = None
+    if O is not None:
+        call()
+        torch.cuda.synchronize()
+        max_err = float(np.max(np.abs(out.double().cpu().numpy() - O.run_workload(w))))
+    for _ in range(warmup):
+        if not args.no_flush:
+            flush()
+        call()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if not args.no_flush:
+            flush()
+        evs[i][0].record(stream)
+        call()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tot_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    t_step = statistics.mean(tot_ms)
+    kv_gbps = kv_unique / (t_step * 1e-3) / 1e9
+    achieved = alg["total"] / (t_step * 1e-3) / 1e9  # one kernel per call
+    src_hash = kernel_source_hash()
+    traffic = read_traffic(src_hash, kname, w.name)
+    return {
+        "workload": w.name,
+        "config": {
+            "workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+            "seq_len_mean": round(float(w.seq_lens.mean()), 1),
+            "seq_len_min": int(w.seq_lens.min()), "seq_len_max": int(w.seq_lens.max()),
+            "num_blocks": w.num_blocks, "shared_prefix_blocks": w.shared_prefix_blocks,
+            "prefix_groups": w.num_groups if use_groups else 0,
+            "cached_prefix_blocks": hint, "seed": w.seed, "kernel": args.kernel,
+            "entry_point": "paged_attn_decode_shared" if use_groups else "paged_attn_decode",
+            "decode_grid": grid, "parallelism": "single GPU",
+        },
+        "dtype": w.dtype,
+        "ms_per_step": round(t_step, 5),
+        "kv_gbps": round(kv_gbps, 2),
+        "hbm_frac": round(kv_gbps / HBM_PEAK_GBPS, 4),
+        "tokens_per_s": round(w.num_seqs / (t_step * 1e-3), 1),
+        "kv_bytes": kv_unique,
+        "kv_bytes_logical": kv_logical,
+        "kv_gbps_logical": round(kv_logical / (t_step * 1e-3) / 1e9, 2),
+        "ms": {
+            "step_mean": round(t_step, 5), "step_median": round(statistics.median(tot_ms), 5),
+            "step_p10": round(sorted(tot_ms)[len(tot_ms) // 10], 5),
+            "step_p90": round(sorted(tot_ms)[(9 * len(tot_ms)) // 10], 5),
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": kname, "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic, "algorithmic_bytes": alg["total"],
+        },
+        "wall_s_timed_loop": round(wall, 4),
+        "max_abs_err_vs_oracle": max_err,
+        "kernel_source_hash": src_hash,
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--kernel", choices=["auto", "valu", "mfma"], default="auto")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--no-prefix-groups", action="store_true",
+                    help="run a workload with prefix groups through paged_attn_decode (every "
+                         "shared block read once per sequence) instead of paged_attn_decode_shared")
     ap.add_argument("--no-prefix-hint", action="store_true",
-                    help="do not pass the shared-prefix cache hint (cached_prefix_blocks)")
+                    help="with --no-prefix-groups: no shared-prefix cache hint either")
+    ap.add_argument("--other-workloads", default="3,4",
+                    help="comma-separated workloads timed after the headline one as sub-entries "
+                         "('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-check", action="store_true", help="skip the oracle spot check")
+    ap.add_argument("--no-check", action="store_true", help="skip the oracle check")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-read-probe", action="store_true")
     ap.add_argument("--no-cache-writes", action="store_true",
@@ -579,7 +713,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.summarize_counters:
-        return summarize_counters(*args.summarize_counters, args.workload, args.kernel)
+        return summarize_counters(*args.summarize_counters, args.workload, args.kernel,
+                                  shared=not args.no_prefix_groups)
     if args.copy_calibration:
         return copy_calibration()
 
@@ -589,7 +724,6 @@ def main() -> int:
               "(see the sharding notes); run with --gpus 1", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import paged_kv_cache_196_amd as pa
@@ -602,155 +736,96 @@ def main() -> int:
         return 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-
-    w = workload.make(args.workload, args.seed)
-    kv_logical = workload.kv_bytes(w)
-    kv_unique = workload.kv_bytes(w, unique=True)
-    alg = algorithmic_bytes(w, kv_unique)
-
-    def up(x):
-        if w.dtype == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
-
-    q, kp, vp = up(w.q), up(w.k_pool), up(w.v_pool)
-    bt = torch.from_numpy(w.block_tables).to(dev)
-    lens = torch.from_numpy(w.seq_lens).to(dev)
-    kern = {"auto": pa.PA_KERNEL_AUTO, "valu": pa.PA_KERNEL_VALU, "mfma": pa.PA_KERNEL_MFMA}[args.kernel]
-    hint = 0 if args.no_prefix_hint else w.shared_prefix_blocks
-    desc = pa.make_desc(q, kp, bt, out_dtype=torch.float32, kernel=kern, cached_prefix_blocks=hint)
-    ws_bytes = pa.pa_workspace_bytes(desc)
-    ws = pa.new_workspace(desc, dev)
-    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    grid = pa.pa_decode_grid(desc)
     stream = torch.cuda.current_stream(dev)
-    sh = stream.cuda_stream
-    scale = float(w.scale)
     flush_src = torch.zeros((1 << 30) // 4, dtype=torch.float32, device=dev)
 
     def flush():
         # read-only pass over 1 GiB: evicts L2 and MALL without dirtying them
         return flush_src.sum()
-    use_mfma = kern == pa.PA_KERNEL_MFMA or (kern == pa.PA_KERNEL_AUTO and w.dtype != "f32")
-    kname = f"decode_kernel<{w.dtype},B{w.block_size},G{w.group},{'mfma' if use_mfma else 'valu'}>"
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        pa.paged_attn_decode(q, kp, vp, bt, lens, scale, out, desc, ws, ws_bytes, sh)
-        if ev is not None:
-            ev[1].record(stream)
-
-    # spot check against the oracle (every output) before timing
-    max_err = None
     O = None
     if not args.no_check:
         import oracle
         O = oracle.load()
-        step()
-        torch.cuda.synchronize()
-        ref = O.run_workload(w)
-        max_err = float(np.max(np.abs(out.double().cpu().numpy() - ref)))
-
-    for i in range(args.warmup):
-        if not args.no_flush:
-            flush()
-        step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if not args.no_flush:
-            flush()
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    tot_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    t_step = statistics.mean(tot_ms)
-    t_dec = t_step  # one kernel per step
-    kv_gbps = kv_unique / (t_step * 1e-3) / 1e9
-    achieved = alg["total"] / (t_dec * 1e-3) / 1e9
-
-    src_hash = kernel_source_hash()
-    traffic = read_traffic(src_hash, kname, w.name)
+    shared = not args.no_prefix_groups
+    w = workload.make(args.workload, args.seed)
+    head = decode_leg(w, args, dev, flush, stream, O, shared, args.steps, args.warmup)
     probe = None if args.no_read_probe else read_probe(flush, dev)
 
     result = {
         "metric": METRIC,
-        "value": round(kv_gbps, 2),
+        "value": head["kv_gbps"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(t_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {
-            "workload": w.name,
-            "num_seqs": w.num_seqs,
-            "num_q_heads": w.num_q_heads,
-            "num_kv_heads": w.num_kv_heads,
-            "head_dim": w.head_dim,
-            "block_size": w.block_size,
-            "seq_len_mean": round(float(w.seq_lens.mean()), 1),
-            "seq_len_min": int(w.seq_lens.min()),
-            "seq_len_max": int(w.seq_lens.max()),
-            "num_blocks": w.num_blocks,
-            "shared_prefix_blocks": w.shared_prefix_blocks,
-            "cached_prefix_blocks": hint,
-            "seed": w.seed,
-            "kernel": args.kernel,
-            "decode_grid": grid,
-            "parallelism": "single GPU",
-        },
-        "hbm_frac": round(kv_gbps / HBM_PEAK_GBPS, 4),
-        "tokens_per_s": round(w.num_seqs / (t_step * 1e-3), 1),
-        "kv_bytes": kv_unique,
-        "kv_bytes_logical": kv_logical,
-        "kv_gbps_logical": round(kv_logical / (t_step * 1e-3) / 1e9, 2),
+        "config": head["config"],
+        "hbm_frac": head["hbm_frac"],
+        "tokens_per_s": head["tokens_per_s"],
+        "kv_bytes": head["kv_bytes"],
+        "kv_bytes_logical": head["kv_bytes_logical"],
+        "kv_gbps_logical": head["kv_gbps_logical"],
         "read_probe": probe,
-        "frac_of_read_probe": round(kv_gbps / probe["gbps"], 4) if probe else None,
-        "ms": {
-            "step_mean": round(t_step, 5), "step_median": round(statistics.median(tot_ms), 5),
-            "step_p10": round(sorted(tot_ms)[len(tot_ms) // 10], 5),
-            "step_p90": round(sorted(tot_ms)[(9 * len(tot_ms)) // 10], 5),
-        },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": kname,
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes": alg["total"],
-        },
+        "frac_of_read_probe": round(head["kv_gbps"] / probe["gbps"], 4) if probe else None,
+        "ms": head["ms"],
+        "roofline": head["roofline"],
         "timing": "HIP events on the launch stream around each kernel of each step; "
                   + ("read-only 1 GiB cache flush before every step, outside the events" if not args.no_flush
                      else "no cache flush"),
-        "wall_s_timed_loop": round(wall, 4),
-        "max_abs_err_vs_oracle": max_err,
-        "kernel_source_hash": src_hash,
+        "wall_s_timed_loop": head["wall_s_timed_loop"],
+        "max_abs_err_vs_oracle": head["max_abs_err_vs_oracle"],
+        "kernel_source_hash": head["kernel_source_hash"],
         "context": {
             "pages_paged_vs_contiguous": "paged kernel ~20-26% slower than a contiguous one "
                                          "(original vLLM paper, hardware not stated)",
             "pages_serving_throughput": "2-4x serving throughput at the same latency (vLLM, end to end)",
         },
     }
+    if w.num_groups > 0 and shared:
+        # the same batch through the ordinary call (each shared block read
+        # once per sequence, with the cache hint), for comparison
+        plain = decode_leg(w, args, dev, flush, stream, None, False, max(10, args.steps // 2),
+                           max(3, args.warmup // 2))
+        result["without_prefix_groups"] = {k: plain[k] for k in (
+            "ms_per_step", "kv_gbps", "hbm_frac", "tokens_per_s", "roofline")}
+        result["without_prefix_groups"]["entry_point"] = plain["config"]["entry_point"]
+        result["without_prefix_groups"]["cached_prefix_blocks"] = plain["config"]["cached_prefix_blocks"]
+    others = [int(x) for x in args.other_workloads.split(",") if x.strip()]
+    subs = {}
+    for wid in others:
+        if wid == args.workload:
+            continue
+        wo = workload.make(wid)
+        leg = decode_leg(wo, args, dev, flush, stream, O, shared, args.steps, args.warmup)
+        subs[str(wid)] = {k: leg[k] for k in (
+            "workload", "dtype", "ms_per_step", "kv_gbps", "hbm_frac", "tokens_per_s", "kv_bytes",
+            "roofline", "max_abs_err_vs_oracle", "ms")}
+        subs[str(wid)]["decode_grid"] = leg["config"]["decode_grid"]
+        del wo
+    if subs:
+        result["workloads"] = subs
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, kv_unique, args.cpu_seconds)
-    result["block_manager"] = block_manager_timing(w, with_cpu=not args.no_cpu_baseline)
-    if not args.no_eviction_scores:
-        result["eviction_scores"] = eviction_scores(w, kp, vp, dev, flush, stream,
-                                                    with_cpu=not args.no_cpu_baseline)
-    if not args.no_cache_writes:
-        # after the decode timing and its check: these write (unread) pool slots
-        result["cache_writes"] = cache_writes(w, kp, vp, dev, flush, stream,
-                                              with_cpu=not args.no_cpu_baseline)
+        result["cpu_baseline"] = cpu_baseline(w, head["kv_bytes"], args.cpu_seconds)
+    # the adjacent rows are measured on the GQA batch (workload 3)
+    wa = workload.make(3)
+    result["block_manager"] = block_manager_timing(wa, with_cpu=not args.no_cpu_baseline)
+    if not (args.no_eviction_scores and args.no_cache_writes):
+        kp = workload.to_device(wa.k_pool, wa.dtype, dev)
+        vp = workload.to_device(wa.v_pool, wa.dtype, dev)
+        if not args.no_eviction_scores:
+            result["eviction_scores"] = eviction_scores(wa, kp, vp, dev, flush, stream,
+                                                        with_cpu=not args.no_cpu_baseline)
+        if not args.no_cache_writes:
+            # these write (unread) pool slots of their own upload
+            result["cache_writes"] = cache_writes(wa, kp, vp, dev, flush, stream,
+                                                  with_cpu=not args.no_cpu_baseline)
+        del kp, vp
     if not args.no_prefill:
         result["prefill"] = prefill_timing(dev, flush, stream, with_cpu=not args.no_cpu_baseline)
     print(json.dumps(result), flush=True)

@@ -217,6 +217,71 @@ int32_t paged_attn_decode_noalloc(const void* q, const void* k_pool, const void*
 int32_t pa_decode_grid(const pa_desc* desc);
 
 /* ------------------------------------------------------------------
+ * Decode with prefix groups: blocks that several sequences share are read
+ * once for the whole group.
+ * ------------------------------------------------------------------ */
+
+/* Sequences that start with the same prompt point their block tables at
+ * the same physical blocks ("PagedAttention: The Cache Was Storing
+ * Nothing", §2.3 "What the table buys that reservations could not").
+ * paged_attn_decode reads such a block once per sequence; this call is
+ * told which sequences share how many leading blocks and reads every
+ * shared block once per group: the group's query heads meet each shared
+ * K/V tile in one pass (up to 32 / G members per pass, as the columns of
+ * one matrix-core tile pair), and each member's result is the merge of its
+ * shared part and its remaining blocks ("39 · PagedAttention", §3 merge
+ * equation).  The result is the same attention as paged_attn_decode's (up
+ * to fp32 rounding order).
+ *
+ * Groups.  Group i is the consecutive sequences group_start[i] ..
+ * group_start[i+1]-1 (device int32 [num_groups + 1], non-decreasing,
+ * group_start[num_groups] <= num_seqs; sequences outside every group share
+ * nothing).  group_shared[i] (device int32 [num_groups], >= 0): the leading
+ * table entries every member shares.  Precondition: for every member b and
+ * j < min(group_shared[i], n_b), block_tables[b][j] is the same physical
+ * block for all members (a member shorter than the shared prefix shares
+ * the blocks it has; its last one is partly its own).  Groups with fewer
+ * than two members or no shared block run as ordinary sequences.
+ *
+ * Built for fp16 / bf16 on the matrix-core kernel with G = Hq/Hkv in
+ * {1, 2, 4, 8}; for every other descriptor (and for num_groups == 0) the
+ * call runs paged_attn_decode with the same workspace, so results are
+ * always defined.
+ *
+ * workspace: at least pa_shared_workspace_bytes(desc) bytes, zero-filled
+ * before its first use; every call leaves it zeroed again.  One launch on
+ * `stream`.  Errors as for paged_attn_decode, plus PA_ERR_SHAPE for
+ * num_groups < 0 and PA_ERR_NULL for missing group arrays; PA_ERR_UNSUPPORTED
+ * when the schedule of this batch and its groups does not fit the
+ * workgroup's LDS (about 36 bytes per sequence and 4 per group besides the
+ * ordinary decode's).  Data-dependent preconditions are checked by
+ * pa_validate_shared_host, not on the device. */
+int32_t paged_attn_decode_shared(const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_tables, const int32_t* seq_lens,
+                                 const int32_t* group_start, const int32_t* group_shared,
+                                 int32_t num_groups, float scale, void* out, const pa_desc* desc,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of paged_attn_decode_shared (the ordinary decode's
+ * workspace, then per-(sequence, KV head) arrival counters and partials,
+ * and partials of shared parts cut by chunk boundaries); 0 on a bad
+ * descriptor. */
+size_t pa_shared_workspace_bytes(const pa_desc* desc);
+
+/* Workgroups of a paged_attn_decode_shared launch for this descriptor and
+ * group count on the current device, or -1 (error, not built, or the LDS
+ * does not fit). */
+int32_t pa_decode_shared_grid(const pa_desc* desc, int32_t num_groups);
+
+/* pa_validate_host, then the groups on HOST copies: group bounds ordered
+ * and inside the batch, group_shared >= 0 (PA_ERR_SHAPE otherwise), and
+ * the shared table entries equal across each group's members
+ * (PA_ERR_TABLE otherwise). */
+int32_t pa_validate_shared_host(const pa_desc* desc, const int32_t* block_tables_host,
+                                const int32_t* seq_lens_host, const int32_t* group_start_host,
+                                const int32_t* group_shared_host, int32_t num_groups);
+
+/* ------------------------------------------------------------------
  * Paged prefill: many query rows per sequence, causal.
  * ------------------------------------------------------------------ */
 

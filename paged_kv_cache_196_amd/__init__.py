@@ -33,6 +33,10 @@ from ._lib import (  # noqa: F401
     pa_workspace_bytes,
     paged_attn_decode,
     paged_attn_decode_noalloc,
+    paged_attn_decode_shared,
+    pa_decode_shared_grid,
+    pa_shared_workspace_bytes,
+    pa_validate_shared_host,
     paged_attn_prefill,
     paged_kv_append,
     paged_kv_block_scores,
@@ -40,4 +44,5 @@ from ._lib import (  # noqa: F401
     status_str,
 )
 from .api import (  # noqa: F401
-    append, block_scores, copy_blocks, decode, ensure_built, make_desc, new_workspace, prefill)
+    append, block_scores, copy_blocks, decode, decode_shared, ensure_built, make_desc,
+    new_shared_workspace, new_workspace, prefill)

@@ -27,7 +27,8 @@ EXPORTS = (
     "paged_kv_copy_blocks", "pa_validate_copy_host", "paged_kv_block_scores", "pa_bm_create",
     "pa_bm_destroy", "pa_bm_num_free", "pa_bm_refcount", "pa_bm_alloc", "pa_bm_release",
     "pa_bm_share", "pa_bm_prepare_append", "paged_attn_prefill", "pa_validate_prefill_host",
-    "paged_attn_decode_noalloc",
+    "paged_attn_decode_noalloc", "paged_attn_decode_shared", "pa_shared_workspace_bytes",
+    "pa_decode_shared_grid", "pa_validate_shared_host",
 )
 
 
@@ -83,6 +84,16 @@ def load() -> ctypes.CDLL:
             lib.paged_attn_decode.restype = ctypes.c_int32
             lib.paged_attn_decode_noalloc.argtypes = [_P, _P, _P, _P, _P, ctypes.c_float, _P, _DP, _P]
             lib.paged_attn_decode_noalloc.restype = ctypes.c_int32
+            lib.paged_attn_decode_shared.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                                     ctypes.c_float, _P, _DP, _P, ctypes.c_size_t,
+                                                     _P]
+            lib.paged_attn_decode_shared.restype = ctypes.c_int32
+            lib.pa_shared_workspace_bytes.argtypes = [_DP]
+            lib.pa_shared_workspace_bytes.restype = ctypes.c_size_t
+            lib.pa_decode_shared_grid.argtypes = [_DP, ctypes.c_int32]
+            lib.pa_decode_shared_grid.restype = ctypes.c_int32
+            lib.pa_validate_shared_host.argtypes = [_DP, _P, _P, _P, _P, ctypes.c_int32]
+            lib.pa_validate_shared_host.restype = ctypes.c_int32
             lib.pa_decode_grid.argtypes = [_DP]
             lib.pa_decode_grid.restype = ctypes.c_int32
             lib.paged_kv_append.argtypes = [_P, _P, _P, _P, _P, _P, _DP, _P]
@@ -203,6 +214,35 @@ def paged_attn_decode_noalloc(q, k_pool, v_pool, block_tables, seq_lens, scale: 
                                           _ptr(seq_lens), float(scale), _ptr(out),
                                           ctypes.byref(desc), _ptr(stream))
     return _check(rc, "paged_attn_decode_noalloc")
+
+
+def paged_attn_decode_shared(q, k_pool, v_pool, block_tables, seq_lens, group_start, group_shared,
+                             num_groups: int, scale: float, out, desc: PaDesc, workspace,
+                             workspace_bytes: int, stream=None) -> int:
+    rc = load().paged_attn_decode_shared(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                                         _ptr(seq_lens), _ptr(group_start), _ptr(group_shared),
+                                         int(num_groups), float(scale), _ptr(out),
+                                         ctypes.byref(desc), _ptr(workspace),
+                                         int(workspace_bytes), _ptr(stream))
+    return _check(rc, "paged_attn_decode_shared")
+
+
+def pa_shared_workspace_bytes(desc: PaDesc) -> int:
+    return int(load().pa_shared_workspace_bytes(ctypes.byref(desc)))
+
+
+def pa_decode_shared_grid(desc: PaDesc, num_groups: int) -> int:
+    return int(load().pa_decode_shared_grid(ctypes.byref(desc), int(num_groups)))
+
+
+def pa_validate_shared_host(desc: PaDesc, block_tables_host, seq_lens_host, group_start_host,
+                            group_shared_host, num_groups: int) -> int:
+    """Host copies as contiguous int32 numpy arrays (group arrays may be None
+    when num_groups is 0)."""
+    return int(load().pa_validate_shared_host(
+        ctypes.byref(desc), block_tables_host.ctypes.data, seq_lens_host.ctypes.data,
+        None if group_start_host is None else group_start_host.ctypes.data,
+        None if group_shared_host is None else group_shared_host.ctypes.data, int(num_groups)))
 
 
 def paged_attn_prefill(q, k_pool, v_pool, block_tables, seq_lens, q_start, max_q_len: int,

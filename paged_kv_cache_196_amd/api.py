@@ -14,6 +14,20 @@ _TORCH_DTYPES = {torch.float32: _lib.PA_F32, torch.float16: _lib.PA_F16,
                  torch.bfloat16: _lib.PA_BF16}
 
 
+def _check_out(out: torch.Tensor, q: torch.Tensor, out_dtype: torch.dtype | None) -> None:
+    """A caller's `out` must be what the library writes: q's shape, the
+    output type, contiguous, on q's device."""
+    want = q.dtype if out_dtype is None else out_dtype
+    if out.dtype != want:
+        raise TypeError(f"out must be {want} (got {out.dtype})")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"out must have q's shape {tuple(q.shape)} (got {tuple(out.shape)})")
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    if out.device != q.device:
+        raise ValueError("out must be on q's device")
+
+
 def ensure_built() -> str:
     """Build libpagedattn.so if it is not there yet; return its path."""
     if not os.path.exists(_lib.LIB_PATH):
@@ -86,6 +100,8 @@ def decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, *,
                      cached_prefix_blocks=cached_prefix_blocks)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    else:
+        _check_out(out, q, out_dtype)
     if workspace is None:
         workspace = new_workspace(desc, q.device)
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
@@ -95,18 +111,73 @@ def decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, *,
     return out
 
 
+def new_shared_workspace(desc: _lib.PaDesc, device) -> torch.Tensor:
+    """A zero-filled workspace for decode_shared (kept zeroed by the library)."""
+    nbytes = _lib.pa_shared_workspace_bytes(desc)
+    if nbytes == 0:
+        raise _lib.PagedAttnError(_lib.pa_check_desc(desc), "new_shared_workspace")
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def decode_shared(q, k_pool, v_pool, block_tables, seq_lens, group_start, group_shared,
+                  scale: float, *, out: torch.Tensor | None = None,
+                  out_dtype: torch.dtype | None = torch.float32, kernel: int = _lib.PA_KERNEL_AUTO,
+                  workspace: torch.Tensor | None = None,
+                  stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """Paged decode attention with prefix groups (paged_attn_decode_shared):
+    group i is the sequences group_start[i] .. group_start[i+1]-1, whose
+    first group_shared[i] table entries are the same physical blocks; those
+    blocks are read once per group.  group_start int32 [num_groups + 1],
+    group_shared int32 [num_groups], device tensors.  Other arguments as for
+    decode(); the workspace comes from new_shared_workspace()."""
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool),
+                    ("block_tables", block_tables), ("seq_lens", seq_lens),
+                    ("group_start", group_start), ("group_shared", group_shared)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens),
+                    ("group_start", group_start), ("group_shared", group_shared)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    if k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+        raise TypeError("q, k_pool and v_pool must share a dtype")
+    ng = group_shared.shape[0]
+    if group_start.shape != (ng + 1,):
+        raise ValueError("group_start must be [num_groups + 1]")
+    NB, Hkv, B, D = k_pool.shape
+    if B % 16 != 0 or tuple(v_pool.shape) != (NB, Hkv, B // 16, D, 16):
+        raise ValueError("v_pool must be [num_blocks][num_kv_heads][block_size/16][head_dim][16]")
+    _check_table(block_tables, q.shape[0])
+    desc = make_desc(q, k_pool, block_tables, out_dtype=out_dtype, kernel=kernel)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    else:
+        _check_out(out, q, out_dtype)
+    if workspace is None:
+        workspace = new_shared_workspace(desc, q.device)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    _lib.paged_attn_decode_shared(q, k_pool, v_pool, block_tables, seq_lens, group_start,
+                                  group_shared, ng, scale, out, desc, workspace,
+                                  workspace.numel() * workspace.element_size(), st.cuda_stream)
+    return out
+
+
 def prefill(q, k_pool, v_pool, block_tables, seq_lens, q_start, scale: float, *,
             max_q_len: int | None = None, out: torch.Tensor | None = None,
             out_dtype: torch.dtype | None = torch.float32, kernel: int = _lib.PA_KERNEL_AUTO,
-            stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+            stream: torch.cuda.Stream | None = None, check_rows: bool = True) -> torch.Tensor:
     """Causal paged prefill on device tensors; returns out [total_q][Hq][D].
 
     q [total_q][Hq][D]; q_start int32 [S + 1] row offsets: sequence b owns
     rows q_start[b] .. q_start[b+1]-1, its newest tokens (already in the
     pools), row i at position seq_lens[b] - n_b + i attending tokens 0 ..
     that position.  max_q_len: the largest n_b (read from q_start on the
-    host when not given, which synchronises).  Pools and tables as for
-    decode(); fp16 / bf16 only."""
+    host when not given).  check_rows (default): read q_start on the host
+    (synchronises) and check that it starts at 0, ends at q's row count and
+    that max_q_len covers every row range; pass False only with a q_start
+    already checked.  Pools and tables as for decode(); fp16 / bf16 only."""
     for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool),
                     ("block_tables", block_tables), ("seq_lens", seq_lens), ("q_start", q_start)):
         if not t.is_cuda:
@@ -127,13 +198,27 @@ def prefill(q, k_pool, v_pool, block_tables, seq_lens, q_start, scale: float, *,
     T, Hq, Dq = q.shape
     if Dq != D:
         raise ValueError("q and k_pool head_dim differ")
-    if max_q_len is None:
-        max_q_len = int((q_start[1:] - q_start[:-1]).max().item()) if S else 0
+    if max_q_len is None or check_rows:
+        # reads q_start on the host (synchronises): rows must match q, and
+        # the launch must cover the longest row range
+        qs = q_start.cpu()
+        n_b = qs[1:] - qs[:-1]
+        if S and (int(qs[0]) != 0 or int(n_b.min()) < 0):
+            raise ValueError("q_start must start at 0 and be non-decreasing")
+        if int(qs[-1]) != T:
+            raise ValueError(f"q_start[-1] = {int(qs[-1])} but q has {T} rows")
+        longest = int(n_b.max()) if S else 0
+        if max_q_len is None:
+            max_q_len = longest
+        elif max_q_len < longest:
+            raise ValueError(f"max_q_len {max_q_len} is below the longest row range {longest}")
     dt = pa_dtype_of(q.dtype)
     odt = dt if out_dtype is None else pa_dtype_of(out_dtype)
     desc = _lib.PaDesc(S, Hq, Hkv, D, B, NB, block_tables.shape[1], dt, odt, kernel, 0)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    else:
+        _check_out(out, q, out_dtype)
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
     _lib.paged_attn_prefill(q, k_pool, v_pool, block_tables, seq_lens, q_start, max_q_len, scale,
                             out, desc, st.cuda_stream)

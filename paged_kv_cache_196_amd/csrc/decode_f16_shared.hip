@@ -1,0 +1,10 @@
+// decode_f16_shared.hip — shared-prefix decode kernels for F16 inputs
+// (prefix groups read once per group; matrix cores), every block size and
+// group size built.
+#include "decode_shared_inst.h"
+
+namespace pa {
+
+Variant decode_shared_variant_f16(int B, int G) { return shared_pick<F16>(B, G); }
+
+}  // namespace pa

@@ -35,13 +35,15 @@
 
 namespace pa {
 
-template <class T, int B, int G>
+// kWide: the LDS of the shared-prefix kernel (room for the prefix items'
+// 32-column merges, shared_prefix.h); the arithmetic is the same.
+template <class T, int B, int G, bool kWide = false>
 struct MfmaEngine {
   static_assert(T::kEsize == 2, "matrix-core path takes fp16 / bf16");
   static_assert(G >= 1 && G <= 16, "query group padded to 16 MFMA columns");
   static_assert(B % kSub == 0, "block size must be a multiple of 16");
 
-  using Smem = MergeSmem<T, G>;
+  using Smem = MergeSmem<T, G, kWide>;
   using Op8 = typename std::conditional<T::kCode == BF16::kCode, bf16x8, f16x8>::type;
   using Op4 = typename std::conditional<T::kCode == BF16::kCode, bf16x4, f16x4>::type;
   using Elem = typename std::conditional<T::kCode == BF16::kCode, __bf16, _Float16>::type;

@@ -33,6 +33,10 @@ Variant decode_variant_bf16_valu(int B, int G);
 Variant decode_variant_f16_valu(int B, int G);
 Variant decode_variant_f32_valu(int B, int G);
 
+// Shared-prefix decode variants (matrix cores, fp16 / bf16; shared_prefix.h).
+Variant decode_shared_variant_bf16(int B, int G);
+Variant decode_shared_variant_f16(int B, int G);
+
 // Prefill launchers (matrix cores: fp16 / bf16), nullptr when not built.
 using PrefillFn = void (*)(const PrefillArgs&, dim3, hipStream_t);
 PrefillFn prefill_variant_bf16(int B, int G);

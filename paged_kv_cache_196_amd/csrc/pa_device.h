@@ -17,6 +17,7 @@ constexpr int kAuxThreads = 64 * kAuxWaves;
 constexpr int kSub = 16;         // tokens per sub-tile (unit of the streaming loop)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxGrid = 2048;   // upper bound on decode workgroups (sizes the workspace)
+constexpr int kWideCols = 32;    // MFMA columns of a prefix item: members x query heads
 constexpr int kMaxSeqs = 8192;   // sequences per call (LDS prefix array)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -44,6 +45,15 @@ struct Args {
   float scale_log2;  // scale * log2(e): scores are kept in base-2 exponent units
   int32_t S, Hq, Hkv, mbs, nwg, out_f32;
   int32_t cached_blocks;  // leading logical blocks read with the cache-retaining policy
+  // Prefix groups (shared-prefix calls only; ngroups = 0 otherwise).
+  const int32_t* grp_start;   // [ngroups + 1] group i = sequences grp_start[i] .. grp_start[i+1]-1
+  const int32_t* grp_shared;  // [ngroups] leading table entries every member shares
+  int32_t ngroups;
+  int* pcnt;       // [S*Hkv] arrival counters of member pairs
+  float* pair_o;   // [S*Hkv][2][G][kD] whole contributions: [0] item, [1] private part
+  float* pair_ml;  // [S*Hkv][2][G][2]
+  float* wide_o;   // [2*kMaxGrid][kWideCols][kD] item fragments cut by chunk boundaries
+  float* wide_ml;  // [2*kMaxGrid][kWideCols][2]
 };
 
 // ------------------------------------------------------------ conversions
@@ -274,7 +284,12 @@ __device__ __forceinline__ int chunk_of_wg(int wg, int nwg) {
 // published and counted in as soon as it is merged, mid-chunk.  Any other
 // partial piece ends its chunk ("late"); by then its partners have usually
 // been counted in, so it folds the split without publishing its own part.
-enum : int { kWhole = 0, kEarly = 1, kLate = 2 };
+//
+// A piece of a member pair (a sequence whose leading blocks are attended by
+// its prefix group's item, shared_prefix.h) is of kind kMember whatever its
+// extent: the pair always has at least two contributions (the item's and
+// its private blocks'), published and counted in on the pair's own counter.
+enum : int { kWhole = 0, kEarly = 1, kLate = 2, kMember = 3 };
 
 struct Piece {
   int b, kvh, L;
@@ -333,13 +348,88 @@ struct Partial {
   float m[kOut], l[kOut], o[kOut];
 };
 
-template <class T, int G>
+// Schedule of a shared-prefix call, in dynamic LDS (built by the prologue
+// of shared_prefix.h).  Sequence b attends its first shb[b] blocks through
+// its sub-group's item and the rest as private blocks; cum is the prefix
+// of private units (private blocks plus V virtual units per sequence with
+// any), icum of item block counts; cI / cP the chunk sizes of the item and
+// private unit spaces.  The scalars live in the workgroup's LDS struct;
+// the array addresses are recomputed from the dynamic LDS symbol wherever
+// they are used (shared_info), so that every access compiles to an LDS
+// access (a pointer kept in memory would come back as a generic pointer,
+// whose loads also wait for the wave's outstanding global stores).
+struct SharedScalars {
+  int nsg, cI, cP, V, B;
+};
+
+struct SharedInfo {
+  const int* lens;      // [S]
+  const int* shb;       // [S]
+  const int* seq_sg;    // [S] sub-group of b, -1 when b has no item
+  const int* cum;       // [S + 1]
+  const int* sg_first;  // [nsg] first member
+  const int* sg_count;  // [nsg] members
+  const int* sg_ref;    // [nsg] member whose table row covers the whole item
+  const int* sg_len;    // [nsg] tokens the item covers (longest member's shared part)
+  const int* icum;      // [nsg + 1]
+  int nsg, cI, cP, B;
+  int V;                // virtual units charged per (sequence, KV head) with private blocks
+};
+
+// Dynamic LDS layout of a shared-prefix call (ints): lens, shb, seq_sg (S
+// each), cum (S + 1), the group bounds and shared counts as loaded
+// (ngroups + 1 each), gbase (ngroups + 1), four sub-group arrays (S each)
+// and icum (S + 1).
+struct SharedLayout {
+  int *lens, *shb, *seq_sg, *cum, *gstart, *gshared, *gbase, *sg_first, *sg_count, *sg_ref,
+      *sg_len, *icum;
+};
+__host__ __device__ constexpr int64_t shared_lds_ints(int64_t S, int64_t ngroups) {
+  return 9 * S + 3 * (ngroups + 1) + 2;
+}
+__device__ __forceinline__ SharedLayout shared_layout(int S, int ng) {
+  extern __shared__ int pa_shared_dyn[];
+  SharedLayout l;
+  l.lens = pa_shared_dyn;
+  l.shb = l.lens + S;
+  l.seq_sg = l.shb + S;
+  l.cum = l.seq_sg + S;
+  l.gstart = l.cum + S + 1;
+  l.gshared = l.gstart + ng + 1;
+  l.gbase = l.gshared + ng + 1;
+  l.sg_first = l.gbase + ng + 1;
+  l.sg_count = l.sg_first + S;
+  l.sg_ref = l.sg_count + S;
+  l.sg_len = l.sg_ref + S;
+  l.icum = l.sg_len + S;
+  return l;
+}
+
+// Where the contributions of member pair `pair` (= b * Hkv + kvh) live:
+// first its item's (one whole-item partial in the pair slot, or one per
+// fragment in the wide chunk slots first_i, 2 * (kf_i + 1), ...), then its
+// private pieces' (one in the pair slot, or one per piece in the narrow
+// chunk slots).  mi is the member's place among its item's columns.
+struct MemberLayout {
+  int pair, mi;
+  int nfr, kf_i, first_i;  // item contributions
+  int npp, kf_p, first_p;  // private contributions (npp = 0: none)
+};
+
+constexpr int kDefer = 128;  // member contributions waiting for their count-in
+
+template <class T, int G, bool kWide = false>
 struct MergeSmem {
   static constexpr int kBatch = piece_batch<T, G>();
   static constexpr int kFoldMl = Partial<G>::kPer * G;
-  float o[kWaves][G][kD + 4];
-  float m[kWaves][G];
-  float l[kWaves][G];
+  // the wide (prefix item) phase: every wave holds 16 columns of `o` and
+  // the (max, sum) of its columns among all kWideCols in m / l
+  static constexpr int kOCols = kWide && G < 16 ? 16 : G;
+  static constexpr int kMCols = kWide && G < kWideCols ? kWideCols : G;
+  static constexpr int kDefers = kWide ? kDefer : 1;
+  float o[kWaves][kOCols][kD + 4];
+  float m[kWaves][kMCols];
+  float l[kWaves][kMCols];
   // (max, sum) of the pieces of one folding round
   float pm[kFoldMl];
   float pl[kFoldMl];
@@ -354,18 +444,55 @@ struct MergeSmem {
   // when this workgroup completes their split)
   Piece early, late;
   int fold_late;
+  // member contributions published and not yet counted in (pair indices)
+  int dpair[kDefers];
+  int dlast[kDefers];
+  MemberLayout dlay[kDefers];
+  int dn;
+  SharedScalars ssc;
 };
+
+// The shared-prefix schedule of this call (see SharedInfo).
+template <class Smem>
+__device__ __forceinline__ SharedInfo shared_info(const Args& a, const Smem& sm) {
+  const SharedLayout l = shared_layout(a.S, a.ngroups);
+  SharedInfo si;
+  si.lens = l.lens;
+  si.shb = l.shb;
+  si.seq_sg = l.seq_sg;
+  si.cum = l.cum;
+  si.sg_first = l.sg_first;
+  si.sg_count = l.sg_count;
+  si.sg_ref = l.sg_ref;
+  si.sg_len = l.sg_len;
+  si.icum = l.icum;
+  si.nsg = sm.ssc.nsg;
+  si.cI = sm.ssc.cI;
+  si.cP = sm.ssc.cP;
+  si.V = sm.ssc.V;
+  si.B = sm.ssc.B;
+  return si;
+}
 
 __device__ __forceinline__ float rescale(float mi, float m) {
   return mi == -INFINITY ? 0.f : fast_exp2(mi - m);
 }
 
 // Workspace partials are exchanged between workgroups that may sit on
-// different XCDs (separate L2s).  They are written and read with relaxed
-// agent-scope atomics (coherent at device scope without whole-L2
-// write-back / invalidate), and a writer waits for its stores to complete
-// before it counts itself in; a reader reads partials only after it has
-// seen every other piece counted in.
+// different XCDs (separate L2s).  Every partial value is written and read
+// with an agent-scope atomic (relaxed), so each one is coherent across the
+// XCDs by itself; the arrival counters order them:
+//   publish: every wave completes its partial stores (compiler barrier and
+//     a wait for its vector memory counter), the workgroup synchronises,
+//     and one thread counts in with an agent-scope read-modify-write;
+//   fold: the thread that saw every other piece counted in (from its
+//     count-in, or from a load of the counter) issues an agent-scope
+//     acquire fence, and the workgroup reads the partials after a barrier.
+// The count-in is not a release operation: on gfx950 an agent-scope release
+// writes back the whole L2 of the XCD (buffer_wbl2), which measured 6 % of
+// a GQA batch-64 call (one per workgroup) for nothing it has to order here,
+// since the published values are atomic stores that have completed before
+// the count-in is issued.  The acquire fence measured free.
 __device__ __forceinline__ void st_agent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -378,16 +505,27 @@ __device__ __forceinline__ int count_in(int* c) {
 __device__ __forceinline__ int counted(const int* c) {
   return __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Pairs with the release count-ins whose total the calling thread saw.
+__device__ __forceinline__ void acquire_counted() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 __device__ __forceinline__ void reset_count(int* c) {
   __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Waits until this wave's stores (and loads) have completed.
-__device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt immediate with vmcnt = 0 and the other counters at their
+// maximum (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt
+// high bits [15:14]): waits for vector memory operations only.
+constexpr int kVmcntZero = 0x0F70;
+// Waits until this wave's stores (and loads) have completed; no memory
+// access is moved across it by the compiler either.
+__device__ __forceinline__ void drain_vmem() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // Merge the kWaves wave partials the waves left in `sm` into this thread's
 // outputs.  Callers synchronise before (waves wrote sm) and after.
-template <class T, int G>
-__device__ inline void merge_waves(const MergeSmem<T, G>& sm, Partial<G>& pt) {
+template <class T, int G, class Smem>
+__device__ inline void merge_waves(const Smem& sm, Partial<G>& pt) {
 #pragma unroll
   for (int r = 0; r < Partial<G>::kOut; ++r) {
     const int idx = threadIdx.x + r * kThreads;
@@ -424,19 +562,25 @@ __device__ inline void store_result(const Args& a, const Piece& pc, const Partia
   }
 }
 
+// A partial's rows: weighted-V sums o_base[g][kD], (max, sum) ml_base[g][2].
 template <int G>
-__device__ inline void store_partial(const Args& a, int slot, const Partial<G>& pt) {
+__device__ inline void store_rows(float* o_base, float* ml_base, const Partial<G>& pt) {
 #pragma unroll
   for (int r = 0; r < Partial<G>::kOut; ++r) {
     const int idx = threadIdx.x + r * kThreads;
     if (idx >= G * kD) continue;
     const int g = idx / kD, d = idx % kD;
-    st_agent(a.ws_o + ((int64_t)slot * G + g) * kD + d, pt.o[r]);
+    st_agent(o_base + (int64_t)g * kD + d, pt.o[r]);
     if (d == 0) {
-      st_agent(a.ws_ml + ((int64_t)slot * G + g) * 2 + 0, pt.m[r]);
-      st_agent(a.ws_ml + ((int64_t)slot * G + g) * 2 + 1, pt.l[r]);
+      st_agent(ml_base + (int64_t)g * 2 + 0, pt.m[r]);
+      st_agent(ml_base + (int64_t)g * 2 + 1, pt.l[r]);
     }
   }
+}
+
+template <int G>
+__device__ inline void store_partial(const Args& a, int slot, const Partial<G>& pt) {
+  store_rows<G>(a.ws_o + (int64_t)slot * G * kD, a.ws_ml + (int64_t)slot * G * 2, pt);
 }
 
 // Folds the npieces partials of a split (sequence, KV head) and writes
@@ -448,8 +592,8 @@ __device__ inline void store_partial(const Args& a, int slot, const Partial<G>& 
 // issues the weighted-V loads of up to kPer pieces together with their
 // (max, sum) loads, so a split of up to kPer pieces costs one round trip.
 // All threads call; the caller has seen every piece counted in.
-template <class T, int G>
-__device__ inline void fold_split(const Args& a, MergeSmem<T, G>& sm, const Piece& pc,
+template <class T, int G, class Smem>
+__device__ inline void fold_split(const Args& a, Smem& sm, const Piece& pc,
                                   const Partial<G>& own, int own_slot) {
   constexpr int kOut = Partial<G>::kOut;
   constexpr int kPer = Partial<G>::kPer;
@@ -510,6 +654,200 @@ __device__ inline void fold_split(const Args& a, MergeSmem<T, G>& sm, const Piec
   store_result<T, G>(a, pc, acc);
 }
 
+// ------------------------------------------------ member pairs (prefix groups)
+//
+// A member pair's result is the fold of its contributions (MemberLayout),
+// each published to the workspace by the workgroup that computed it and
+// then counted in on the pair's counter a.pcnt[pair]; the workgroup whose
+// count-in completes the pair folds it.  Count-ins are batched: a
+// workgroup lists the contributions it published (sm.dpair) and counts
+// them in together (flush_members) after its prefix items, when the list
+// is full and at the end of its chunk, so no wave waits for a count-in in
+// the middle of the stream.  Publication and reading follow the counter
+// protocol above (count_in: acquire-release at agent scope after every
+// wave's stores completed and a barrier; partials read after a barrier
+// that follows the count-ins).
+
+__device__ inline MemberLayout member_layout(const Args& a, const SharedInfo& si, int pair) {
+  MemberLayout m;
+  const int b = pair / a.Hkv, kvh = pair % a.Hkv;
+  const int s = si.seq_sg[b];
+  m.pair = pair;
+  m.mi = b - si.sg_first[s];
+  const int nI = blocks_of(si.sg_len[s], si.B);
+  const int uI = si.icum[s] * a.Hkv + kvh * nI;
+  m.kf_i = uI / si.cI;
+  m.nfr = (uI + nI - 1) / si.cI - m.kf_i + 1;
+  m.first_i = 2 * m.kf_i + (uI != m.kf_i * si.cI ? 1 : 0);
+  const int np = blocks_of(si.lens[b], si.B) - si.shb[b];
+  m.npp = m.kf_p = m.first_p = 0;
+  if (np > 0) {
+    const int uP = si.cum[b] * a.Hkv + kvh * (np + si.V);
+    m.kf_p = uP / si.cP;
+    m.npp = (uP + np - 1) / si.cP - m.kf_p + 1;
+    m.first_p = 2 * m.kf_p + (uP != m.kf_p * si.cP ? 1 : 0);
+  }
+  return m;
+}
+
+// Bases of contribution i (0 <= i < nfr + npp) of a member pair: weighted-V
+// rows [G][kD] and (max, sum) pairs [G][2].
+template <int G>
+__device__ inline void member_contrib(const Args& a, const MemberLayout& m, int i, const float*& o,
+                                      const float*& ml) {
+  if (i < m.nfr) {
+    if (m.nfr == 1) {
+      o = a.pair_o + (int64_t)(2 * m.pair) * G * kD;
+      ml = a.pair_ml + (int64_t)(2 * m.pair) * G * 2;
+    } else {
+      const int slot = i == 0 ? m.first_i : 2 * (m.kf_i + i);
+      const int64_t col = (int64_t)slot * kWideCols + m.mi * G;
+      o = a.wide_o + col * kD;
+      ml = a.wide_ml + col * 2;
+    }
+    return;
+  }
+  i -= m.nfr;
+  if (m.npp == 1) {
+    o = a.pair_o + (int64_t)(2 * m.pair + 1) * G * kD;
+    ml = a.pair_ml + (int64_t)(2 * m.pair + 1) * G * 2;
+  } else {
+    const int slot = i == 0 ? m.first_p : 2 * (m.kf_p + i);
+    o = a.ws_o + (int64_t)slot * G * kD;
+    ml = a.ws_ml + (int64_t)slot * G * 2;
+  }
+}
+
+constexpr int kMemberFoldU = 8;  // outputs per thread folded together at a chunk end
+
+// Folds the nf member pairs listed in sm.dpair / sm.dlay and writes out.
+// Each thread takes U outputs at a time and issues the loads of their
+// contributions two at a time, so that a round of folds costs one memory
+// round trip per two contributions.  Contributions are combined in their
+// fixed order whichever workgroup folds.  All threads call.
+template <class T, int G, int U, class Smem>
+__device__ inline void fold_members(const Args& a, Smem& sm, int nf) {
+  constexpr int kPer = G * kD;
+  const int total = nf * kPer;
+  for (int x0 = 0; x0 < total; x0 += kThreads * U) {
+    float M[U], L[U], O[U];
+    int pi[U], g[U], d[U], E[U];
+    int emax = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int x = x0 + threadIdx.x + u * kThreads;
+      const int xc = x < total ? x : total - 1;
+      pi[u] = xc / kPer;
+      g[u] = (xc % kPer) / kD;
+      d[u] = xc % kD;
+      E[u] = x < total ? sm.dlay[pi[u]].nfr + sm.dlay[pi[u]].npp : 0;
+      emax = max(emax, E[u]);
+      M[u] = -INFINITY;
+      L[u] = 0.f;
+      O[u] = 0.f;
+    }
+    for (int i0 = 0; i0 < emax; i0 += 2) {
+      float vo[U][2], vm[U][2], vl[U][2];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          vo[u][j] = 0.f;
+          vm[u][j] = -INFINITY;
+          vl[u][j] = 0.f;
+          if (i0 + j < E[u]) {
+            const float* o;
+            const float* ml;
+            member_contrib<G>(a, sm.dlay[pi[u]], i0 + j, o, ml);
+            vo[u][j] = ld_agent(o + g[u] * kD + d[u]);
+            vm[u][j] = ld_agent(ml + g[u] * 2);
+            vl[u][j] = ld_agent(ml + g[u] * 2 + 1);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float Mn = fmaxf(M[u], fmaxf(vm[u][0], vm[u][1]));
+        const float f0 = rescale(M[u], Mn), f1 = rescale(vm[u][0], Mn), f2 = rescale(vm[u][1], Mn);
+        L[u] = L[u] * f0 + f1 * vl[u][0] + f2 * vl[u][1];
+        O[u] = O[u] * f0 + f1 * vo[u][0] + f2 * vo[u][1];
+        M[u] = Mn;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (x0 + threadIdx.x + u * kThreads >= total) continue;
+      const int pair = sm.dlay[pi[u]].pair;
+      const int b = pair / a.Hkv, kvh = pair % a.Hkv;
+      store_out<T>(a.out, ((int64_t)b * a.Hq + kvh * G + g[u]) * kD + d[u], O[u] / L[u], a.out_f32);
+    }
+  }
+}
+
+// Counts in every contribution listed in sm.dpair (each thread stored its
+// part of them before) and folds the pairs this workgroup completed.  All
+// threads call; the list is empty afterwards.
+template <class T, int G, int U, class Smem>
+__device__ inline void flush_members(const Args& a, Smem& sm) {
+  const int n = uniform(sm.dn);  // callers come here after a barrier
+  if (n == 0) return;
+  drain_vmem();     // this wave's partial stores have completed ...
+  __syncthreads();  // ... and every other wave's
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const int pair = sm.dpair[i];
+    const MemberLayout m = member_layout(a, shared_info(a, sm), pair);
+    const int r = count_in(a.pcnt + pair);
+    const bool last = r == m.nfr + m.npp - 1;
+    if (last) {
+      reset_count(a.pcnt + pair);
+      acquire_counted();
+    }
+    sm.dlast[i] = last;
+    sm.dlay[i] = m;
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    // keep the completed pairs, in list order (in place: a lane writes at or
+    // below the entry it read, and every lane reads before any writes)
+    const int lane = threadIdx.x;
+    const uint64_t below = (uint64_t(1) << lane) - 1;
+    int nf = 0;
+    for (int base = 0; base < n; base += 64) {
+      const int i = base + lane;
+      const bool keep = i < n && sm.dlast[i];
+      const MemberLayout m = sm.dlay[i < n ? i : 0];
+      const uint64_t km = __builtin_amdgcn_ballot_w64(keep);
+      if (keep) sm.dlay[nf + __builtin_popcountll(km & below)] = m;
+      nf += __builtin_popcountll(km);
+    }
+    if (lane == 0) sm.dn = nf;
+  }
+  __syncthreads();
+  const int nf = sm.dn;
+  if (nf > 0) fold_members<T, G, U>(a, sm, nf);
+  __syncthreads();
+  if (threadIdx.x == 0) sm.dn = 0;
+  __syncthreads();
+}
+
+// A piece of a member pair, merged across the waves (pt): publish it in its
+// slot and list it for the next count-in.  The list has room: it is
+// flushed between batches of pieces whenever a whole batch might not fit
+// (run_decode_shared), so no count-in or fold runs inside the stream.  All
+// threads call.
+template <class T, int G, class Smem>
+__device__ inline void publish_member(const Args& a, Smem& sm, const Piece& pc, const Partial<G>& pt) {
+  if constexpr (Smem::kDefers > 1) {
+    const int pair = pc.b * a.Hkv + pc.kvh;
+    if (pc.npieces == 1)
+      store_rows<G>(a.pair_o + (int64_t)(2 * pair + 1) * G * kD,
+                    a.pair_ml + (int64_t)(2 * pair + 1) * G * 2, pt);
+    else
+      store_partial<G>(a, pc.slot, pt);
+    if (threadIdx.x == 0) sm.dpair[sm.dn++] = pair;
+  }
+}
+
 // The last piece of a chunk when it is partial ("late").  sm.seen is the
 // split's arrival count read while the waves were merging (-1 if not
 // read).  When every other piece has already counted in, this workgroup
@@ -518,8 +856,8 @@ __device__ inline void fold_split(const Args& a, MergeSmem<T, G>& sm, const Piec
 // if it turned out to be the last.  The fold itself runs at the end of the
 // chunk (finish_chunk), outside the streaming loop, from the own partial
 // left in LDS.
-template <class T, int G>
-__device__ inline void finish_late(const Args& a, MergeSmem<T, G>& sm, const Piece& pc,
+template <class T, int G, class Smem>
+__device__ inline void finish_late(const Args& a, Smem& sm, const Piece& pc,
                                    const Partial<G>& pt) {
   int* cnt = a.counters + pc.kfirst;
   bool fold = uniform(sm.seen) == pc.npieces - 1;
@@ -566,13 +904,15 @@ __device__ inline void finish_late(const Args& a, MergeSmem<T, G>& sm, const Pie
 // split (finish_late).  Values returned by memory are moved to LDS where
 // they arrive, so no load is left in flight into a register that the
 // streaming loop reuses.
-template <class T, int G>
-__device__ inline void finish_piece(const Args& a, MergeSmem<T, G>& sm, const Piece& pc) {
+template <class T, int G, class Smem>
+__device__ inline void finish_piece(const Args& a, Smem& sm, const Piece& pc) {
   __syncthreads();
   Partial<G> pt;
   merge_waves<T, G>(sm, pt);
   if (pc.kind == kWhole) {
     store_result<T, G>(a, pc, pt);
+  } else if (pc.kind == kMember) {
+    publish_member<T, G>(a, sm, pc, pt);
   } else if (pc.kind == kEarly) {
     store_partial<G>(a, pc.slot, pt);
     drain_vmem();
@@ -590,9 +930,13 @@ __device__ inline void finish_piece(const Args& a, MergeSmem<T, G>& sm, const Pi
 // End of the chunk: fold the late piece's split if finish_late chose to
 // (own partial in LDS), and the early piece's split if its count-in was
 // the last one.  All threads call.
-template <class T, int G>
-__device__ inline void finish_chunk(const Args& a, MergeSmem<T, G>& sm) {
-  if (threadIdx.x == 0) sm.flag = sm.early_seen >= 0 && sm.early_seen == sm.early.npieces - 1;
+template <class T, int G, class Smem>
+__device__ inline void finish_chunk(const Args& a, Smem& sm) {
+  if (threadIdx.x == 0) {
+    sm.flag = sm.early_seen >= 0 && sm.early_seen == sm.early.npieces - 1;
+    // thread 0 read the counts of both splits: acquire before their folds
+    if (sm.flag || sm.fold_late) acquire_counted();
+  }
   __syncthreads();
   if (uniform(sm.fold_late)) {
     const Piece pc = uniform_piece(sm.late);
@@ -615,6 +959,7 @@ __device__ inline void finish_chunk(const Args& a, MergeSmem<T, G>& sm) {
     for (int r = 0; r < Partial<G>::kOut; ++r) none.m[r] = none.l[r] = none.o[r] = 0.f;
     fold_split<T, G>(a, sm, pc, none, -1);
   }
+  if constexpr (Smem::kDefers > 1) flush_members<T, G, kMemberFoldU>(a, sm);
 }
 
 // out = 0 for sequences of length 0 (every query head).  Sequences are
@@ -814,9 +1159,19 @@ __device__ inline void stream_batch(const Args& a, typename Engine::Smem& sm) {
 // and further rounds of 64 continue until the batch is full or the chunk
 // ends.  Pieces are contiguous in flat order, so the next batch starts
 // where the last listed piece ends.
-template <int B, class Smem>
-__device__ inline void list_batch(const Args& a, Smem& sm, const int* cum, const int* lens_s, int s,
-                                  int e, int chunk, int c) {
+// With prefix groups (kShared) cum counts private blocks only: sequence b's
+// units start after its shb[b] leading blocks (attended by its item), and
+// every piece of a sequence with an item is a member piece.
+//
+// V > 0: every (sequence, KV head) with blocks is charged V virtual units
+// after its real ones (cum counts n_b + V for such sequences), so that the
+// equal chunks balance time rather than blocks: a piece costs a merge and
+// its output on top of its blocks.  A chunk boundary inside those virtual
+// units leaves no piece there; pieces, kinds and split counts follow the
+// real blocks only.
+template <int B, bool kShared, class Smem>
+__device__ inline void list_batch(const Args& a, Smem& sm, const int* cum, const int* lens_s,
+                                  const int* shb, int s, int e, int chunk, int c, int V) {
   const int lane = threadIdx.x & 63;
   const int f0 = uniform(sm.next_f);
   if (lane == 0) {
@@ -832,30 +1187,33 @@ __device__ inline void list_batch(const Args& a, Smem& sm, const int* cum, const
   for (int lin = kvh0; n < Smem::kBatch; lin += 64) {
     const int L = lin + lane;
     const int b = b0 + L / a.Hkv, kvh = L % a.Hkv;
-    int nb = 0, ustart = 0;
+    int nb = 0, real = 0, ustart = 0;
     if (b < a.S) {
-      nb = cum[b + 1] - cum[b];
+      nb = cum[b + 1] - cum[b];  // units of each KV head of b (real + V)
+      real = nb > 0 ? nb - V : 0;
       ustart = cum[b] * a.Hkv + kvh * nb;
     }
+    const int f = L == kvh0 ? f0 : ustart;
     const bool past = b >= a.S || (nb > 0 && ustart >= e);
-    const bool ok = !past && nb > 0;
+    const bool ok = !past && real > 0 && f - ustart < real;
     const uint64_t okm = __builtin_amdgcn_ballot_w64(ok);
     const int idx = n + __builtin_popcountll(okm & below);
     if (ok && idx < Smem::kBatch) {
-      const int f = L == kvh0 ? f0 : ustart;
-      const int pe = min(e, ustart + nb);
+      const int pe = min(e, ustart + real);
       const int j0 = f - ustart, j1 = pe - ustart;
       Piece pc;
       pc.b = b;
       pc.kvh = kvh;
       pc.L = lens_s[b];
-      pc.tok_begin = j0 * B;
-      pc.tok_end = min(j1 * B, pc.L);
+      const int off = kShared ? shb[b] * B : 0;
+      pc.tok_begin = off + j0 * B;
+      pc.tok_end = min(off + j1 * B, pc.L);
       pc.nsub = (pc.tok_end - pc.tok_begin + kSub - 1) / kSub;
-      pc.kind = (j0 == 0 && j1 == nb) ? kWhole : (f == s && pe < e) ? kEarly : kLate;
+      pc.kind = (kShared && off > 0) ? kMember
+                : (j0 == 0 && j1 == real) ? kWhole : (f == s && pe < e) ? kEarly : kLate;
       pc.slot = 2 * chunk + (f == s ? 0 : 1);
       pc.kfirst = ustart / c;
-      pc.npieces = (ustart + nb - 1) / c - pc.kfirst + 1;
+      pc.npieces = (ustart + real - 1) / c - pc.kfirst + 1;
       pc.first_slot = 2 * pc.kfirst + (ustart != pc.kfirst * c ? 1 : 0);
       sm.plist[idx] = pc;
       if (idx == Smem::kBatch - 1) sm.next_f = pe;
@@ -889,7 +1247,7 @@ __device__ inline void run_decode(const Args& a) {
   }
   __syncthreads();
   while (true) {
-    if (threadIdx.x < 64) list_batch<B>(a, sm, cum, lens_s, s, e, chunk, c);
+    if (threadIdx.x < 64) list_batch<B, false>(a, sm, cum, lens_s, nullptr, s, e, chunk, c, 0);
     __syncthreads();
     const int npl = sm.npl;
     if (npl == 0) break;

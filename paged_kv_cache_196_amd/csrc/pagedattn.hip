@@ -11,6 +11,7 @@
 // in the workspace, where the last one to finish folds them.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string.h>
 #include <unordered_map>
@@ -117,6 +118,58 @@ void bind_workspace(Args* a, void* ws, int counters, int slots, int G) {
   a->ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + cnt);
   a->ws_ml = a->ws_o + (size_t)slots * G * kD;
 }
+
+// Workspace of a shared-prefix call: the ordinary decode workspace first
+// (split counters and narrow partials, same layout), then the member
+// pairs' counters [S*Hkv], their whole-contribution slots pair_o
+// [S*Hkv][2][G][kD] / pair_ml [S*Hkv][2][G][2], and the wide slots of item
+// fragments wide_o [2*kMaxSharedGrid][kWideCols][kD] / wide_ml [..][2].
+constexpr int kMaxSharedGrid = 512;
+
+struct SharedWs {
+  size_t pcnt, pair_o, pair_ml, wide_o, wide_ml, total;
+};
+
+SharedWs shared_ws_layout(const pa_desc* d) {
+  const size_t G = (size_t)(d->num_q_heads / d->num_kv_heads);
+  const size_t pairs = (size_t)d->num_seqs * d->num_kv_heads;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  SharedWs w;
+  size_t off = al(ws_layout_bytes(kMaxGrid, 2 * kMaxGrid, (int)G));
+  w.pcnt = off;
+  off = al(off + sizeof(int) * pairs);
+  w.pair_o = off;
+  off = al(off + sizeof(float) * pairs * 2 * G * kD);
+  w.pair_ml = off;
+  off = al(off + sizeof(float) * pairs * 2 * G * 2);
+  w.wide_o = off;
+  off = al(off + sizeof(float) * 2 * kMaxSharedGrid * kWideCols * kD);
+  w.wide_ml = off;
+  off = al(off + sizeof(float) * 2 * kMaxSharedGrid * kWideCols * 2);
+  w.total = off;
+  return w;
+}
+
+void bind_shared_workspace(Args* a, void* ws, const SharedWs& w) {
+  char* base = static_cast<char*>(ws);
+  a->pcnt = reinterpret_cast<int*>(base + w.pcnt);
+  a->pair_o = reinterpret_cast<float*>(base + w.pair_o);
+  a->pair_ml = reinterpret_cast<float*>(base + w.pair_ml);
+  a->wide_o = reinterpret_cast<float*>(base + w.wide_o);
+  a->wide_ml = reinterpret_cast<float*>(base + w.wide_ml);
+}
+
+// The shared-prefix kernel of a descriptor: matrix cores (fp16 / bf16, kernel
+// AUTO or MFMA); an empty Variant otherwise.
+Variant pick_shared(const pa_desc* d) {
+  if (!use_mfma(d)) return Variant{};
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (d->dtype == PA_BF16) return decode_shared_variant_bf16(d->block_size, G);
+  if (d->dtype == PA_F16) return decode_shared_variant_f16(d->block_size, G);
+  return Variant{};
+}
+
+size_t shared_lds(int S, int ngroups) { return (size_t)shared_lds_ints(S, ngroups) * sizeof(int); }
 
 // Prefill variant of a descriptor: matrix cores only (fp16 / bf16).
 PrefillFn pick_prefill(const pa_desc* d) {
@@ -275,6 +328,11 @@ static int32_t prepare(const void* q, const void* k_pool, const void* v_pool, co
   a->nwg = g;
   a->out_f32 = d->out_dtype == PA_F32 ? 1 : 0;
   a->cached_blocks = d->cached_prefix_blocks;
+  a->grp_start = nullptr;
+  a->grp_shared = nullptr;
+  a->ngroups = 0;
+  a->pcnt = nullptr;
+  a->pair_o = a->pair_ml = a->wide_o = a->wide_ml = nullptr;
   *grid = g;
   return PA_OK;
 }
@@ -314,6 +372,92 @@ int32_t paged_attn_decode_noalloc(const void* q, const void* k_pool, const void*
   if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
   const Variant v = pick(d);
   if (v.launch(a, grid, prefix_lds(a.S), s) != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+size_t pa_shared_workspace_bytes(const pa_desc* d) {
+  if (pa_check_desc(d) != PA_OK) return 0;
+  return shared_ws_layout(d).total;
+}
+
+int32_t pa_validate_shared_host(const pa_desc* d, const int32_t* bt, const int32_t* lens,
+                                const int32_t* group_start, const int32_t* group_shared,
+                                int32_t num_groups) {
+  const int32_t st = pa_validate_host(d, bt, lens);
+  if (st != PA_OK) return st;
+  if (num_groups < 0) return PA_ERR_SHAPE;
+  if (num_groups == 0) return PA_OK;
+  if (!group_start || !group_shared) return PA_ERR_NULL;
+  if (group_start[0] < 0 || group_start[num_groups] > d->num_seqs) return PA_ERR_SHAPE;
+  const int64_t B = d->block_size, mbs = d->max_blocks_per_seq;
+  for (int32_t g = 0; g < num_groups; ++g) {
+    const int32_t f = group_start[g], e = group_start[g + 1];
+    if (e < f || group_shared[g] < 0) return PA_ERR_SHAPE;
+    if (e - f < 2 || group_shared[g] == 0) continue;
+    // the member covering the most shared blocks holds the reference row
+    int32_t ref = f;
+    int64_t most = -1;
+    for (int32_t b = f; b < e; ++b) {
+      const int64_t nb = std::min<int64_t>(pa_blocks_for_len(lens[b], d->block_size), group_shared[g]);
+      if (nb > most) {
+        most = nb;
+        ref = b;
+      }
+    }
+    for (int32_t b = f; b < e; ++b) {
+      const int64_t nb = std::min<int64_t>(pa_blocks_for_len(lens[b], d->block_size), group_shared[g]);
+      for (int64_t j = 0; j < nb; ++j)
+        if (bt[b * mbs + j] != bt[ref * mbs + j]) return PA_ERR_TABLE;
+    }
+  }
+  (void)B;
+  return PA_OK;
+}
+
+int32_t pa_decode_shared_grid(const pa_desc* d, int32_t num_groups) {
+  if (pa_check_desc(d) != PA_OK || num_groups < 0) return -1;
+  const DeviceInfo info = device_info();
+  if (!info.ok) return -1;
+  const Variant v = pick_shared(d);
+  if (!v.launch) return -1;
+  const int per_cu = v.occ(shared_lds(d->num_seqs, num_groups));
+  if (per_cu <= 0) return -1;
+  int grid = info.cus * per_cu;
+  if (grid > kMaxSharedGrid) grid = kMaxSharedGrid;
+  return grid;
+}
+
+int32_t paged_attn_decode_shared(const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* bt, const int32_t* lens,
+                                 const int32_t* group_start, const int32_t* group_shared,
+                                 int32_t num_groups, float scale, void* out, const pa_desc* d,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  const int32_t st0 = pa_check_desc(d);
+  if (st0 != PA_OK) return st0;
+  if (num_groups < 0) return PA_ERR_SHAPE;
+  if (num_groups > 0 && (!group_start || !group_shared)) return PA_ERR_NULL;
+  if (d->num_seqs > 0 && (!ws || ws_bytes < shared_ws_layout(d).total || ((uintptr_t)ws & 15u)))
+    return PA_ERR_WORKSPACE;
+  const Variant v = pick_shared(d);
+  if (num_groups == 0 || !v.launch)  // no group to share, or not the matrix-core kernel
+    return paged_attn_decode(q, k_pool, v_pool, bt, lens, scale, out, d, ws, ws_bytes, stream);
+  Args a;
+  int grid = 0;
+  const int32_t st = prepare(q, k_pool, v_pool, bt, lens, scale, out, d, true, ws, ws_bytes, &a,
+                             &grid);
+  if (st != PA_OK || grid == 0) return st;
+  grid = pa_decode_shared_grid(d, num_groups);
+  if (grid <= 0) return PA_ERR_UNSUPPORTED;  // LDS of this batch and its groups does not fit
+  a.nwg = grid;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  bind_workspace(&a, ws, kMaxGrid, 2 * kMaxGrid, G);
+  bind_shared_workspace(&a, ws, shared_ws_layout(d));
+  a.grp_start = group_start;
+  a.grp_shared = group_shared;
+  a.ngroups = num_groups;
+  if (v.launch(a, grid, shared_lds(a.S, num_groups), static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return PA_ERR_LAUNCH;
   return PA_OK;
 }
 

@@ -6,16 +6,14 @@ import numpy as np
 import torch
 
 import paged_kv_cache_196_amd as pa
+import workload
 
 TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
 KERNELS = {"valu": pa.PA_KERNEL_VALU, "mfma": pa.PA_KERNEL_MFMA}
 TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
-def device_tensor(x: np.ndarray, dtype: str, dev="cuda"):
-    if dtype == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
-    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+device_tensor = workload.to_device
 
 
 class Uploaded:
@@ -26,6 +24,8 @@ class Uploaded:
         self.v = device_tensor(w.v_pool, w.dtype)
         self.bt = torch.from_numpy(w.block_tables).cuda()
         self.lens = torch.from_numpy(w.seq_lens).cuda()
+        self.gs = torch.from_numpy(w.group_start).cuda()
+        self.gsh = torch.from_numpy(w.group_shared).cuda()
 
     def run(self, kernel="auto", out_dtype=torch.float32, cached_prefix_blocks=0):
         k = pa.PA_KERNEL_AUTO if kernel == "auto" else KERNELS[kernel]
@@ -44,3 +44,26 @@ def max_err(got: torch.Tensor, ref: np.ndarray) -> float:
     assert g.shape == ref.shape
     assert np.all(np.isfinite(g)), "non-finite output"
     return float(np.max(np.abs(g - ref))) if g.size else 0.0
+
+
+def desc_of(up, kernel="auto", out_dtype=torch.float32):
+    k = pa.PA_KERNEL_AUTO if kernel == "auto" else KERNELS[kernel]
+    return pa.make_desc(up.q, up.k, up.bt, out_dtype=out_dtype, kernel=k)
+
+
+def run_shared(up, kernel="auto", out_dtype=torch.float32, workspace=None, group_start=None,
+               group_shared=None):
+    """paged_attn_decode_shared on an uploaded workload (its own prefix groups
+    unless others are given), after the host check of the groups."""
+    w = up.w
+    gs = w.group_start if group_start is None else np.asarray(group_start, np.int32)
+    gsh = w.group_shared if group_shared is None else np.asarray(group_shared, np.int32)
+    desc = desc_of(up, kernel, out_dtype)
+    assert pa.pa_validate_shared_host(desc, w.block_tables, w.seq_lens, gs, gsh, gsh.shape[0]) == 0
+    k = pa.PA_KERNEL_AUTO if kernel == "auto" else KERNELS[kernel]
+    out = torch.full(up.q.shape, float("nan"), dtype=out_dtype, device=up.q.device)
+    pa.decode_shared(up.q, up.k, up.v, up.bt, up.lens, torch.from_numpy(gs).cuda(),
+                     torch.from_numpy(gsh).cuda(), float(w.scale), out=out, out_dtype=out_dtype,
+                     kernel=k, workspace=workspace)
+    torch.cuda.synchronize()
+    return out

@@ -319,3 +319,34 @@ def test_noalloc_argument_errors_before_any_launch(lib):
     import torch
     if not torch.cuda.is_available():
         assert f(P, P, P, P, P, 0.1, P, pa._lib.ctypes.byref(d), None) == 9
+
+
+def test_shared_prefix_host_checks(lib):
+    """pa_validate_shared_host: group bounds and shared counts, and the
+    shared table entries equal across members (checked on host copies)."""
+    d = _desc(num_seqs=5, max_blocks_per_seq=4, num_blocks=64)
+    lens = np.array([40, 64, 10, 0, 33], np.int32)
+    bt = np.full((5, 4), -1, np.int32)
+    bt[0, :3] = [5, 6, 7]
+    bt[1, :4] = [5, 6, 8, 9]
+    bt[2, :1] = [5]
+    bt[4, :3] = [11, 12, 13]
+    ok = pa.pa_validate_shared_host
+    gs, gsh = np.array([0, 4, 5], np.int32), np.array([2, 3], np.int32)
+    assert ok(d, bt, lens, gs, gsh, 2) == 0
+    assert ok(d, bt, lens, None, None, 0) == 0
+    assert ok(d, bt, lens, gs, gsh, -1) == 2
+    assert ok(d, bt, lens, np.array([0, 4, 6], np.int32), gsh, 2) == 2   # past the batch
+    assert ok(d, bt, lens, np.array([0, 4, 3], np.int32), gsh, 2) == 2   # decreasing
+    assert ok(d, bt, lens, gs, np.array([2, -1], np.int32), 2) == 2
+    assert ok(d, bt, lens, gs, np.array([3, 3], np.int32), 2) == 8       # entry 2 differs
+    bt2 = bt.copy()
+    bt2[2, 0] = 9                                                         # short member differs
+    assert ok(d, bt2, lens, gs, gsh, 2) == 8
+    assert pa.pa_shared_workspace_bytes(d) > pa.pa_workspace_bytes(d)
+    P = 1 << 20
+    f = lib.paged_attn_decode_shared
+    nb = pa.pa_shared_workspace_bytes(d)
+    assert f(P, P, P, P, P, P, P, -1, 0.1, P, pa._lib.ctypes.byref(d), P, nb, None) == 2
+    assert f(P, P, P, P, P, None, P, 1, 0.1, P, pa._lib.ctypes.byref(d), P, nb, None) == 1
+    assert f(P, P, P, P, P, P, P, 1, 0.1, P, pa._lib.ctypes.byref(d), P, nb - 1, None) == 5

@@ -67,6 +67,14 @@ class Workload:
     scale: np.float32
     seed: int = 0
     shared_prefix_blocks: int = 0  # leading logical blocks shared within prefix groups
+    # prefix groups: group i = sequences group_start[i] .. group_start[i+1]-1,
+    # whose first group_shared[i] table entries are the same physical blocks
+    group_start: np.ndarray = dataclasses.field(default_factory=lambda: np.zeros(1, np.int32))
+    group_shared: np.ndarray = dataclasses.field(default_factory=lambda: np.zeros(0, np.int32))
+
+    @property
+    def num_groups(self) -> int:
+        return int(self.group_shared.shape[0])
 
     @property
     def num_seqs(self) -> int:
@@ -83,6 +91,14 @@ class Workload:
     def blocks_per_seq(self) -> np.ndarray:
         B = self.block_size
         return (self.seq_lens.astype(np.int64) + B - 1) // B
+
+
+def to_device(x: np.ndarray, dtype: str, dev="cuda") -> torch.Tensor:
+    """Upload a storage array of workload dtype `dtype` (bf16 as raw uint16
+    bits) as a torch tensor of that type on `dev`."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
 
 
 def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -121,13 +137,17 @@ def build(*, name: str, dtype: str, seq_lens, num_q_heads: int, num_kv_heads: in
           head_dim: int, block_size: int, seed: int, num_blocks: int | None = None,
           pool_factor: float = 1.25, max_blocks_per_seq: int | None = None,
           prefix_group: int = 0, prefix_blocks: int = 0, k_head_scale=None,
-          tables=None, shuffle: bool = True, chunk_blocks: int = 2048) -> Workload:
+          tables=None, shuffle: bool = True, chunk_blocks: int = 2048,
+          group_sizes=None, group_blocks=None) -> Workload:
     """General seeded builder; every named workload goes through it.
 
     seq_lens: int lengths (already drawn).  tables: explicit block tables
     (list of lists) instead of drawing them.  prefix_group > 0: consecutive
     groups of that many sequences share their first `prefix_blocks`
-    physical blocks.  k_head_scale: per-KV-head multipliers applied to K in
+    physical blocks.  group_sizes / group_blocks: consecutive groups of the
+    given sizes sharing the given numbers of leading blocks (sequences after
+    the last group share nothing); a member shorter than its group's shared
+    prefix holds only the shared blocks its length needs.  k_head_scale: per-KV-head multipliers applied to K in
     float32 before rounding.  num_blocks: pool size; default
     ceil(pool_factor * demand).
     """
@@ -149,29 +169,39 @@ def build(*, name: str, dtype: str, seq_lens, num_q_heads: int, num_kv_heads: in
     else:
         if prefix_group > 0:
             groups = [list(range(s, min(s + prefix_group, S))) for s in range(0, S, prefix_group)]
-            demand = len(groups) * prefix_blocks + int(np.maximum(nb - prefix_blocks, 0).sum())
+            gblocks = [prefix_blocks] * len(groups)
+        elif group_sizes is not None:
+            groups, s0 = [], 0
+            for n in group_sizes:
+                groups.append(list(range(s0, s0 + n)))
+                s0 += n
+            assert s0 <= S, "groups exceed the batch"
+            gblocks = [int(x) for x in group_blocks]
+            assert len(gblocks) == len(groups)
         else:
-            groups = []
-            demand = int(nb.sum())
+            groups, gblocks = [], []
+        covered = sum(len(g) for g in groups)
+        shared_of = np.zeros(S, np.int64)
+        for grp, k in zip(groups, gblocks):
+            shared_of[grp] = k
+        demand = int(sum(gblocks)) + int(np.maximum(nb - shared_of, 0).sum())
         if num_blocks is None:
             num_blocks = max(1, int(math.ceil(pool_factor * demand)))
         assert num_blocks >= demand, "pool smaller than demand"
         ids = rng_blk.permutation(num_blocks) if shuffle else np.arange(num_blocks)
         nxt = 0
-        if prefix_group > 0:
-            for grp in groups:
-                pref = ids[nxt: nxt + prefix_blocks]
-                nxt += prefix_blocks
-                for b in grp:
-                    k = min(prefix_blocks, int(nb[b]))
-                    bt[b, :k] = pref[:k]
-                    rest = int(nb[b]) - k
-                    bt[b, k: k + rest] = ids[nxt: nxt + rest]
-                    nxt += rest
-        else:
-            for b in range(S):
-                bt[b, : nb[b]] = ids[nxt: nxt + nb[b]]
-                nxt += int(nb[b])
+        for grp, kg in zip(groups, gblocks):
+            pref = ids[nxt: nxt + kg]
+            nxt += kg
+            for b in grp:
+                k = min(kg, int(nb[b]))
+                bt[b, :k] = pref[:k]
+                rest = int(nb[b]) - k
+                bt[b, k: k + rest] = ids[nxt: nxt + rest]
+                nxt += rest
+        for b in range(covered, S):
+            bt[b, : nb[b]] = ids[nxt: nxt + nb[b]]
+            nxt += int(nb[b])
 
     # Longest attended prefix of every physical block (0 = unreferenced).
     valid = np.zeros(num_blocks, np.int64)
@@ -207,13 +237,19 @@ def build(*, name: str, dtype: str, seq_lens, num_q_heads: int, num_kv_heads: in
 
     qf = rng_q.standard_normal((S, num_q_heads, D), dtype=np.float32)
     q = round_to(qf, dtype).reshape(qf.shape)
+    if tables is None and groups:
+        g_start = np.array([g[0] for g in groups] + [groups[-1][-1] + 1], np.int32)
+        g_shared = np.array(gblocks, np.int32)
+    else:
+        g_start, g_shared = np.zeros(1, np.int32), np.zeros(0, np.int32)
     return Workload(name=name, dtype=dtype, num_q_heads=num_q_heads, num_kv_heads=Hkv,
                     head_dim=D, block_size=B, num_blocks=int(num_blocks),
                     max_blocks_per_seq=int(max_blocks_per_seq),
                     seq_lens=lens.astype(np.int32), block_tables=bt, q=q,
                     k_pool=k_pool, v_pool=v_pool,
                     scale=np.float32(1.0 / math.sqrt(head_dim)), seed=seed,
-                    shared_prefix_blocks=int(prefix_blocks) if prefix_group > 1 else 0)
+                    shared_prefix_blocks=int(prefix_blocks) if prefix_group > 1 else 0,
+                    group_start=g_start, group_shared=g_shared)
 
 
 CONFIG_NAMES = {
