@@ -54,6 +54,7 @@ struct Args {
   float* pair_ml;  // [S*Hkv][2][G][2]
   float* wide_o;   // [2*kMaxGrid][kWideCols][kD] item fragments cut by chunk boundaries
   float* wide_ml;  // [2*kMaxGrid][kWideCols][2]
+  int32_t stage_cap;  // member partials the workgroup's LDS can hold until its next count-in
 };
 
 // ------------------------------------------------------------ conversions
@@ -383,6 +384,7 @@ struct SharedInfo {
 struct SharedLayout {
   int *lens, *shb, *seq_sg, *cum, *gstart, *gshared, *gbase, *sg_first, *sg_count, *sg_ref,
       *sg_len, *icum;
+  float* stage;  // [stage_cap][G * kD + 2 * G] member partials awaiting their count-in
 };
 __host__ __device__ constexpr int64_t shared_lds_ints(int64_t S, int64_t ngroups) {
   return 9 * S + 3 * (ngroups + 1) + 2;
@@ -402,6 +404,7 @@ __device__ __forceinline__ SharedLayout shared_layout(int S, int ng) {
   l.sg_ref = l.sg_count + S;
   l.sg_len = l.sg_ref + S;
   l.icum = l.sg_len + S;
+  l.stage = reinterpret_cast<float*>(l.icum + S + 1);
   return l;
 }
 
@@ -414,6 +417,7 @@ struct MemberLayout {
   int pair, mi;
   int nfr, kf_i, first_i;  // item contributions
   int npp, kf_p, first_p;  // private contributions (npp = 0: none)
+  int stage, own;          // LDS stage entry of contribution `own` (-1: none)
 };
 
 constexpr int kDefer = 128;  // member contributions waiting for their count-in
@@ -447,8 +451,10 @@ struct MergeSmem {
   // member contributions published and not yet counted in (pair indices)
   int dpair[kDefers];
   int dlast[kDefers];
+  int dstage[kDefers];  // LDS stage entry of a listed private part (-1: published)
+  int dpiece[kDefers];  // its piece index among the pair's private pieces (-1: item part)
   MemberLayout dlay[kDefers];
-  int dn;
+  int dn, nstage;
   SharedScalars ssc;
 };
 
@@ -681,6 +687,8 @@ __device__ inline MemberLayout member_layout(const Args& a, const SharedInfo& si
   m.first_i = 2 * m.kf_i + (uI != m.kf_i * si.cI ? 1 : 0);
   const int np = blocks_of(si.lens[b], si.B) - si.shb[b];
   m.npp = m.kf_p = m.first_p = 0;
+  m.stage = -1;
+  m.own = -1;
   if (np > 0) {
     const int uP = si.cum[b] * a.Hkv + kvh * (np + si.V);
     m.kf_p = uP / si.cP;
@@ -720,6 +728,13 @@ __device__ inline void member_contrib(const Args& a, const MemberLayout& m, int 
 
 constexpr int kMemberFoldU = 8;  // outputs per thread folded together at a chunk end
 
+// LDS stage entry e: a member partial's weighted-V sums [G][kD], then its
+// maxima [G] and sums [G].
+template <int G>
+__device__ __forceinline__ float* stage_entry(const Args& a, int e) {
+  return shared_layout(a.S, a.ngroups).stage + (int64_t)e * (G * kD + 2 * G);
+}
+
 // Folds the nf member pairs listed in sm.dpair / sm.dlay and writes out.
 // Each thread takes U outputs at a time and issues the loads of their
 // contributions two at a time, so that a round of folds costs one memory
@@ -756,12 +771,20 @@ __device__ inline void fold_members(const Args& a, Smem& sm, int nf) {
           vm[u][j] = -INFINITY;
           vl[u][j] = 0.f;
           if (i0 + j < E[u]) {
-            const float* o;
-            const float* ml;
-            member_contrib<G>(a, sm.dlay[pi[u]], i0 + j, o, ml);
-            vo[u][j] = ld_agent(o + g[u] * kD + d[u]);
-            vm[u][j] = ld_agent(ml + g[u] * 2);
-            vl[u][j] = ld_agent(ml + g[u] * 2 + 1);
+            const MemberLayout& m = sm.dlay[pi[u]];
+            if (m.stage >= 0 && i0 + j == m.own) {
+              const float* e = stage_entry<G>(a, m.stage);
+              vo[u][j] = e[g[u] * kD + d[u]];
+              vm[u][j] = e[G * kD + g[u]];
+              vl[u][j] = e[G * kD + G + g[u]];
+            } else {
+              const float* o;
+              const float* ml;
+              member_contrib<G>(a, m, i0 + j, o, ml);
+              vo[u][j] = ld_agent(o + g[u] * kD + d[u]);
+              vm[u][j] = ld_agent(ml + g[u] * 2);
+              vl[u][j] = ld_agent(ml + g[u] * 2 + 1);
+            }
           }
         }
       }
@@ -784,30 +807,65 @@ __device__ inline void fold_members(const Args& a, Smem& sm, int nf) {
   }
 }
 
-// Counts in every contribution listed in sm.dpair (each thread stored its
-// part of them before) and folds the pairs this workgroup completed.  All
-// threads call; the list is empty afterwards.
+// Counts in the contributions listed in sm.dpair and folds the pairs this
+// workgroup completes.  A private part still in the LDS stage first checks
+// whether every other contribution of its pair is already counted in: then
+// the workgroup folds the pair from the stage without publishing or counting
+// in (nobody else can fold it, and the counter is put back to zero);
+// otherwise it is published from the stage and counted in like the rest.
+// All threads call; the list and the stage are empty afterwards.
 template <class T, int G, int U, class Smem>
 __device__ inline void flush_members(const Args& a, Smem& sm) {
+  constexpr int kEntry = G * kD + 2 * G;
   const int n = uniform(sm.dn);  // callers come here after a barrier
   if (n == 0) return;
-  drain_vmem();     // this wave's partial stores have completed ...
-  __syncthreads();  // ... and every other wave's
   for (int i = threadIdx.x; i < n; i += kThreads) {
     const int pair = sm.dpair[i];
-    const MemberLayout m = member_layout(a, shared_info(a, sm), pair);
-    const int r = count_in(a.pcnt + pair);
-    const bool last = r == m.nfr + m.npp - 1;
-    if (last) {
-      reset_count(a.pcnt + pair);
-      acquire_counted();
+    MemberLayout m = member_layout(a, shared_info(a, sm), pair);
+    const int st = sm.dstage[i];
+    int fast = 0;
+    if (st >= 0) {
+      m.stage = st;
+      m.own = m.nfr + sm.dpiece[i];
+      fast = counted(a.pcnt + pair) == m.nfr + m.npp - 1 ? 2 : 0;
     }
-    sm.dlast[i] = last;
+    sm.dlast[i] = fast;
     sm.dlay[i] = m;
   }
   __syncthreads();
+  // publish the staged parts that do not complete their pair
+  for (int i = 0; i < n; ++i) {
+    const MemberLayout& m = sm.dlay[i];
+    if (m.stage < 0 || sm.dlast[i] != 0) continue;
+    const float* e = stage_entry<G>(a, m.stage);
+    const float* o;
+    const float* ml;
+    member_contrib<G>(a, m, m.own, o, ml);
+    for (int x = threadIdx.x; x < kEntry; x += kThreads) {
+      if (x < G * kD) {
+        st_agent(const_cast<float*>(o) + x, e[x]);
+      } else {
+        const int g = (x - G * kD) % G, which = (x - G * kD) / G;  // 0: max, 1: sum
+        st_agent(const_cast<float*>(ml) + 2 * g + which, e[x]);
+      }
+    }
+  }
+  drain_vmem();     // this wave's partial stores have completed ...
+  __syncthreads();  // ... and every other wave's
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    const MemberLayout& m = sm.dlay[i];
+    int* cnt = a.pcnt + m.pair;
+    bool fold = sm.dlast[i] == 2;
+    if (!fold) fold = count_in(cnt) == m.nfr + m.npp - 1;
+    if (fold) {
+      reset_count(cnt);
+      acquire_counted();
+    }
+    sm.dlast[i] = fold;
+  }
+  __syncthreads();
   if (threadIdx.x < 64) {
-    // keep the completed pairs, in list order (in place: a lane writes at or
+    // keep the pairs to fold, in list order (in place: a lane writes at or
     // below the entry it read, and every lane reads before any writes)
     const int lane = threadIdx.x;
     const uint64_t below = (uint64_t(1) << lane) - 1;
@@ -826,7 +884,10 @@ __device__ inline void flush_members(const Args& a, Smem& sm) {
   const int nf = sm.dn;
   if (nf > 0) fold_members<T, G, U>(a, sm, nf);
   __syncthreads();
-  if (threadIdx.x == 0) sm.dn = 0;
+  if (threadIdx.x == 0) {
+    sm.dn = 0;
+    sm.nstage = 0;
+  }
   __syncthreads();
 }
 
@@ -839,12 +900,36 @@ template <class T, int G, class Smem>
 __device__ inline void publish_member(const Args& a, Smem& sm, const Piece& pc, const Partial<G>& pt) {
   if constexpr (Smem::kDefers > 1) {
     const int pair = pc.b * a.Hkv + pc.kvh;
-    if (pc.npieces == 1)
+    const int ns = uniform(sm.nstage);
+    const bool stage = ns < a.stage_cap;
+    if (stage) {
+      float* e = stage_entry<G>(a, ns);
+#pragma unroll
+      for (int r = 0; r < Partial<G>::kOut; ++r) {
+        const int idx = threadIdx.x + r * kThreads;
+        if (idx >= G * kD) continue;
+        const int g = idx / kD, d = idx % kD;
+        e[idx] = pt.o[r];
+        if (d == 0) {
+          e[G * kD + g] = pt.m[r];
+          e[G * kD + G + g] = pt.l[r];
+        }
+      }
+    } else if (pc.npieces == 1) {
       store_rows<G>(a.pair_o + (int64_t)(2 * pair + 1) * G * kD,
                     a.pair_ml + (int64_t)(2 * pair + 1) * G * 2, pt);
-    else
+    } else {
       store_partial<G>(a, pc.slot, pt);
-    if (threadIdx.x == 0) sm.dpair[sm.dn++] = pair;
+    }
+    if (threadIdx.x == 0) {
+      const int i = sm.dn;
+      sm.dpair[i] = pair;
+      sm.dstage[i] = stage ? ns : -1;
+      sm.dpiece[i] = pc.npieces == 1 ? 0 : pc.slot / 2 - pc.kfirst;
+      sm.dn = i + 1;
+    }
+    // sm.nstage moves on after the barrier that ends finish_piece (every
+    // wave reads it above)
   }
 }
 
@@ -925,6 +1010,12 @@ __device__ inline void finish_piece(const Args& a, Smem& sm, const Piece& pc) {
     finish_late<T, G>(a, sm, pc, pt);
   }
   __syncthreads();
+  if constexpr (Smem::kDefers > 1) {
+    // the stage entry publish_member filled (if any) is taken now that
+    // every wave has read the stage count; the next reader comes after the
+    // next barrier
+    if (pc.kind == kMember && threadIdx.x == 0 && sm.nstage < a.stage_cap) ++sm.nstage;
+  }
 }
 
 // End of the chunk: fold the late piece's split if finish_late chose to

@@ -171,6 +171,29 @@ Variant pick_shared(const pa_desc* d) {
 
 size_t shared_lds(int S, int ngroups) { return (size_t)shared_lds_ints(S, ngroups) * sizeof(int); }
 
+// Member partials a shared-prefix workgroup can keep in LDS until its next
+// count-in: the most (up to the count-in list length) whose dynamic LDS
+// still lets the kernel run, found by bisection on the occupancy query and
+// cached per (kernel, LDS of the schedule).
+int stage_capacity(const Variant& v, size_t base, size_t entry) {
+  static std::mutex mu;
+  static std::unordered_map<uint64_t, int> cache;
+  const uint64_t key = (uint64_t)(uintptr_t)v.launch * 1000003u ^ (uint64_t)base * 131u ^ entry;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  int lo = 0, hi = kDefer;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (v.occ(base + (size_t)mid * entry) > 0) lo = mid; else hi = mid - 1;
+  }
+  std::lock_guard<std::mutex> lk(mu);
+  cache[key] = lo;
+  return lo;
+}
+
 // Prefill variant of a descriptor: matrix cores only (fp16 / bf16).
 PrefillFn pick_prefill(const pa_desc* d) {
   if (d->kernel == PA_KERNEL_VALU || d->dtype == PA_F32) return nullptr;
@@ -333,6 +356,7 @@ static int32_t prepare(const void* q, const void* k_pool, const void* v_pool, co
   a->ngroups = 0;
   a->pcnt = nullptr;
   a->pair_o = a->pair_ml = a->wide_o = a->wide_ml = nullptr;
+  a->stage_cap = 0;
   *grid = g;
   return PA_OK;
 }
@@ -455,7 +479,10 @@ int32_t paged_attn_decode_shared(const void* q, const void* k_pool, const void* 
   a.grp_start = group_start;
   a.grp_shared = group_shared;
   a.ngroups = num_groups;
-  if (v.launch(a, grid, shared_lds(a.S, num_groups), static_cast<hipStream_t>(stream)) !=
+  const size_t base = shared_lds(a.S, num_groups);
+  const size_t entry = sizeof(float) * (size_t)(G * kD + 2 * G);
+  a.stage_cap = stage_capacity(v, base, entry);
+  if (v.launch(a, grid, base + (size_t)a.stage_cap * entry, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return PA_ERR_LAUNCH;
   return PA_OK;

@@ -67,11 +67,11 @@ __device__ inline void block_scan(int n, F count, int* out, int* wsum) {
 
 // Virtual units charged per (sequence, KV head) in the private unit space.
 // On the serving batch a workgroup's time after its prefix items measured
-// linear in its chunk's 16-token blocks (0.27 us each) and pieces (1.95 us
+// linear in its chunk's 16-token blocks (~0.3 us each) and pieces (~2 us
 // each: the merge across the waves, the publication and the fold at the
-// chunk end), so a piece is charged 7 blocks and the equal chunks balance
-// time.
-constexpr int kPieceUnits = 7;
+// chunk end); charges of 7, 8, 10 and 13 blocks per piece measured 268,
+// 265, 266 and 269 us per call.
+constexpr int kPieceUnits = 8;
 
 // Builds the shared-prefix schedule in dynamic LDS (SharedLayout, scalars
 // in sm.ssc).  A group of M >= 2 members with shared > 0 blocks is cut into
@@ -155,15 +155,21 @@ __device__ inline void shared_prologue(const Args& a, Smem& sm, int* wsum) {
   __syncthreads();
 }
 
+// Sub-tiles in flight per wave in the item phase.  Two, as in the ordinary
+// engine, measured as fast as three (the most that fit the registers): at
+// the start of the kernel every workgroup fetches its items at once, and
+// the chip's bandwidth bounds them.
+constexpr int kItemTiles = 2;
+
 // One piece of an item: blocks [j0, j1) of sub-group sg's shared blocks,
 // KV head kvh, all its members' query heads as up to kWideCols MFMA
 // columns (two 16-column tiles when they need more than 16).  Each wave
 // owns one column tile: with two tiles, waves 0-3 hold tile 0 and waves 4-7
 // tile 1, and the two halves walk the same 16-token sub-tiles in step (the
 // second read of a sub-tile is served by the cache, so HBM sees it once);
-// with one tile all eight waves share the sub-tiles.  Two sub-tiles are in
-// flight per wave, as in the ordinary engine, and the wave partials of all
-// columns merge in LDS in one pass.  A whole item's member parts go to the
+// with one tile all eight waves share the sub-tiles.  kItemTiles sub-tiles
+// are in flight per wave, and the wave partials of all columns merge in
+// LDS in one pass.  A whole item's member parts go to the
 // pair slots (or straight to `out` for a member without private blocks); a
 // fragment cut by chunk boundaries goes to wide slot `slot` for the fold.
 // All threads call.
@@ -200,10 +206,10 @@ __device__ inline void item_piece(const Args& a, Smem& sm, const SharedInfo& si,
     const int bytes = uniform(live ? B * kD * 2 : 0);
     M::template load_tile<kCachedPolicy>(a, kvh, tok % B, phys, bytes, tile);
   };
-  Tile t0, t1;
+  Tile tl[kItemTiles];
   int t = wave % wpt;
-  load(t, t0);
-  load(t + wpt, t1);
+#pragma unroll
+  for (int k = 0; k < kItemTiles; ++k) load(t + k * wpt, tl[k]);
   // members' query heads (column c = member * G + head), zero past the
   // last, staged while the first sub-tiles are on their way
   uint4* wq = &sm.q[0][0];
@@ -285,13 +291,17 @@ __device__ inline void item_piece(const Args& a, Smem& sm, const SharedInfo& si,
       acc[x] = M::mma_pv(tl.v[x], plo, acc[x]);
     }
   };
+  // every pass refills each tile register after its compute (an empty
+  // load past the end), so the loads in flight are always in the order
+  // they are consumed
   while (t < nsub) {
-    compute(t0, tb + kSub * t, min(kSub, te - (tb + kSub * t)));
-    load(t + 2 * wpt, t0);
-    const int t1s = t + wpt;
-    if (t1s < nsub) compute(t1, tb + kSub * t1s, min(kSub, te - (tb + kSub * t1s)));
-    load(t + 3 * wpt, t1);
-    t += 2 * wpt;
+#pragma unroll
+    for (int k = 0; k < kItemTiles; ++k) {
+      const int tk = t + k * wpt;
+      if (tk < nsub) compute(tl[k], tb + kSub * tk, min(kSub, te - (tb + kSub * tk)));
+      load(tk + kItemTiles * wpt, tl[k]);
+    }
+    t += kItemTiles * wpt;
   }
 
   // wave partials -> LDS (wave w holds column tile w / wpt), then every
@@ -353,7 +363,12 @@ __device__ inline void item_piece(const Args& a, Smem& sm, const SharedInfo& si,
     if (add && whole) add = blocks_of(si.lens[b], B) != si.shb[b];
     const uint64_t am = __builtin_amdgcn_ballot_w64(add);
     const int n0 = sm.dn;
-    if (add) sm.dpair[n0 + __builtin_popcountll(am & ((uint64_t(1) << lane) - 1))] = b * a.Hkv + kvh;
+    if (add) {
+      const int i = n0 + __builtin_popcountll(am & ((uint64_t(1) << lane) - 1));
+      sm.dpair[i] = b * a.Hkv + kvh;
+      sm.dstage[i] = -1;
+      sm.dpiece[i] = -1;
+    }
     if (lane == 0) sm.dn = n0 + __builtin_popcountll(am);
   }
   __syncthreads();
@@ -392,6 +407,7 @@ __device__ inline void run_decode_shared(const Args& a) {
     sm.fold_late = 0;
     sm.early_seen = -1;
     sm.dn = 0;
+    sm.nstage = 0;
   }
   shared_prologue<B, G>(a, sm, wsum);
   const int chunk = chunk_of_wg(blockIdx.x, a.nwg);
