@@ -553,6 +553,7 @@ def block_manager_timing(w, with_cpu: bool, steps: int = 50) -> dict:
         lens += 1
     t_step = (time.perf_counter() - t0) / steps
     bm.close()
+    contended = contended_alloc_timing(NB, B)
     res = {
         "bound": "host (no device work)",
         "alloc_ns_per_block": round(statistics.median(ta) / n * 1e9, 2),
@@ -560,6 +561,7 @@ def block_manager_timing(w, with_cpu: bool, steps: int = 50) -> dict:
         "blocks_per_call": n,
         "prepare_append_us_per_step": round(t_step * 1e6, 2),
         "sequences": S,
+        "contended": contended,
     }
     if with_cpu:
         from oracle.block_manager import BlockManagerModel
@@ -571,6 +573,36 @@ def block_manager_timing(w, with_cpu: bool, steps: int = 50) -> dict:
             st, pos, cows = m.prepare_append(mt, ml)
             ml = [x + 1 for x in ml]
         res["model_prepare_append_us_per_step"] = round((time.perf_counter() - t0) / steps * 1e6, 1)
+    return res
+
+
+def contended_alloc_timing(NB: int, B: int, threads: int = 8) -> dict:
+    """The lock-free manager under contention, timed natively (Python
+    threads would measure the interpreter lock): the library's timing
+    driver runs `threads` host threads that each allocate a batch of blocks
+    with one pa_bm_alloc call and release them with one pa_bm_release
+    call, over and over, on one shared manager; reported per block
+    allocated and released, summed over all threads, beside one thread
+    alone, for 64 blocks per call (a scheduler step) and 1 block per call
+    (the worst case: every block an exchange on the shared words)."""
+    import json as _json
+    import subprocess
+
+    import paged_kv_cache_196_amd as pa
+    from paged_kv_cache_196_amd import build as pab
+
+    exe = pab.BM_CONTEND
+    if not os.path.exists(exe):
+        raise RuntimeError(f"{exe} is not built (python -m paged_kv_cache_196_amd.build)")
+    pa.load()
+    res = {}
+    for batch in (64, 1):
+        nb = max(NB, threads * batch)
+        r = subprocess.run([exe, str(threads), str(batch), "300", str(nb)], capture_output=True,
+                           text=True, timeout=60)
+        if r.returncode != 0:
+            raise RuntimeError("bm_contend failed: " + r.stdout + r.stderr)
+        res[f"batch_{batch}"] = _json.loads(r.stdout)
     return res
 
 

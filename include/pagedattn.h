@@ -432,9 +432,21 @@ int32_t paged_kv_block_scores(const void* k_pool, const void* v_pool,
  * §2.3: tables may point at the same physical blocks (shared prompts, beam
  * search); a block is copied only when a sequence diverges and writes
  * into it.  Ids come from a bump pointer (never-used blocks in id order)
- * and a LIFO free list (released blocks, most recent first), O(1) each;
- * every block counts the table entries that point at it.  Not thread-safe:
- * calls on one manager must be serialised by the caller.
+ * and a free-list stack (released blocks, most recent first), O(1) each;
+ * every block counts the table entries that point at it.
+ *
+ * Lock-free ("Paged Attention Meets FlexAttention", "What carries the
+ * argument": pages handed out in constant time without locks): any number
+ * of threads may call into one manager at once.  pa_bm_alloc and
+ * pa_bm_prepare_append stay all or nothing under concurrency (their blocks
+ * are reserved before any is taken).  What a caller must still order
+ * itself: calls that update the same table rows, and sharing or releasing
+ * a block while a concurrent pa_bm_prepare_append writes into it (forking
+ * a sequence in the middle of its own append step).  Called from one
+ * thread, every result equals that of the plain model of the tests.
+ * A call moves all of its blocks on or off the free list in one exchange,
+ * so under contention ask for a step's blocks in one call rather than one
+ * block per call.
  * ------------------------------------------------------------------ */
 
 typedef struct pa_block_manager pa_block_manager; /* opaque */

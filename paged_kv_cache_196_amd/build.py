@@ -2,7 +2,9 @@
 
 Every translation unit (the C ABI, the decode kernels per element type and
 engine, the prefill kernels per element type, the cache-write and scan
-kernels) is compiled to an object in parallel, then linked.
+kernels) is compiled to an object in parallel, then linked.  The host-only
+timing driver csrc/bm_contend.cpp (block manager under contention) is then
+built with the host compiler against the library.
 
     python -m paged_kv_cache_196_amd.build
 """
@@ -21,6 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 SOURCES = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpagedattn.so")
+BM_CONTEND = os.path.join(PKG, "bm_contend")
 OBJ_DIR = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 
@@ -80,7 +83,18 @@ def build(verbose: bool = False, extra=(), jobs: int | None = None) -> str:
     if rc != 0:
         raise RuntimeError("link failed:\n" + "\n".join(errs))
     os.replace(tmp, LIB)
+    rc, errs = _run(host_tool_command(os.path.join(CSRC, "bm_contend.cpp"), BM_CONTEND))
+    if rc != 0:
+        raise RuntimeError("bm_contend build failed:\n" + "\n".join(errs))
     return LIB
+
+
+def host_tool_command(src: str, out: str) -> list:
+    """A host program that calls the library's C entry points (no device
+    code of its own), linked to libpagedattn.so beside it."""
+    cxx = shutil.which("g++") or shutil.which("c++") or "g++"
+    return [cxx, "-O2", "-std=c++17", "-pthread", "-I", INCLUDE, src, "-o", out,
+            "-L", PKG, "-lpagedattn", "-Wl,-rpath,$ORIGIN"]
 
 
 if __name__ == "__main__":

@@ -16,6 +16,7 @@
 #include <string.h>
 #include <unordered_map>
 #include <unordered_set>
+#include <vector>
 
 #include "pagedattn.h"
 #include "block_manager.h"
@@ -627,17 +628,15 @@ int32_t pa_bm_refcount(const pa_block_manager* bm, int32_t block) {
 int32_t pa_bm_alloc(pa_block_manager* bm, int32_t n, int32_t* ids) {
   if (!bm || (n > 0 && !ids)) return PA_ERR_NULL;
   if (n < 0) return PA_ERR_SHAPE;
-  if (bm->m.num_free() < n) return PA_ERR_NOMEM;
-  for (int32_t i = 0; i < n; ++i) ids[i] = bm->m.take();
+  if (!bm->m.reserve(n)) return PA_ERR_NOMEM;
+  bm->m.take_reserved_n(n, ids);
   return PA_OK;
 }
 
 int32_t pa_bm_release(pa_block_manager* bm, const int32_t* ids, int32_t n) {
   if (!bm || (n > 0 && !ids)) return PA_ERR_NULL;
   if (n < 0) return PA_ERR_SHAPE;
-  for (int32_t i = 0; i < n; ++i)
-    if (!bm->m.drop(ids[i])) return PA_ERR_TABLE;
-  return PA_OK;
+  return bm->m.drop_n(ids, n) == n ? PA_OK : PA_ERR_TABLE;
 }
 
 int32_t pa_bm_share(pa_block_manager* bm, const int32_t* ids, int32_t n) {
@@ -656,16 +655,19 @@ int32_t pa_bm_prepare_append(pa_block_manager* bm, int32_t* bt, int32_t mbs, con
   if (num_seqs < 0 || mbs <= 0) return PA_ERR_SHAPE;
   if (num_seqs > 0 && (!bt || !lens || !pos || !cow_src || !cow_dst)) return PA_ERR_NULL;
   const int32_t B = bm->m.block_size();
-  // Pass 1: validate every sequence and count the fresh blocks the step
-  // needs (a copy of a block shared only within this batch is needed once:
-  // after the first writer copies it, the next one owns it alone).
+  // Pass 1: validate every sequence and decide what it needs (a copy of a
+  // block shared only within this batch is needed once: after the first
+  // writer copies it, the next one owns it alone); count the fresh blocks.
+  enum : uint8_t { kKeep = 0, kFresh = 1, kCopy = 2 };
+  std::vector<uint8_t> act(num_seqs > 0 ? num_seqs : 0, kKeep);
   std::unordered_map<int32_t, int32_t> drops;
-  int64_t need = 0;
+  int32_t need = 0;
   for (int32_t b = 0; b < num_seqs; ++b) {
     const int32_t L = lens[b];
     if (L < 0) continue;
     if (L / B >= mbs) return PA_ERR_TABLE;
     if (L % B == 0) {
+      act[b] = kFresh;
       ++need;
       continue;
     }
@@ -673,12 +675,19 @@ int32_t pa_bm_prepare_append(pa_block_manager* bm, int32_t* bt, int32_t mbs, con
     const int32_t rc = bm->m.refcount(e) - (drops.count(e) ? drops[e] : 0);
     if (rc <= 0) return PA_ERR_TABLE;
     if (rc > 1) {
+      act[b] = kCopy;
       ++need;
       ++drops[e];
     }
   }
-  if (need > bm->m.num_free()) return PA_ERR_NOMEM;
-  // Pass 2: apply (cannot fail).
+  // All or nothing: the fresh blocks are reserved before any is taken, and
+  // taken in one go (in the order single takes would give them: the drops
+  // below never free a block, since each drops one of several references).
+  if (!bm->m.reserve(need)) return PA_ERR_NOMEM;
+  std::vector<int32_t> fresh(need > 0 ? need : 1);
+  bm->m.take_reserved_n(need, fresh.data());
+  int32_t next = 0;
+  // Pass 2: apply the decisions (cannot fail).
   for (int32_t b = 0; b < num_seqs; ++b) {
     const int32_t L = lens[b];
     if (L < 0) {
@@ -686,10 +695,10 @@ int32_t pa_bm_prepare_append(pa_block_manager* bm, int32_t* bt, int32_t mbs, con
       continue;
     }
     int32_t* entry = bt + (int64_t)b * mbs + L / B;
-    if (L % B == 0) {
-      *entry = bm->m.take();
-    } else if (bm->m.refcount(*entry) > 1) {
-      const int32_t id = bm->m.take();
+    if (act[b] == kFresh) {
+      *entry = fresh[next++];
+    } else if (act[b] == kCopy) {
+      const int32_t id = fresh[next++];
       cow_src[*num_cow] = *entry;
       cow_dst[*num_cow] = id;
       ++*num_cow;

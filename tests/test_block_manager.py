@@ -273,3 +273,208 @@ def test_library_errors():
     assert L.pa_bm_create(0, 16) is None and L.pa_bm_create(4, 0) is None
     assert L.pa_bm_num_free(None) == -1 and L.pa_bm_refcount(None, 0) == -1
     lib.close()
+
+
+# ------------------------------------------------------ concurrency
+
+def _canonical(tables):
+    """Relabel block ids by order of first appearance (row-major), so that
+    two runs that differ only in which physical ids they drew compare equal."""
+    names = {}
+    return [[names.setdefault(x, len(names)) if x >= 0 else -1 for x in row] for row in tables]
+
+
+def _drive(m, seed, B, steps=250, width=24):
+    """One client's script of operations on its own sequences: new
+    sequences, forks (shared rows), finished sequences, decode steps over
+    all of its rows.  The script depends on statuses only, never on which
+    ids the manager hands out, so run against the library from a thread
+    (while other clients work) and against the model alone it must build
+    tables of the same sharing structure.  Returns (tables, lens, copies)."""
+    rng = np.random.default_rng(seed)
+    tables = np.zeros((0, width), np.int32)
+    lens, copies = [], 0
+    lib = not isinstance(m, bmm.BlockManagerModel)
+    for _ in range(steps):
+        op = rng.random()
+        if op < 0.2 or not lens:
+            L = int(rng.integers(1, 4 * B))
+            n = -(-L // B)
+            st, ids = m.alloc(n)
+            assert st == bmm.OK
+            row = np.full((1, width), -1, np.int32)
+            row[0, :n] = ids
+            tables = np.concatenate([tables, row])
+            lens.append(L)
+        elif op < 0.3:
+            k = int(rng.integers(len(lens)))
+            assert m.share(list(tables[k][tables[k] >= 0])) == bmm.OK
+            tables = np.concatenate([tables, tables[k: k + 1]])
+            lens.append(lens[k])
+        elif op < 0.4 and len(lens) > 1:
+            k = int(rng.integers(len(lens)))
+            assert m.release(list(tables[k][tables[k] >= 0])) == bmm.OK
+            tables = np.delete(tables, k, axis=0)
+            del lens[k]
+        else:
+            skip = [L if L < width * B - 1 and rng.random() > 0.1 else -1 for L in lens]
+            if lib:
+                tables = np.ascontiguousarray(tables)
+                st, _, cs, _ = m.prepare_append(tables, skip)
+                n_cow = len(cs)
+            else:
+                mt = [list(r) for r in tables]
+                st, _, cows = m.prepare_append(mt, skip)
+                tables = np.array(mt, np.int32).reshape(-1, width)
+                n_cow = len(cows)
+            assert st == bmm.OK
+            copies += n_cow
+            lens = [L + 1 if s >= 0 else L for L, s in zip(lens, skip)]
+    return tables, lens, copies
+
+
+def _run_threads(fn, n):
+    import threading
+    errors, out = [], [None] * n
+
+    def body(i):
+        try:
+            out[i] = fn(i)
+        except BaseException as e:  # noqa: BLE001 - reported by the main thread
+            errors.append(e)
+
+    th = [threading.Thread(target=body, args=(i,)) for i in range(n)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    if errors:
+        raise errors[0]
+    return out
+
+
+@pytest.mark.parametrize("B", [16, 1])
+def test_concurrent_clients_match_model(B):
+    """Eight threads drive one library manager at once (ctypes releases
+    the interpreter lock around each call).  Each client's tables must have
+    the sharing structure the model builds for the same script alone, no id
+    may appear in two clients' tables, and every reference count and the
+    free count must equal what the tables hold."""
+    T, NB = 8, 12000
+    lib = pa.BlockManager(NB, B)
+    res = _run_threads(lambda i: _drive(lib, 100 + i, B), T)
+    owner = {}
+    refs = np.zeros(NB, np.int64)
+    for i, (tables, lens, copies) in enumerate(res):
+        mt, ml, mc = _drive(bmm.BlockManagerModel(NB, B), 100 + i, B)
+        assert _canonical(tables.tolist()) == _canonical(mt.tolist()) and lens == ml and copies == mc, i
+        for x in tables[tables >= 0].tolist():
+            assert owner.setdefault(x, i) == i, (x, i)   # one client's block only
+            refs[x] += 1
+    assert [lib.refcount(x) for x in range(NB)] == refs.tolist()
+    assert lib.num_free() == NB - len(owner)
+    for tables, _, _ in res:
+        for row in tables:
+            assert lib.release(row[row >= 0]) == 0
+    assert lib.num_free() == NB and all(lib.refcount(x) == 0 for x in range(NB))
+    lib.close()
+
+
+def test_concurrent_exhaustion_all_or_nothing():
+    """Eight threads contend for a pool far too small for all of them:
+    every allocation either hands out all it asked for or fails with
+    PA_ERR_NOMEM and nothing, a failed decode step leaves the client's
+    table untouched, and after everything is released the pool is whole."""
+    T, NB, B, W = 8, 96, 4, 12
+
+    def client(i):
+        rng = np.random.default_rng(7 + i)
+        rows, lens, fails = [], [], 0
+        for _ in range(600):
+            op = rng.random()
+            if op < 0.35:
+                n = int(rng.integers(1, 9))
+                st, ids = lib.alloc(n)
+                assert st in (0, 10)
+                if st == 0:
+                    assert len(ids) == n and len(set(ids.tolist())) == n
+                    row = np.full(W, -1, np.int32)
+                    row[:n] = ids
+                    rows.append(row)
+                    lens.append(n * B)
+                else:
+                    assert len(ids) == 0
+                    fails += 1
+            elif op < 0.6 and rows:
+                k = int(rng.integers(len(rows)))
+                assert lib.release(rows[k][rows[k] >= 0]) == 0
+                del rows[k], lens[k]
+            elif rows:
+                t = np.ascontiguousarray(np.stack(rows))
+                before = t.copy()
+                skip = [L if L < W * B else -1 for L in lens]
+                st, pos, cs, _ = lib.prepare_append(t, skip)
+                assert st in (0, 10) and len(cs) == 0
+                if st == 0:
+                    rows = list(t)
+                    lens = [L + 1 if s >= 0 else L for L, s in zip(lens, skip)]
+                else:
+                    assert np.array_equal(t, before)
+                    fails += 1
+        return rows, fails
+
+    lib = pa.BlockManager(NB, B)
+    res = _run_threads(client, T)
+    held = [x for rows, _ in res for r in rows for x in r[r >= 0].tolist()]
+    assert len(held) == len(set(held)) and lib.num_free() == NB - len(held)
+    assert sum(f for _, f in res) > 0          # the pool really ran dry
+    for rows, _ in res:
+        for r in rows:
+            assert lib.release(r[r >= 0]) == 0
+    assert lib.num_free() == NB
+    st, ids = lib.alloc(NB)
+    assert st == 0 and sorted(ids.tolist()) == list(range(NB))
+    lib.close()
+
+
+def _sanitizer_build(tmp_path, name, flags):
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not found")
+    exe = str(tmp_path / name)
+    cmd = [gxx, "-O1", "-g", "-std=c++17", "-pthread", *flags,
+           "-I", os.path.join(ROOT, "paged_kv_cache_196_amd", "csrc"),
+           os.path.join(ROOT, "tests", "bm_stress.cpp"), "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    return exe
+
+
+@pytest.mark.parametrize("name,flags,env", [
+    ("tsan", ["-fsanitize=thread"], {"TSAN_OPTIONS": "halt_on_error=1"}),
+    ("asan", ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=all"],
+     {"ASAN_OPTIONS": "detect_leaks=1"}),
+    ("plain", ["-O2"], {}),
+])
+def test_block_manager_stress_under_sanitizers(tmp_path, name, flags, env):
+    """The block manager header compiled on the host alone (no device
+    code) into tests/bm_stress.cpp: eight threads of random allocations,
+    shares of their own and of other threads' published blocks, and
+    releases, singly and in batches, with reference counts and free counts
+    checked after every round.  ThreadSanitizer must report no data race,
+    AddressSanitizer and UBSan no invalid access, leak or undefined
+    behaviour.  The 48-block pool keeps the free list's head under constant
+    exchange: a head without its tag (ABA) hands a block out twice or links
+    the list into a cycle there, which fails the counts or the time limit."""
+    import subprocess
+    exe = _sanitizer_build(tmp_path, name, flags)
+    runs = [["1024", "8", "4", "20000"], ["48", "8", "4", "20000"]]
+    if name == "plain":
+        runs.append(["48", "8", "10", "100000"])
+    for argv in runs:
+        r = subprocess.run([exe, *argv], capture_output=True, text=True,
+                           env={**os.environ, **env}, timeout=120)
+        assert r.returncode == 0 and r.stdout.strip() == "ok", (argv, r.stdout + r.stderr)
+        assert "WARNING" not in r.stderr and "ERROR" not in r.stderr, r.stderr
