@@ -89,6 +89,39 @@ def build(verbose: bool = False, extra=(), jobs: int | None = None) -> str:
     return LIB
 
 
+def resource_usage(jobs: int | None = None) -> dict:
+    """Per-kernel resource use of every translation unit, read from the
+    compiler's resource-usage remarks (device code only; the objects go to
+    a temporary directory).  Returns {kernel symbol: {"VGPRs": n,
+    "ScratchSize": bytes per lane, "Occupancy": waves per SIMD, ...}}."""
+    import re
+    import tempfile
+
+    keys = {"VGPRs": "VGPRs", "AGPRs": "AGPRs", "TotalSGPRs": "SGPRs",
+            "ScratchSize [bytes/lane]": "ScratchSize", "Occupancy [waves/SIMD]": "Occupancy",
+            "VGPRs Spill": "VGPRSpill", "SGPRs Spill": "SGPRSpill", "LDS Size [bytes/block]": "LDS"}
+    with tempfile.TemporaryDirectory() as tmp:
+        cmds = [[hipcc(), *FLAGS, "--offload-device-only", "-Rpass-analysis=kernel-resource-usage",
+                 "-c", src, "-o", os.path.join(tmp, os.path.basename(src) + ".o")] for src in SOURCES]
+        jobs = jobs or min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
+        with ThreadPoolExecutor(jobs) as ex:
+            results = list(ex.map(lambda c: subprocess.run(c, capture_output=True, text=True), cmds))
+    usage = {}
+    for cmd, r in zip(cmds, results):
+        if r.returncode != 0:
+            raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + r.stderr[-3000:])
+        cur = None
+        for line in r.stderr.splitlines():
+            m = re.search(r"remark: Function Name: (\S+)", line)
+            if m:
+                cur = usage.setdefault(m.group(1), {})
+                continue
+            m = re.search(r"remark: +([A-Za-z][^:]*?): (\d+) \[", line)
+            if m and cur is not None and m.group(1) in keys:
+                cur[keys[m.group(1)]] = int(m.group(2))
+    return usage
+
+
 def host_tool_command(src: str, out: str) -> list:
     """A host program that calls the library's C entry points (no device
     code of its own), linked to libpagedattn.so beside it."""

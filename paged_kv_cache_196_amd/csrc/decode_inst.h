@@ -41,16 +41,26 @@ Variant make_variant() {
   return v;
 }
 
-// Group sizes built: 1, 2, 4, 8 for both engines, 16 on the matrix cores.
+// Group sizes built: 1, 2, 4, 8, 16 on the matrix cores; on the vector
+// ALU those whose registers hold without spilling (1, 2, 4 for 16-bit
+// types, 1 for fp32).  Other query groups run as virtual groups of one of
+// these (the host's plan).
 template <class T, int B, bool M>
 Variant pick_group(int G) {
+  constexpr int kMaxG = M ? 16 : T::kEsize == 4 ? 1 : 4;
   switch (G) {
     case 1: return make_variant<T, B, 1, M>();
-    case 2: return make_variant<T, B, 2, M>();
-    case 4: return make_variant<T, B, 4, M>();
-    case 8: return make_variant<T, B, 8, M>();
+    case 2:
+      if constexpr (kMaxG >= 2) return make_variant<T, B, 2, M>();
+      return Variant{};
+    case 4:
+      if constexpr (kMaxG >= 4) return make_variant<T, B, 4, M>();
+      return Variant{};
+    case 8:
+      if constexpr (kMaxG >= 8) return make_variant<T, B, 8, M>();
+      return Variant{};
     case 16:
-      if constexpr (M) return make_variant<T, B, 16, M>();
+      if constexpr (kMaxG >= 16) return make_variant<T, B, 16, M>();
       return Variant{};
     default: return Variant{};
   }

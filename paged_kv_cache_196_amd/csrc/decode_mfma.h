@@ -100,7 +100,7 @@ struct MfmaEngine {
   static __device__ __forceinline__ void load_tile(const Args& a, int kvh, int s16, int phys,
                                                    int bytes, Tile& t) {
     const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
-    const int64_t tile = ((int64_t)phys * a.Hkv + kvh) * kTileBytes;
+    const int64_t tile = ((int64_t)phys * a.Hp + pool_head(a, kvh)) * kTileBytes;
     const auto rk = tile_rsrc(a.kp, tile, bytes);
     const auto rv = tile_rsrc(a.vp, tile, bytes);
     const int koff = (col * kD + 8 * grp) * 2;    // this lane's K bytes inside a sub-tile

@@ -2,21 +2,33 @@
 //
 // Same driver as the matrix-core engine (pa_device.h streams 16-token
 // sub-tiles of each piece); this engine loads a sub-tile and folds it into a
-// wave's online-softmax state with fp32 FMAs.
+// wave's online-softmax state with fp32 arithmetic.
 //
 // Scores.  The K sub-tile (16 token rows, token-major) is read as 16-byte
 // chunks, one per lane per load: a token row spans RL lanes (RL = 16 for
 // 16-bit types, 32 for fp32), so one load covers 64/RL tokens.  Each lane
-// dots its chunk with the matching slice of every query head of the group;
-// the RL partial sums of a row are then summed by DPP row moves (and one
-// cross-row exchange for fp32), leaving the token's score in all RL lanes.
+// dots its chunk with the matching chunk of a query head (packed dot2
+// instructions with fp32 accumulation for 16-bit types, fp32 FMAs for
+// fp32); the RL partial sums of a row are then summed by DPP row moves (and
+// one cross-row exchange for fp32), leaving the token's score in all RL
+// lanes.  The heads of the group are taken one after another, so only one
+// head's scores are live at a time.
 //
 // Weighted values.  The V group of the sub-tile is stored transposed
 // (its 16 tokens of one value dimension contiguous): each 16-byte chunk
-// holds E consecutive tokens of one dimension.  The probabilities of the sub-tile go through a 16-float
-// per-wave LDS line so every lane can read the E it needs; each lane then
-// accumulates o[dim] += sum_e p_e v_e for its dimensions, and the RV lanes
-// sharing a dimension are summed once at the end of the piece.
+// holds E consecutive tokens of one dimension.  The probabilities of the
+// sub-tile go through a 16-float per-wave LDS line per head; each lane
+// converts its V chunks once, then for each head reads the E probabilities
+// it needs and accumulates o[dim] += sum_e p_e v_e for its dimensions; the
+// RV lanes sharing a dimension are summed once at the end of the piece.
+//
+// Register budget: two sub-tiles in flight, the accumulators of the group,
+// one head's query chunk, scores and probabilities, and the converted V
+// chunks (the query group stays in LDS) fit the 256 VGPRs a wave has at
+// two waves per SIMD, with nothing spilled to scratch, for groups of up to
+// 4 heads (16-bit types) or 1 head (fp32); larger groups run as several
+// virtual groups of the largest built size (the K/V tiles are then read
+// once per virtual group).
 //
 // Online softmax as in the matrix-core engine ("39 · PagedAttention", §2,
 // one softmax over all scores, kept as a running max and rescaled sums).
@@ -28,7 +40,7 @@ namespace pa {
 
 template <class T, int B, int G>
 struct ValuEngine {
-  static_assert(G >= 1 && G <= 8, "vector path holds the whole group in registers");
+  static_assert(G >= 1 && G <= (T::kEsize == 4 ? 1 : 4), "group sizes whose state fits the registers without spilling");
   static_assert(B % kSub == 0, "block size must be a multiple of 16");
   static constexpr int E = 16 / T::kEsize;  // elements per 16-byte chunk
   static constexpr int RL = kD / E;         // lanes per K row
@@ -47,7 +59,7 @@ struct ValuEngine {
     uint4 v[NV];
   };
   struct Query {
-    float f[G][E];  // this lane's slice of every query head of the group
+    int p;  // the piece whose staged query group (LDS) the sub-tiles are scored against
   };
   struct State {
     float acc[NV][G];
@@ -72,10 +84,33 @@ struct ValuEngine {
     }
   }
 
-  static __device__ __forceinline__ void load_query(const Smem& sm, int p, Query& q) {
-    const int rlane = (threadIdx.x & 63) % RL;
-#pragma unroll
-    for (int g = 0; g < G; ++g) chunk_to_float<T>(sm.q[p][g * kD / E + rlane], q.f[g]);
+  static __device__ __forceinline__ void load_query(const Smem&, int p, Query& q) { q.p = p; }
+
+  // Dot product of a query chunk and a K chunk (E elements), fp32 result.
+  static __device__ __forceinline__ float chunk_dot(const uint4& q, const uint4& k) {
+    if constexpr (T::kCode == F32::kCode) {
+      float d = __uint_as_float(q.x) * __uint_as_float(k.x);
+      d = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), d);
+      d = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), d);
+      return fmaf(__uint_as_float(q.w), __uint_as_float(k.w), d);
+    } else if constexpr (T::kCode == BF16::kCode) {
+      typedef __bf16 pair __attribute__((ext_vector_type(2)));
+      float d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(pair, q.x),
+                                                __builtin_bit_cast(pair, k.x), 0.f, false);
+      d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(pair, q.y), __builtin_bit_cast(pair, k.y), d,
+                                          false);
+      d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(pair, q.z), __builtin_bit_cast(pair, k.z), d,
+                                          false);
+      return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(pair, q.w), __builtin_bit_cast(pair, k.w),
+                                             d, false);
+    } else {
+      typedef _Float16 pair __attribute__((ext_vector_type(2)));
+      float d = __builtin_amdgcn_fdot2(__builtin_bit_cast(pair, q.x), __builtin_bit_cast(pair, k.x), 0.f,
+                                       false);
+      d = __builtin_amdgcn_fdot2(__builtin_bit_cast(pair, q.y), __builtin_bit_cast(pair, k.y), d, false);
+      d = __builtin_amdgcn_fdot2(__builtin_bit_cast(pair, q.z), __builtin_bit_cast(pair, k.z), d, false);
+      return __builtin_amdgcn_fdot2(__builtin_bit_cast(pair, q.w), __builtin_bit_cast(pair, k.w), d, false);
+    }
   }
 
   // The sub-tile starting at slot s16 of physical block `phys`, KV head kvh.
@@ -83,7 +118,7 @@ struct ValuEngine {
   static __device__ __forceinline__ void load_tile(const Args& a, int kvh, int s16, int phys,
                                                    int bytes, Tile& t) {
     const int lane = threadIdx.x & 63, rlane = lane % RL, vlane = lane % RV;
-    const int64_t tile = ((int64_t)phys * a.Hkv + kvh) * kTileBytes;
+    const int64_t tile = ((int64_t)phys * a.Hp + pool_head(a, kvh)) * kTileBytes;
     const auto rk = tile_rsrc(a.kp, tile, bytes);
     const auto rv = tile_rsrc(a.vp, tile, bytes);
     const int koff = ((lane / RL) * kD + rlane * E) * T::kEsize;    // K bytes of load 0
@@ -102,26 +137,18 @@ struct ValuEngine {
                                                  Tile& t, int valid) {
     const int lane = threadIdx.x & 63, rlane = lane % RL, vlane = lane % RV;
     const int wave = uniform(threadIdx.x >> 6);
-    float x[NK][G];
-#pragma unroll
-    for (int n = 0; n < NK; ++n) {
-      float kf[E];
-      chunk_to_float<T>(t.k[n], kf);
-      const bool ok = n * TPL + lane / RL < valid;
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) d = fmaf(q.f[g][e], kf[e], d);
-        d = row_sum(d);
-        x[n][g] = ok ? d * a.scale_log2 : -INFINITY;
-      }
-    }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float bm = x[0][g];
+      const uint4 qc = sm.q[q.p][g * kD / E + rlane];  // this lane's chunk of head g
+      float x[NK];
 #pragma unroll
-      for (int n = 1; n < NK; ++n) bm = fmaxf(bm, x[n][g]);
+      for (int n = 0; n < NK; ++n) {
+        const float d = row_sum(chunk_dot(qc, t.k[n]));
+        x[n] = n * TPL + lane / RL < valid ? d * a.scale_log2 : -INFINITY;
+      }
+      float bm = x[0];
+#pragma unroll
+      for (int n = 1; n < NK; ++n) bm = fmaxf(bm, x[n]);
       if constexpr (RL == 16) bm = max_xor16(bm);
       bm = max_xor32(bm);
       const float mn = fmaxf(st.m[g], bm);
@@ -130,41 +157,39 @@ struct ValuEngine {
       float ps = 0.f;
 #pragma unroll
       for (int n = 0; n < NK; ++n) {
-        x[n][g] = fast_exp2(x[n][g] - mn);
-        ps += x[n][g];
+        x[n] = fast_exp2(x[n] - mn);
+        ps += x[n];
       }
       st.lsum[g] = st.lsum[g] * alpha + ps;
 #pragma unroll
       for (int n = 0; n < NV; ++n) st.acc[n][g] *= alpha;
-    }
-    // Probabilities to the wave's LDS line: one lane per token row writes.
-    if (rlane == 0) {
+      // this head's probabilities to the wave's LDS line: one lane per token row writes
+      if (rlane == 0) {
 #pragma unroll
-      for (int n = 0; n < NK; ++n)
-#pragma unroll
-        for (int g = 0; g < G; ++g) sm.p[wave][g][n * TPL + lane / RL] = x[n][g];
+        for (int n = 0; n < NK; ++n) sm.p[wave][g][n * TPL + lane / RL] = x[n];
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float pw[G][E];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int e = 0; e < E; ++e) pw[g][e] = sm.p[wave][g][vlane * E + e];
-    const bool tail = valid < kSub;
+    float vf[NV][E];
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
-      float vf[E];
-      chunk_to_float<T>(t.v[n], vf);
-      if (tail) {
+      chunk_to_float<T>(t.v[n], vf[n]);
+      if (valid < kSub) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) vf[e] = (vlane * E + e < valid) ? vf[e] : 0.f;
+        for (int e = 0; e < E; ++e) vf[n][e] = (vlane * E + e < valid) ? vf[n][e] : 0.f;
       }
+    }
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g) {
+      float pw[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) st.acc[n][g] = fmaf(pw[g][e], vf[e], st.acc[n][g]);
+      for (int e = 0; e < E; ++e) pw[e] = sm.p[wave][g][vlane * E + e];
+#pragma unroll
+      for (int n = 0; n < NV; ++n)
+#pragma unroll
+        for (int e = 0; e < E; ++e) st.acc[n][g] = fmaf(pw[e], vf[n][e], st.acc[n][g]);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();

@@ -49,6 +49,7 @@ struct PrefillArgs {
   void* out;           // [total_q][Hq][kD]
   float scale_log2;
   int32_t S, Hq, Hkv, mbs, tiles, out_f32;  // tiles: column tiles per (sequence, KV head)
+  int32_t Hp, kv_split, kv_shift;           // virtual KV heads, as in the decode arguments
 };
 
 constexpr int kPrefillTiles = 3;  // 16-column tiles per wave: they share every K/V load (3: two waves per SIMD)

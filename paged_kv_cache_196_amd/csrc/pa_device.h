@@ -44,6 +44,11 @@ struct Args {
   int* counters;  // [kMaxGrid] pieces finished per split (sequence, KV head)
   float scale_log2;  // scale * log2(e): scores are kept in base-2 exponent units
   int32_t S, Hq, Hkv, mbs, nwg, out_f32;
+  // Virtual KV heads: a query group of split * G heads runs as `split`
+  // groups of G, one per virtual KV head; Hkv counts virtual heads, Hp the
+  // pool's heads, and virtual head v reads pool head v / split (shift =
+  // log2(split) when a power of two, else -1).
+  int32_t Hp, kv_split, kv_shift;
   int32_t cached_blocks;  // leading logical blocks read with the cache-retaining policy
   // Prefix groups (shared-prefix calls only; ngroups = 0 otherwise).
   const int32_t* grp_start;   // [ngroups + 1] group i = sequences grp_start[i] .. grp_start[i+1]-1
@@ -56,6 +61,12 @@ struct Args {
   float* wide_ml;  // [2*kMaxGrid][kWideCols][2]
   int32_t stage_cap;  // member partials the workgroup's LDS can hold until its next count-in
 };
+
+// Pool KV head of virtual KV head kvh (the K/V tiles it reads).
+template <class A>
+__device__ __forceinline__ int pool_head(const A& a, int kvh) {
+  return a.kv_shift >= 0 ? kvh >> a.kv_shift : kvh / a.kv_split;
+}
 
 // ------------------------------------------------------------ conversions
 

@@ -32,8 +32,7 @@ inline bool use_mfma(const pa_desc* d) {
   return d->dtype != PA_F32;
 }
 
-Variant pick(const pa_desc* d) {
-  const int G = d->num_q_heads / d->num_kv_heads;
+Variant decode_variant(const pa_desc* d, int G) {
   const int B = d->block_size;
   const bool mf = use_mfma(d);
   switch (d->dtype) {
@@ -42,6 +41,40 @@ Variant pick(const pa_desc* d) {
     case PA_BF16: return mf ? decode_variant_bf16_mfma(B, G) : decode_variant_bf16_valu(B, G);
     default: return Variant{};
   }
+}
+
+// How a descriptor's query group runs: the kernel for group size G and
+// `split` = (query heads per KV head) / G virtual KV heads per pool head.
+// G is the largest built size that divides the query group, so a group
+// the kernels hold directly runs as one (split = 1); a larger one (MQA's
+// 32 or 64 heads on one KV head, 8 on the vector ALU) runs as several
+// virtual groups that each read the K/V tiles of their pool head.
+struct Plan {
+  Variant v;
+  int G = 0, split = 1, shift = 0;
+  int hkv = 0;  // virtual KV heads: num_kv_heads * split
+};
+
+template <class Get>
+Plan make_plan(const pa_desc* d, Get get) {
+  Plan p;
+  const int group = d->num_q_heads / d->num_kv_heads;
+  for (int g = 16; g >= 1; g /= 2) {
+    if (group % g != 0) continue;
+    const Variant v = get(g);
+    if (!v.launch) continue;
+    p.v = v;
+    p.G = g;
+    p.split = group / g;
+    p.shift = (p.split & (p.split - 1)) == 0 ? __builtin_ctz((unsigned)p.split) : -1;
+    p.hkv = d->num_kv_heads * p.split;
+    return p;
+  }
+  return p;
+}
+
+Plan plan_decode(const pa_desc* d) {
+  return make_plan(d, [d](int g) { return decode_variant(d, g); });
 }
 
 // Per-device facts queried once.
@@ -136,7 +169,9 @@ SharedWs shared_ws_layout(const pa_desc* d) {
   const size_t pairs = (size_t)d->num_seqs * d->num_kv_heads;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   SharedWs w;
-  size_t off = al(ws_layout_bytes(kMaxGrid, 2 * kMaxGrid, (int)G));
+  // the leading part also serves the plain decode these calls fall back to
+  const int g_plain = plan_decode(d).G;
+  size_t off = al(ws_layout_bytes(kMaxGrid, 2 * kMaxGrid, std::max((int)G, g_plain)));
   w.pcnt = off;
   off = al(off + sizeof(int) * pairs);
   w.pair_o = off;
@@ -161,7 +196,8 @@ void bind_shared_workspace(Args* a, void* ws, const SharedWs& w) {
 }
 
 // The shared-prefix kernel of a descriptor: matrix cores (fp16 / bf16, kernel
-// AUTO or MFMA); an empty Variant otherwise.
+// AUTO or MFMA), for query groups it holds directly (1, 2, 4 or 8 heads per
+// KV head, no virtual split); an empty Variant otherwise.
 Variant pick_shared(const pa_desc* d) {
   if (!use_mfma(d)) return Variant{};
   const int G = d->num_q_heads / d->num_kv_heads;
@@ -195,12 +231,29 @@ int stage_capacity(const Variant& v, size_t base, size_t entry) {
   return lo;
 }
 
-// Prefill variant of a descriptor: matrix cores only (fp16 / bf16).
-PrefillFn pick_prefill(const pa_desc* d) {
-  if (d->kernel == PA_KERNEL_VALU || d->dtype == PA_F32) return nullptr;
-  const int G = d->num_q_heads / d->num_kv_heads;
-  return d->dtype == PA_BF16 ? prefill_variant_bf16(d->block_size, G)
-                             : prefill_variant_f16(d->block_size, G);
+// Prefill plan of a descriptor: matrix cores only (fp16 / bf16), query
+// groups as in the decode plan.
+struct PrefillPlan {
+  PrefillFn fn = nullptr;
+  int G = 0, split = 1, shift = 0;
+};
+
+PrefillPlan plan_prefill(const pa_desc* d) {
+  PrefillPlan p;
+  if (d->kernel == PA_KERNEL_VALU || d->dtype == PA_F32) return p;
+  const int group = d->num_q_heads / d->num_kv_heads;
+  for (int g = 16; g >= 1; g /= 2) {
+    if (group % g != 0) continue;
+    const PrefillFn fn = d->dtype == PA_BF16 ? prefill_variant_bf16(d->block_size, g)
+                                             : prefill_variant_f16(d->block_size, g);
+    if (!fn) continue;
+    p.fn = fn;
+    p.G = g;
+    p.split = group / g;
+    p.shift = (p.split & (p.split - 1)) == 0 ? __builtin_ctz((unsigned)p.split) : -1;
+    return p;
+  }
+  return p;
 }
 
 }  // namespace pa
@@ -257,10 +310,11 @@ int32_t pa_check_desc(const pa_desc* d) {
   if (d->kernel < PA_KERNEL_AUTO || d->kernel > PA_KERNEL_MFMA) return PA_ERR_UNSUPPORTED;
   if (d->kernel == PA_KERNEL_MFMA && d->dtype == PA_F32) return PA_ERR_UNSUPPORTED;
   if (d->num_seqs > kMaxSeqs) return PA_ERR_UNSUPPORTED;
+  const Plan p = plan_decode(d);
+  if (!p.v.launch) return PA_ERR_UNSUPPORTED;
   // flat unit indices are int32
-  if ((int64_t)d->num_seqs * d->max_blocks_per_seq * d->num_kv_heads >= ((int64_t)1 << 31))
+  if ((int64_t)d->num_seqs * d->max_blocks_per_seq * p.hkv >= ((int64_t)1 << 31))
     return PA_ERR_UNSUPPORTED;
-  if (!pick(d).launch) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 
@@ -289,7 +343,7 @@ int64_t pa_v_elem_offset(const pa_desc* d, int32_t block, int32_t kv_head, int32
 
 size_t pa_workspace_bytes(const pa_desc* d) {
   if (pa_check_desc(d) != PA_OK) return 0;
-  return ws_layout_bytes(kMaxGrid, 2 * kMaxGrid, d->num_q_heads / d->num_kv_heads);
+  return ws_layout_bytes(kMaxGrid, 2 * kMaxGrid, plan_decode(d).G);
 }
 
 int32_t pa_validate_host(const pa_desc* d, const int32_t* bt, const int32_t* lens) {
@@ -312,7 +366,7 @@ int32_t pa_decode_grid(const pa_desc* d) {
   if (pa_check_desc(d) != PA_OK) return -1;
   const DeviceInfo info = device_info();
   if (!info.ok) return -1;
-  const Variant v = pick(d);
+  const Variant v = plan_decode(d).v;
   const int per_cu = v.occ(prefix_lds(d->num_seqs));
   if (per_cu <= 0) return -1;  // the workgroup's LDS does not fit a CU
   int grid = info.cus * per_cu;
@@ -345,9 +399,13 @@ static int32_t prepare(const void* q, const void* k_pool, const void* v_pool, co
   a->lens = lens;
   a->out = out;
   a->scale_log2 = scale * kLog2e;
+  const Plan p = plan_decode(d);
   a->S = d->num_seqs;
   a->Hq = d->num_q_heads;
-  a->Hkv = d->num_kv_heads;
+  a->Hkv = p.hkv;
+  a->Hp = d->num_kv_heads;
+  a->kv_split = p.split;
+  a->kv_shift = p.shift;
   a->mbs = d->max_blocks_per_seq;
   a->nwg = g;
   a->out_f32 = d->out_dtype == PA_F32 ? 1 : 0;
@@ -370,9 +428,9 @@ int32_t paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
   const int32_t st = prepare(q, k_pool, v_pool, bt, lens, scale, out, d, true, ws, ws_bytes, &a,
                              &grid);
   if (st != PA_OK || grid == 0) return st;
-  bind_workspace(&a, ws, kMaxGrid, 2 * kMaxGrid, d->num_q_heads / d->num_kv_heads);
-  const Variant v = pick(d);
-  if (v.launch(a, grid, prefix_lds(a.S), static_cast<hipStream_t>(stream)) != hipSuccess)
+  const Plan p = plan_decode(d);
+  bind_workspace(&a, ws, kMaxGrid, 2 * kMaxGrid, p.G);
+  if (p.v.launch(a, grid, prefix_lds(a.S), static_cast<hipStream_t>(stream)) != hipSuccess)
     return PA_ERR_LAUNCH;
   return PA_OK;
 }
@@ -385,7 +443,8 @@ int32_t paged_attn_decode_noalloc(const void* q, const void* k_pool, const void*
   const int32_t st = prepare(q, k_pool, v_pool, bt, lens, scale, out, d, false, nullptr, 0, &a,
                              &grid);
   if (st != PA_OK || grid == 0) return st;
-  const int G = d->num_q_heads / d->num_kv_heads;
+  const Plan p = plan_decode(d);
+  const int G = p.G;
   if (ws_layout_bytes(grid, 2 * grid, G) > kScratchBytes) return PA_ERR_SCRATCH;
   void* ws = scratch_ptr();
   if (!ws) return PA_ERR_DEVICE;
@@ -395,8 +454,7 @@ int32_t paged_attn_decode_noalloc(const void* q, const void* k_pool, const void*
   // so the pair of launches can also be captured into a graph)
   hipLaunchKernelGGL(clear_ints_kernel, dim3(1), dim3(256), 0, s, a.counters, grid);
   if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
-  const Variant v = pick(d);
-  if (v.launch(a, grid, prefix_lds(a.S), s) != hipSuccess) return PA_ERR_LAUNCH;
+  if (p.v.launch(a, grid, prefix_lds(a.S), s) != hipSuccess) return PA_ERR_LAUNCH;
   return PA_OK;
 }
 
@@ -731,16 +789,16 @@ int32_t paged_attn_prefill(const void* q, const void* k_pool, const void* v_pool
   const int32_t st = pa_check_desc(d);
   if (st != PA_OK) return st;
   if (max_q_len < 0) return PA_ERR_SHAPE;
-  const PrefillFn launch = pick_prefill(d);
-  if (!launch) return PA_ERR_UNSUPPORTED;
+  const PrefillPlan pp = plan_prefill(d);
+  if (!pp.fn) return PA_ERR_UNSUPPORTED;
   if (d->num_seqs == 0 || max_q_len == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !bt || !lens || !q_start || !out) return PA_ERR_NULL;
   if (((uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool | (uintptr_t)out) & 15u) return PA_ERR_ALIGN;
   if (!device_info().ok) return PA_ERR_DEVICE;
-  const int G = d->num_q_heads / d->num_kv_heads;
-  const int rows_per_wave = kSub / G * kPrefillTiles;
+  const int rows_per_wave = kSub / pp.G * kPrefillTiles;
   const int64_t tiles = (max_q_len + rows_per_wave - 1) / rows_per_wave;
-  const int64_t items = tiles * d->num_kv_heads * d->num_seqs;
+  const int64_t hkv = (int64_t)d->num_kv_heads * pp.split;  // virtual KV heads
+  const int64_t items = tiles * hkv * d->num_seqs;
   if (items >= ((int64_t)1 << 31) - kAuxWaves) return PA_ERR_UNSUPPORTED;
   PrefillArgs a;
   a.q = q;
@@ -753,12 +811,15 @@ int32_t paged_attn_prefill(const void* q, const void* k_pool, const void* v_pool
   a.scale_log2 = scale * kLog2e;
   a.S = d->num_seqs;
   a.Hq = d->num_q_heads;
-  a.Hkv = d->num_kv_heads;
+  a.Hkv = (int32_t)hkv;
+  a.Hp = d->num_kv_heads;
+  a.kv_split = pp.split;
+  a.kv_shift = pp.shift;
   a.mbs = d->max_blocks_per_seq;
   a.tiles = (int32_t)tiles;
   a.out_f32 = d->out_dtype == PA_F32 ? 1 : 0;
   const dim3 grid((unsigned)((items + kAuxWaves - 1) / kAuxWaves));
-  launch(a, grid, static_cast<hipStream_t>(stream));
+  pp.fn(a, grid, static_cast<hipStream_t>(stream));
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

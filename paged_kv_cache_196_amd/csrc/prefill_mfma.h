@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kAuxThreads) void prefill_kernel(PrefillArgs a) {
   for (int j = 0; j < nsub; ++j) {
     const int tok0 = j * kSub;
     const int phys = row_bt[tok0 / B];
-    const int64_t tile = ((int64_t)phys * a.Hkv + kvh) * kTileBytes;
+    const int64_t tile = ((int64_t)phys * a.Hp + pool_head(a, kvh)) * kTileBytes;
     const auto rk = tile_rsrc(a.kp, tile, kTileBytes);
     const auto rv = tile_rsrc(a.vp, tile, kTileBytes);
     const int soff = (tok0 % B) * kD * 2;

@@ -89,7 +89,7 @@ def _desc(**kw):
     ("num_q_heads", 0, 2), ("num_kv_heads", 3, 2), ("num_seqs", -1, 2), ("block_size", 0, 2),
     ("num_blocks", 0, 2), ("max_blocks_per_seq", 0, 2), ("dtype", 5, 3), ("out_dtype", pa.PA_F16, 3),
     ("head_dim", 64, 4), ("block_size", 8, 4), ("block_size", 48, 4), ("kernel", 9, 4),
-    ("num_q_heads", 8 * 32, 4), ("num_seqs", 9000, 4), ("cached_prefix_blocks", -1, 2),
+    ("max_blocks_per_seq", 1 << 26, 4), ("num_seqs", 9000, 4), ("cached_prefix_blocks", -1, 2),
 ])
 def test_descriptor_errors(lib, field, value, code):
     assert pa.pa_check_desc(_desc()) == 0
@@ -109,8 +109,32 @@ def test_descriptor_fields_match_the_header():
 def test_mfma_with_fp32_is_unsupported(lib):
     assert pa.pa_check_desc(_desc(dtype=pa.PA_F32, kernel=pa.PA_KERNEL_MFMA)) == 4
     assert pa.pa_check_desc(_desc(dtype=pa.PA_F32, kernel=pa.PA_KERNEL_VALU)) == 0
-    assert pa.pa_check_desc(_desc(num_q_heads=128, num_kv_heads=8, kernel=pa.PA_KERNEL_VALU)) == 4
-    assert pa.pa_check_desc(_desc(num_q_heads=128, num_kv_heads=8, kernel=pa.PA_KERNEL_MFMA)) == 0
+
+
+def test_every_query_group_is_planned(lib):
+    """Any number of query heads per KV head is accepted: a group the
+    kernels hold directly (1-16 heads on the matrix cores; 1, 2, 4 on the
+    vector ALU for 16-bit types, 1 for fp32) runs as one, a larger or odd
+    one as virtual groups of the largest built size dividing it.  The
+    workspace is sized by that kernel group, which pins the plan."""
+    def ws(G, **kw):
+        d = _desc(num_q_heads=2 * G, num_kv_heads=2, **kw)
+        assert pa.pa_check_desc(d) == 0, (G, kw)
+        return pa.pa_workspace_bytes(d)
+    for kernel in (pa.PA_KERNEL_AUTO, pa.PA_KERNEL_MFMA, pa.PA_KERNEL_VALU):
+        for G in (1, 2, 3, 4, 5, 6, 8, 12, 16, 24, 32, 64):
+            ws(G, kernel=kernel)
+    per_head = ws(2) - ws(1)                       # one more head per kernel group
+    assert per_head > 0 and ws(4) - ws(1) == 3 * per_head
+    mf = pa.PA_KERNEL_MFMA
+    assert ws(64, kernel=mf) == ws(32, kernel=mf) == ws(16, kernel=mf) == ws(1) + 15 * per_head
+    assert ws(12, kernel=mf) == ws(4, kernel=mf) and ws(24, kernel=mf) == ws(8, kernel=mf)
+    assert ws(3, kernel=mf) == ws(5, kernel=mf) == ws(1)
+    va = pa.PA_KERNEL_VALU
+    assert ws(8, kernel=va) == ws(16, kernel=va) == ws(4, kernel=va) == ws(1) + 3 * per_head
+    assert ws(6, kernel=va) == ws(2, kernel=va)
+    for G in (2, 4, 8):
+        assert ws(G, dtype=pa.PA_F32, kernel=va) == ws(1)
 
 
 @pytest.mark.parametrize("B", [16, 32])

@@ -65,12 +65,12 @@ EDGE_LENS = [1, 2, 15, 16, 17, 31, 32, 33, 47, 48, 63, 64, 65, 127, 129, 255, 30
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("B", [16, 32])
-@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 6, 8, 12, 16, 32, 64])
 def test_ragged_edges(O, dtype, B, G):
     """Lengths around block and sub-tile boundaries, empty sequences and a
-    sequence filling its whole table row, for each group size."""
-    if dtype == "f32" and G == 16:
-        pytest.skip("group 16 is built for the matrix-core kernel only")
+    sequence filling its whole table row, for each group size: those the
+    kernels hold directly and those that run as virtual groups (odd sizes,
+    MQA-sized groups, groups beyond the vector ALU's registers)."""
     rng = np.random.default_rng(1000 + B + G)
     lens = list(EDGE_LENS) + [0, 0]
     rng.shuffle(lens)
@@ -83,10 +83,26 @@ def test_ragged_edges(O, dtype, B, G):
     ref = O.run_workload(w)
     up = Uploaded(w)
     for kern in kernels_for(dtype):
-        if kern == "valu" and G == 16:
-            continue
         err = max_err(up.run(kern), ref)
         assert err <= TOL[dtype], (dtype, B, G, kern, err)
+
+
+@pytest.mark.parametrize("Hq", [32, 64])
+def test_mqa_full_size(O, Hq):
+    """Multi-query decode at full size (512 sequences of 512-8192 tokens,
+    one KV head shared by all Hq query heads): every output of every kernel
+    against the oracle."""
+    w = workload.make_mqa(Hq)
+    _log(f"[parity] {w.name}: oracle")
+    ref = O.run_workload(w)
+    up = Uploaded(w)
+    for kern in ["auto"] + kernels_for(w.dtype):
+        _log(f"[parity] {w.name} kernel={kern}")
+        err = max_err(up.run(kern), ref)
+        _log(f"[parity] {w.name} kernel={kern} max_abs_err={err:.3e}")
+        assert err <= TOL[w.dtype], (Hq, kern, err)
+    del up
+    torch.cuda.empty_cache()
 
 
 def test_single_sequence_single_token(O):

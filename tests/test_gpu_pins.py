@@ -47,8 +47,6 @@ def test_block_size_16_and_32_agree(O, G):
     assert np.array_equal(O.run_workload(w32), ref)
     a, b = Uploaded(w16), Uploaded(w32)
     for kern in kernels_for("bf16"):
-        if kern == "valu" and G == 16:
-            continue
         _log(f"[pins] block size 16 vs 32, G={G} kernel={kern}")
         assert max_err(a.run(kern), ref) <= TOL["bf16"], (kern, 16)
         assert max_err(b.run(kern), ref) <= TOL["bf16"], (kern, 32)
@@ -95,8 +93,6 @@ def test_single_token_returns_its_value_row_exactly(G):
         want[b] = np.repeat(to_f32(V[0], w.dtype), G, axis=0)
     up = Uploaded(w)
     for kern in kernels_for(w.dtype):
-        if kern == "valu" and G == 16:
-            continue
         got = up.run(kern).cpu().numpy()
         assert np.array_equal(got, want), kern
 

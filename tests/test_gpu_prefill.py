@@ -50,7 +50,7 @@ LENS = [1, 2, 15, 16, 17, 33, 64, 65, 129, 300, 511]
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("B", [16, 32])
-@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 8, 16, 32, 64])
 def test_prefill_ragged(O, dtype, B, G):
     """Whole prompts, chunks, single rows and empty query sets over lengths
     around block and sub-tile boundaries, for each group size."""

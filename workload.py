@@ -311,6 +311,30 @@ def make(cfg: int, seed: int | None = None, *, batch: int | None = None,
     raise ValueError(f"unknown config {cfg}")
 
 
+def mqa_name(num_q_heads: int, batch: int = 512) -> str:
+    return f"mqa-b{batch}-h{num_q_heads}kv1-bf16-b16"
+
+
+def make_mqa(num_q_heads: int, seed: int | None = None, *, batch: int | None = None,
+             max_len: int | None = None) -> Workload:
+    """Multi-query decode ("PagedAttention: The Cache Was Storing Nothing",
+    §3.1: every query head shares one key head and one value head): the
+    GQA decode workload's length distribution (uniform in [512, 8192],
+    bf16, block size 16, head_dim 128, shuffled blocks, q/K/V ~ N(0, 1)) on
+    one KV head with num_q_heads query heads (32 or 64), and 512 sequences,
+    so that the (sequence, KV head) count and the K/V bytes match the GQA
+    workload's 64 sequences x 8 KV heads."""
+    seed = 30 + num_q_heads if seed is None else seed
+    rng_len = _streams(seed)[0]
+    S = batch or 512
+    lens = rng_len.integers(512, 8192, size=S, endpoint=True)
+    if max_len:
+        lens = np.minimum(lens, max_len)
+    return build(name=mqa_name(num_q_heads, S), dtype="bf16", seq_lens=lens,
+                 num_q_heads=num_q_heads, num_kv_heads=1, head_dim=128, block_size=16, seed=seed,
+                 max_blocks_per_seq=512)
+
+
 def kv_bytes_per_token(num_kv_heads: int, head_dim: int, esize: int, layers: int = 1) -> int:
     """K and V bytes one token occupies: 2 x KV heads x head dim x layers x
     element bytes ("PagedAttention: The Cache Was Storing Nothing", §3)."""
