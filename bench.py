@@ -725,9 +725,9 @@ def main() -> int:
                          "shared block read once per sequence) instead of paged_attn_decode_shared")
     ap.add_argument("--no-prefix-hint", action="store_true",
                     help="with --no-prefix-groups: no shared-prefix cache hint either")
-    ap.add_argument("--other-workloads", default="3,4",
-                    help="comma-separated workloads timed after the headline one as sub-entries "
-                         "('' for none)")
+    ap.add_argument("--other-workloads", default="3,4,mqa64",
+                    help="comma-separated workloads timed after the headline one as sub-entries: "
+                         "config numbers, or mqa32 / mqa64 for the multi-query decode ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the oracle check")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -828,17 +828,17 @@ def main() -> int:
             "ms_per_step", "kv_gbps", "hbm_frac", "tokens_per_s", "roofline")}
         result["without_prefix_groups"]["entry_point"] = plain["config"]["entry_point"]
         result["without_prefix_groups"]["cached_prefix_blocks"] = plain["config"]["cached_prefix_blocks"]
-    others = [int(x) for x in args.other_workloads.split(",") if x.strip()]
+    others = [x.strip() for x in args.other_workloads.split(",") if x.strip()]
     subs = {}
     for wid in others:
-        if wid == args.workload:
+        if wid == str(args.workload):
             continue
-        wo = workload.make(wid)
+        wo = workload.make_mqa(int(wid[3:])) if wid.startswith("mqa") else workload.make(int(wid))
         leg = decode_leg(wo, args, dev, flush, stream, O, shared, args.steps, args.warmup)
-        subs[str(wid)] = {k: leg[k] for k in (
+        subs[wid] = {k: leg[k] for k in (
             "workload", "dtype", "ms_per_step", "kv_gbps", "hbm_frac", "tokens_per_s", "kv_bytes",
             "roofline", "max_abs_err_vs_oracle", "ms")}
-        subs[str(wid)]["decode_grid"] = leg["config"]["decode_grid"]
+        subs[wid]["decode_grid"] = leg["config"]["decode_grid"]
         del wo
     if subs:
         result["workloads"] = subs

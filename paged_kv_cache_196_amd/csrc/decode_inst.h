@@ -41,7 +41,8 @@ Variant make_variant() {
   return v;
 }
 
-// Group sizes built: 1, 2, 4, 8, 16 on the matrix cores; on the vector
+// Group sizes built: 1, 2, 4, 8, 16 on the matrix cores, and 32, 64 as
+// column-split groups (MQA); on the vector
 // ALU those whose registers hold without spilling (1, 2, 4 for 16-bit
 // types, 1 for fp32).  Other query groups run as virtual groups of one of
 // these (the host's plan).
@@ -61,6 +62,12 @@ Variant pick_group(int G) {
       return Variant{};
     case 16:
       if constexpr (kMaxG >= 16) return make_variant<T, B, 16, M>();
+      return Variant{};
+    case 32:
+      if constexpr (M) return make_variant<T, B, 32, M>();
+      return Variant{};
+    case 64:
+      if constexpr (M) return make_variant<T, B, 64, M>();
       return Variant{};
     default: return Variant{};
   }

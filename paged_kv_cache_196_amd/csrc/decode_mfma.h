@@ -10,14 +10,16 @@
 //       4 x v_mfma_f32_16x16x32_{bf16,f16}; A = K rows straight from the
 //       token-major K tile, B = the query group (loaded once per piece).
 //   O^T[128 dims][16 heads] += V^T[128][16 tok] . P^T[16 tok][16 heads]
-//       8 dim tiles x v_mfma_f32_16x16x16_{bf16,f16}; A = the V group of
+//       8 dim tiles x v_mfma_f32_16x16x32_{bf16,f16}; A = the V group of
 //       the sub-tile, stored transposed ([128][16]) and read as-is, B = P^T,
 //       which is exactly the C-layout of S^T, so the probabilities never
 //       leave their registers.
 // P is fed as hi + lo halves (p = hi + lo, both in the input type), so
 // the weighted sum keeps ~16 mantissa bits instead of the 8 (bf16) or 11
 // (fp16) one rounding would leave; this keeps the result within the fp32
-// accumulation budget.
+// accumulation budget.  Both halves go through one 32-deep product per dim
+// tile (each lane's 4 tokens appear twice along K: once against hi, once
+// against lo), at the instruction rate of one 16-deep product.
 //
 // MFMA operand layouts used (wave64, 16x16 tiles; lane = 16*grp + col):
 //   A (16 x K): lane holds row `col`, K elements grp*k..grp*k+k-1 (k = K/4)
@@ -40,10 +42,12 @@ namespace pa {
 template <class T, int B, int G, bool kWide = false>
 struct MfmaEngine {
   static_assert(T::kEsize == 2, "matrix-core path takes fp16 / bf16");
-  static_assert(G >= 1 && G <= 16, "query group padded to 16 MFMA columns");
+  static_assert((G >= 1 && G <= 16) || G == 32 || G == 64,
+                "query group padded to 16 MFMA columns, or split into column tiles of 16");
   static_assert(B % kSub == 0, "block size must be a multiple of 16");
 
   using Smem = MergeSmem<T, G, kWide>;
+  static constexpr int NT = kTilesPerWave<G>;  // 16-column tiles each sub-tile is scored against
   using Op8 = typename std::conditional<T::kCode == BF16::kCode, bf16x8, f16x8>::type;
   using Op4 = typename std::conditional<T::kCode == BF16::kCode, bf16x4, f16x4>::type;
   using Elem = typename std::conditional<T::kCode == BF16::kCode, __bf16, _Float16>::type;
@@ -54,12 +58,12 @@ struct MfmaEngine {
     uint2 v[8];  // V^T: dim 16x + col, tokens 4grp .. 4grp+3   (x = 0..7)
   };
   struct Query {
-    uint4 op[4];  // B operand of the score product: head `col`, dims 32x + 8grp .. +8
+    uint4 op[NT][4];  // B operand of column tile t: head `col` of t, dims 32x + 8grp .. +8
   };
   struct State {
-    f32x4 acc[8];  // O^T tile x: dims 16x + 4grp .. +4 of head `col`
-    float m;       // running max of head `col` (base-2 units)
-    float lsum;    // this lane's share of the running sum of 2^(s - m)
+    f32x4 acc[NT][8];  // O^T tile x of column tile t: dims 16x + 4grp .. +4 of its head `col`
+    float m[NT];       // running max of that head (base-2 units)
+    float lsum[NT];    // this lane's share of the running sum of 2^(s - m)
   };
 
   static __device__ __forceinline__ f32x4 mma_qk(const uint4& k, const uint4& q, f32x4 c) {
@@ -71,28 +75,44 @@ struct MfmaEngine {
       return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
 
-  static __device__ __forceinline__ f32x4 mma_pv(const uint2& v, const Op4& p, f32x4 c) {
-    const Op4 a = __builtin_bit_cast(Op4, v);
+  // c += V^T . (P_hi + P_lo)^T for one 16-dim tile in a single 32-deep
+  // product: the lane's 8 K elements are its 4 tokens twice, paired with
+  // the hi probabilities in the first four and the lo ones in the last four
+  // (A = the V chunk repeated, B = phi then plo).
+  static __device__ __forceinline__ f32x4 mma_pv2(const uint2& v, const Op4& phi, const Op4& plo,
+                                                  f32x4 c) {
+    const Op8 a = __builtin_bit_cast(Op8, make_uint4(v.x, v.y, v.x, v.y));
+    const uint2 h = __builtin_bit_cast(uint2, phi), l = __builtin_bit_cast(uint2, plo);
+    const Op8 b = __builtin_bit_cast(Op8, make_uint4(h.x, h.y, l.x, l.y));
     if constexpr (T::kCode == BF16::kCode)
-      return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, p, c, 0, 0, 0);
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     else
-      return __builtin_amdgcn_mfma_f32_16x16x16f16(a, p, c, 0, 0, 0);
+      return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
 
   static __device__ __forceinline__ void reset(State& st) {
 #pragma unroll
-    for (int x = 0; x < 8; ++x) st.acc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-    st.m = -INFINITY;
-    st.lsum = 0.f;
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int x = 0; x < 8; ++x) st.acc[t][x] = f32x4{0.f, 0.f, 0.f, 0.f};
+      st.m[t] = -INFINITY;
+      st.lsum[t] = 0.f;
+    }
   }
 
-  // Query group of piece p from its LDS staging (zero columns >= G).
+  // Query group of piece p from its LDS staging (zero columns >= G); a
+  // wave of column group c takes heads 32c + 16t + col of its tiles t.
   static __device__ __forceinline__ void load_query(const Smem& sm, int p, Query& q) {
     const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
-    const int c0 = (col * kD + 8 * grp) * 2 / 16;  // 16-byte chunk of dims 8grp.. of head col
+    const int base = kColGroups<G> > 1 ? (int)(threadIdx.x >> 6) / kColWaves<G> * 32 : 0;
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
-      q.op[x] = col < G ? sm.q[p][c0 + 4 * x] : make_uint4(0, 0, 0, 0);
+    for (int t = 0; t < NT; ++t) {
+      const int head = base + 16 * t + col;
+      const int c0 = (head * kD + 8 * grp) * 2 / 16;  // 16-byte chunk of dims 8grp.. of the head
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        q.op[t][x] = head < G ? sm.q[p][c0 + 4 * x] : make_uint4(0, 0, 0, 0);
+    }
   }
 
   // The sub-tile starting at slot s16 of physical block `phys`, KV head kvh.
@@ -116,34 +136,37 @@ struct MfmaEngine {
   static __device__ __forceinline__ void compute(const Args& a, Smem&, const Query& q, State& st,
                                                  Tile& t, int valid) {
     const int lane = threadIdx.x & 63, grp = lane >> 4;
-    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+    Op4 phi[NT], plo[NT];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) s = mma_qk(t.k[x], q.op[x], s);
-    float xr[4];
+    for (int ct = 0; ct < NT; ++ct) {
+      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) xr[r] = (4 * grp + r < valid) ? s[r] * a.scale_log2 : -INFINITY;
-    float bm = fmaxf(fmaxf(xr[0], xr[1]), fmaxf(xr[2], xr[3]));
-    bm = max_xor16(bm);
-    bm = max_xor32(bm);
-    const float mn = fmaxf(st.m, bm);
-    if (wave_any(mn > st.m)) {
-      // The max grew somewhere in the wave: rescale sums and accumulators
-      // (alpha = 1 in lanes whose max did not move).
-      const float alpha = fast_exp2(st.m - mn);
-      st.lsum *= alpha;
+      for (int x = 0; x < 4; ++x) s = mma_qk(t.k[x], q.op[ct][x], s);
+      float xr[4];
 #pragma unroll
-      for (int x = 0; x < 8; ++x) st.acc[x] *= alpha;
-      st.m = mn;
-    }
-    float p[4];
+      for (int r = 0; r < 4; ++r) xr[r] = (4 * grp + r < valid) ? s[r] * a.scale_log2 : -INFINITY;
+      float bm = fmaxf(fmaxf(xr[0], xr[1]), fmaxf(xr[2], xr[3]));
+      bm = max_xor16(bm);
+      bm = max_xor32(bm);
+      const float mn = fmaxf(st.m[ct], bm);
+      if (wave_any(mn > st.m[ct])) {
+        // The max grew somewhere in the wave: rescale sums and accumulators
+        // (alpha = 1 in lanes whose max did not move).
+        const float alpha = fast_exp2(st.m[ct] - mn);
+        st.lsum[ct] *= alpha;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(xr[r] - st.m);
-    st.lsum += (p[0] + p[1]) + (p[2] + p[3]);
-    Op4 phi, plo;
+        for (int x = 0; x < 8; ++x) st.acc[ct][x] *= alpha;
+        st.m[ct] = mn;
+      }
+      float p[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      phi[r] = (Elem)p[r];
-      plo[r] = (Elem)(p[r] - (float)phi[r]);
+      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(xr[r] - st.m[ct]);
+      st.lsum[ct] += (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        phi[ct][r] = (Elem)p[r];
+        plo[ct][r] = (Elem)(p[r] - (float)phi[ct][r]);
+      }
     }
     if (valid < kSub) {
       // Slots past the sequence end may hold anything (NaN included):
@@ -159,22 +182,26 @@ struct MfmaEngine {
     }
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
-      st.acc[x] = mma_pv(t.v[x], phi, st.acc[x]);
-      st.acc[x] = mma_pv(t.v[x], plo, st.acc[x]);
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) {
+        st.acc[ct][x] = mma_pv2(t.v[x], phi[ct], plo[ct], st.acc[ct][x]);
+      }
     }
   }
 
-  // Wave partial -> LDS (lsum summed over the 4 row groups of each column).
-  static __device__ __forceinline__ void to_lds(Smem& sm, const State& st, int wave) {
+  // Wave partial of column tile `t` -> LDS (lsum summed over the 4 row
+  // groups of each column); a column-split group writes the tile's 16
+  // heads at columns 0..15, one tile per merge round.
+  static __device__ __forceinline__ void to_lds(Smem& sm, const State& st, int wave, int t = 0) {
     const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
-    float lsum = sum_xor16(st.lsum);
+    float lsum = sum_xor16(st.lsum[t]);
     lsum = sum_xor32(lsum);
     if (col < G) {
 #pragma unroll
       for (int x = 0; x < 8; ++x)
-        *reinterpret_cast<f32x4*>(&sm.o[wave][col][16 * x + 4 * grp]) = st.acc[x];
+        *reinterpret_cast<f32x4*>(&sm.o[wave][col][16 * x + 4 * grp]) = st.acc[t][x];
       if (grp == 0) {
-        sm.m[wave][col] = st.m;
+        sm.m[wave][col] = st.m[t];
         sm.l[wave][col] = lsum;
       }
     }

@@ -342,6 +342,22 @@ __device__ __forceinline__ Piece uniform_piece(const Piece& p) {
 constexpr int kQueryLdsBytes = 32768;
 constexpr int kFoldLoads = 64;  // workspace loads per thread in flight when folding a split
 
+// Query groups wider than one MFMA column tile (MQA: 32 or 64 heads on one
+// KV head): every wave scores each K/V sub-tile it loads against two
+// column tiles of 16 heads (32 heads), and the waves form G / 32 column
+// groups of kColWaves waves; a group takes its 32 heads and deals the
+// sub-tiles among its own waves.  Two groups (64 heads) read the same
+// sub-tiles at about the same time, so each is fetched from HBM once.
+// Merging goes through the 16-column wave arrays one column tile (round)
+// at a time.
+template <int G>
+constexpr int kTilesPerWave = G > 16 ? 2 : 1;
+template <int G>
+constexpr int kColGroups = G > 16 ? G / 32 : 1;
+template <int G>
+constexpr int kColWaves = kWaves / kColGroups<G>;
+static_assert(kColGroups<64> <= kWaves, "one wave at least per column group");
+
 // Pieces listed per batch: their query groups are staged in LDS together.
 template <class T, int G>
 constexpr int piece_batch() {
@@ -356,7 +372,10 @@ constexpr int piece_batch() {
 template <int G>
 struct Partial {
   static constexpr int kOut = (G * kD + kThreads - 1) / kThreads;
-  static constexpr int kPer = kFoldLoads / kOut < 32 ? kFoldLoads / kOut : 32;  // pieces per fold round
+  // pieces per fold round (half the loads in flight for column-split
+  // groups, whose many outputs per thread would not fit the registers)
+  static constexpr int kLoads = G > 16 ? kFoldLoads / 2 : kFoldLoads;
+  static constexpr int kPer = kLoads / kOut < 32 ? kLoads / kOut : 32;
   float m[kOut], l[kOut], o[kOut];
 };
 
@@ -439,8 +458,9 @@ struct MergeSmem {
   static constexpr int kFoldMl = Partial<G>::kPer * G;
   // the wide (prefix item) phase: every wave holds 16 columns of `o` and
   // the (max, sum) of its columns among all kWideCols in m / l
-  static constexpr int kOCols = kWide && G < 16 ? 16 : G;
-  static constexpr int kMCols = kWide && G < kWideCols ? kWideCols : G;
+  // a column-split group: every wave holds the 16 columns of its tile
+  static constexpr int kOCols = (kWide && G < 16) || G > 16 ? 16 : G;
+  static constexpr int kMCols = kWide && G < kWideCols ? kWideCols : (G > 16 ? 16 : G);
   static constexpr int kDefers = kWide ? kDefer : 1;
   float o[kWaves][kOCols][kD + 4];
   float m[kWaves][kMCols];
@@ -467,6 +487,12 @@ struct MergeSmem {
   MemberLayout dlay[kDefers];
   int dn, nstage;
   SharedScalars ssc;
+  // The workgroup's own partial of a late piece (all G heads), kept in the
+  // wave-partial arrays (free by then) with its heads laid out flat.
+  __device__ float& own_o(int g, int d) { return (&o[0][0][0])[g * (kD + 4) + d]; }
+  __device__ float& own_m(int g) { return (&m[0][0])[g]; }
+  __device__ float& own_l(int g) { return (&l[0][0])[g]; }
+  static_assert(kWaves * kOCols >= G && kWaves * kMCols >= G, "own partial fits the wave arrays");
 };
 
 // The shared-prefix schedule of this call (see SharedInfo).
@@ -541,6 +567,24 @@ __device__ __forceinline__ void drain_vmem() {
 
 // Merge the kWaves wave partials the waves left in `sm` into this thread's
 // outputs.  Callers synchronise before (waves wrote sm) and after.
+// Merge of output (g, d) over waves w0 .. w0 + W - 1, whose partials of
+// the head sit at column gl of the wave arrays.
+template <int W, class Smem>
+__device__ __forceinline__ void merge_output(const Smem& sm, int w0, int gl, int d, float& M,
+                                             float& l, float& o) {
+  M = sm.m[w0][gl];
+#pragma unroll
+  for (int w = 1; w < W; ++w) M = fmaxf(M, sm.m[w0 + w][gl]);
+  o = 0.f;
+  l = 0.f;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    const float f = rescale(sm.m[w0 + w][gl], M);
+    o += f * sm.o[w0 + w][gl][d];
+    l += f * sm.l[w0 + w][gl];
+  }
+}
+
 template <class T, int G, class Smem>
 __device__ inline void merge_waves(const Smem& sm, Partial<G>& pt) {
 #pragma unroll
@@ -550,20 +594,7 @@ __device__ inline void merge_waves(const Smem& sm, Partial<G>& pt) {
     pt.l[r] = 0.f;
     pt.o[r] = 0.f;
     if (idx >= G * kD) continue;
-    const int g = idx / kD, d = idx % kD;
-    float M = sm.m[0][g];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm.m[w][g]);
-    float o = 0.f, l = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = rescale(sm.m[w][g], M);
-      o += f * sm.o[w][g][d];
-      l += f * sm.l[w][g];
-    }
-    pt.m[r] = M;
-    pt.l[r] = l;
-    pt.o[r] = o;
+    merge_output<kWaves>(sm, 0, idx / kD, idx % kD, pt.m[r], pt.l[r], pt.o[r]);
   }
 }
 
@@ -641,8 +672,8 @@ __device__ inline void fold_split(const Args& a, Smem& sm, const Piece& pc,
       const int slot = slot_of(p0 + e / G), g = e % G;
       const float* ml = a.ws_ml + ((int64_t)slot * G + g) * 2;
       const bool mine = slot == own_slot;
-      sm.pm[e] = mine ? sm.m[0][g] : ld_agent(ml);
-      sm.pl[e] = mine ? sm.l[0][g] : ld_agent(ml + 1);
+      sm.pm[e] = mine ? sm.own_m(g) : ld_agent(ml);
+      sm.pl[e] = mine ? sm.own_l(g) : ld_agent(ml + 1);
     }
     __syncthreads();
 #pragma unroll
@@ -959,7 +990,7 @@ __device__ inline void finish_late(const Args& a, Smem& sm, const Piece& pc,
   bool fold = uniform(sm.seen) == pc.npieces - 1;
   if (fold) {
     if (threadIdx.x == 0) reset_count(cnt);
-    // merge_waves of every wave reads sm.m[0] / sm.l[0], overwritten below
+    // merge_waves of every wave reads the wave arrays, overwritten below
     __syncthreads();
   } else {
     store_partial<G>(a, pc.slot, pt);
@@ -980,16 +1011,81 @@ __device__ inline void finish_late(const Args& a, Smem& sm, const Piece& pc,
     const int idx = threadIdx.x + r * kThreads;
     if (idx >= G * kD) continue;
     const int g = idx / kD, d = idx % kD;
-    sm.o[0][g][d] = pt.o[r];
+    sm.own_o(g, d) = pt.o[r];
     if (d == 0) {
-      sm.m[0][g] = pt.m[r];
-      sm.l[0][g] = pt.l[r];
+      sm.own_m(g) = pt.m[r];
+      sm.own_l(g) = pt.l[r];
     }
   }
   if (threadIdx.x == 0) {
     sm.late = pc;
     sm.fold_late = 1;
   }
+}
+
+// finish_piece for a column-split group (two column tiles per wave): the
+// wave partials go through the 16-column wave arrays one column tile per
+// round (Engine::to_lds of that round), and each output of the round is
+// merged and emitted on its own (out for a whole piece, the piece's
+// workspace slot otherwise), so only a few are live in registers while
+// the next sub-tiles are in flight.  A late piece always publishes its
+// partial; when this workgroup completes its split, the fold at the end of
+// the chunk reads every piece, its own included, from the workspace.  All
+// threads call; thread 0 has set sm.seen.
+template <class T, int G, class Engine, class Smem, class State>
+__device__ inline void finish_piece_rounds(const Args& a, Smem& sm, const Piece& pc,
+                                           const State& st, int wave) {
+  constexpr int W = kColWaves<G>;
+  constexpr int kPerRound = kColGroups<G> * 16 * kD;  // outputs of one round
+  static_assert(kPerRound % kThreads == 0, "every thread owns the same number of outputs");
+  const bool whole = pc.kind == kWhole;
+  float* const o_base = a.ws_o + (int64_t)pc.slot * G * kD;
+  float* const ml_base = a.ws_ml + (int64_t)pc.slot * G * 2;
+#pragma unroll
+  for (int round = 0; round < kTilesPerWave<G>; ++round) {
+    __syncthreads();  // the wave arrays are free (the previous round's merges are done)
+    Engine::to_lds(sm, st, wave, round);
+    __syncthreads();
+#pragma unroll 2
+    for (int r = 0; r < kPerRound / kThreads; ++r) {
+      const int idx = threadIdx.x + r * kThreads;
+      const int cg = idx / (16 * kD), c = idx / kD % 16, d = idx % kD;
+      const int g = cg * 32 + round * 16 + c;
+      float M, l, o;
+      merge_output<W>(sm, cg * W, c, d, M, l, o);
+      if (whole) {
+        store_out<T>(a.out, ((int64_t)pc.b * a.Hq + pc.kvh * G + g) * kD + d, o / l, a.out_f32);
+      } else {
+        st_agent(o_base + (int64_t)g * kD + d, o);
+        if (d == 0) {
+          st_agent(ml_base + (int64_t)g * 2 + 0, M);
+          st_agent(ml_base + (int64_t)g * 2 + 1, l);
+        }
+      }
+    }
+  }
+  if (!whole) {
+    drain_vmem();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int* cnt = a.counters + pc.kfirst;
+      if (pc.kind == kEarly) {
+        sm.early_seen = count_in(cnt);
+        sm.early = pc;
+      } else {
+        // the last arrival folds: either every other piece was already
+        // counted in when the stream began this one, or this count-in is
+        // the last
+        const bool last = sm.seen == pc.npieces - 1 || count_in(cnt) == pc.npieces - 1;
+        if (last) {
+          reset_count(cnt);
+          sm.late = pc;
+          sm.fold_late = 1;
+        }
+      }
+    }
+  }
+  __syncthreads();
 }
 
 // Emit a piece after its waves wrote their partials to LDS (to_lds) and
@@ -1043,15 +1139,22 @@ __device__ inline void finish_chunk(const Args& a, Smem& sm) {
   if (uniform(sm.fold_late)) {
     const Piece pc = uniform_piece(sm.late);
     Partial<G> own;
+    if constexpr (kTilesPerWave<G> > 1) {
+      // column-split groups published their own partial too: read every piece
 #pragma unroll
-    for (int r = 0; r < Partial<G>::kOut; ++r) {
-      const int idx = min(threadIdx.x + r * kThreads, G * kD - 1);
-      const int g = idx / kD, d = idx % kD;
-      own.m[r] = sm.m[0][g];
-      own.l[r] = sm.l[0][g];
-      own.o[r] = sm.o[0][g][d];
+      for (int r = 0; r < Partial<G>::kOut; ++r) own.m[r] = own.l[r] = own.o[r] = 0.f;
+      fold_split<T, G>(a, sm, pc, own, -1);
+    } else {
+#pragma unroll
+      for (int r = 0; r < Partial<G>::kOut; ++r) {
+        const int idx = min(threadIdx.x + r * kThreads, G * kD - 1);
+        const int g = idx / kD, d = idx % kD;
+        own.m[r] = sm.own_m(g);
+        own.l[r] = sm.own_l(g);
+        own.o[r] = sm.own_o(g, d);
+      }
+      fold_split<T, G>(a, sm, pc, own, pc.slot);
     }
-    fold_split<T, G>(a, sm, pc, own, pc.slot);
   }
   if (uniform(sm.flag)) {
     const Piece pc = uniform_piece(sm.early);
@@ -1143,11 +1246,14 @@ __device__ inline void stream_batch(const Args& a, typename Engine::Smem& sm) {
       c.te = uniform(sm.plist[c.p].tok_end);
     }
   };
+  // The waves of a column group deal the sub-tiles among themselves (all
+  // kWaves waves when the group is one column tile).
+  constexpr int kStride = kColWaves<G>;
   auto advance = [&](Cur& c) {
-    c.j += kWaves;
+    c.j += kStride;
     if (c.j >= c.n) settle(c);
   };
-  Cur c{0, wave, 0, 0, 0, 0, 0};
+  Cur c{0, wave % kStride, 0, 0, 0, 0, 0};
   settle(c);
 
   int cur = 0;  // piece whose state the wave holds
@@ -1163,9 +1269,14 @@ __device__ inline void stream_batch(const Args& a, typename Engine::Smem& sm) {
     do {
       const Piece pc = uniform_piece(sm.plist[cur]);
       const int seen = last ? split_seen(a, pc) : -1;
-      Engine::to_lds(sm, st, wave);
-      if (threadIdx.x == 0) sm.seen = seen;
-      finish_piece<T, G>(a, sm, pc);
+      if constexpr (kTilesPerWave<G> > 1) {
+        if (threadIdx.x == 0) sm.seen = seen;
+        finish_piece_rounds<T, G, Engine>(a, sm, pc, st, wave);
+      } else {
+        Engine::to_lds(sm, st, wave);
+        if (threadIdx.x == 0) sm.seen = seen;
+        finish_piece<T, G>(a, sm, pc);
+      }
       Engine::reset(st);
     } while (++cur < p);
     if (p < npl) Engine::load_query(sm, p, q);
@@ -1187,7 +1298,8 @@ __device__ inline void stream_batch(const Args& a, typename Engine::Smem& sm) {
       const int tok = uniform(u.tb + kSub * u.j), kvh = uniform(u.kvh);
       phys = uniform(phys);
       const int bytes = uniform(live ? B * kD * T::kEsize : 0);
-      if (tok / B < a.cached_blocks)
+      // column groups re-read each other's sub-tiles: keep them cached
+      if (kColGroups<G> > 1 || tok / B < a.cached_blocks)
         Engine::template load_tile<kCachedPolicy>(a, kvh, tok % B, phys, bytes, t);
       else
         Engine::template load_tile<kStreamPolicy>(a, kvh, tok % B, phys, bytes, t);

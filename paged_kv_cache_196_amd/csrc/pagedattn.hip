@@ -56,10 +56,10 @@ struct Plan {
 };
 
 template <class Get>
-Plan make_plan(const pa_desc* d, Get get) {
+Plan make_plan(const pa_desc* d, Get get, int max_g) {
   Plan p;
   const int group = d->num_q_heads / d->num_kv_heads;
-  for (int g = 16; g >= 1; g /= 2) {
+  for (int g = max_g; g >= 1; g /= 2) {
     if (group % g != 0) continue;
     const Variant v = get(g);
     if (!v.launch) continue;
@@ -73,8 +73,10 @@ Plan make_plan(const pa_desc* d, Get get) {
   return p;
 }
 
-Plan plan_decode(const pa_desc* d) {
-  return make_plan(d, [d](int g) { return decode_variant(d, g); });
+// max_g caps the kernel group (a power of two), e.g. to bound the
+// workspace a group's partials take.
+Plan plan_decode(const pa_desc* d, int max_g = 64) {
+  return make_plan(d, [d](int g) { return decode_variant(d, g); }, max_g);
 }
 
 // Per-device facts queried once.
@@ -362,16 +364,19 @@ int32_t pa_validate_host(const pa_desc* d, const int32_t* bt, const int32_t* len
   return PA_OK;
 }
 
-int32_t pa_decode_grid(const pa_desc* d) {
-  if (pa_check_desc(d) != PA_OK) return -1;
+// Workgroups of a decode launch with plan p: every CU filled to the
+// kernel's occupancy, at most kMaxGrid; -1 if no workgroup fits a CU.
+static int plan_grid(const Plan& p, int S) {
   const DeviceInfo info = device_info();
   if (!info.ok) return -1;
-  const Variant v = plan_decode(d).v;
-  const int per_cu = v.occ(prefix_lds(d->num_seqs));
+  const int per_cu = p.v.occ(prefix_lds(S));
   if (per_cu <= 0) return -1;  // the workgroup's LDS does not fit a CU
-  int grid = info.cus * per_cu;
-  if (grid > kMaxGrid) grid = kMaxGrid;
-  return grid;
+  return std::min(info.cus * per_cu, kMaxGrid);
+}
+
+int32_t pa_decode_grid(const pa_desc* d) {
+  if (pa_check_desc(d) != PA_OK) return -1;
+  return plan_grid(plan_decode(d), d->num_seqs);
 }
 
 // Checks the call (a caller workspace too when check_ws) and fills every
@@ -380,7 +385,8 @@ int32_t pa_decode_grid(const pa_desc* d) {
 // *grid = 0: nothing to launch.
 static int32_t prepare(const void* q, const void* k_pool, const void* v_pool, const int32_t* bt,
                        const int32_t* lens, float scale, void* out, const pa_desc* d,
-                       bool check_ws, const void* ws, size_t ws_bytes, Args* a, int* grid) {
+                       const Plan& p, bool check_ws, const void* ws, size_t ws_bytes, Args* a,
+                       int* grid) {
   const int32_t st = pa_check_desc(d);
   if (st != PA_OK) return st;
   *grid = 0;
@@ -390,7 +396,7 @@ static int32_t prepare(const void* q, const void* k_pool, const void* v_pool, co
   if (check_ws && (!ws || ws_bytes < pa_workspace_bytes(d) || ((uintptr_t)ws & 15u)))
     return PA_ERR_WORKSPACE;
   if (!device_info().ok) return PA_ERR_DEVICE;
-  const int g = pa_decode_grid(d);
+  const int g = plan_grid(p, d->num_seqs);
   if (g <= 0) return PA_ERR_UNSUPPORTED;  // LDS of this batch size and group does not fit
   a->q = q;
   a->kp = k_pool;
@@ -399,7 +405,6 @@ static int32_t prepare(const void* q, const void* k_pool, const void* v_pool, co
   a->lens = lens;
   a->out = out;
   a->scale_log2 = scale * kLog2e;
-  const Plan p = plan_decode(d);
   a->S = d->num_seqs;
   a->Hq = d->num_q_heads;
   a->Hkv = p.hkv;
@@ -425,10 +430,12 @@ int32_t paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
                           const pa_desc* d, void* ws, size_t ws_bytes, void* stream) {
   Args a;
   int grid = 0;
-  const int32_t st = prepare(q, k_pool, v_pool, bt, lens, scale, out, d, true, ws, ws_bytes, &a,
-                             &grid);
-  if (st != PA_OK || grid == 0) return st;
+  const int32_t st0 = pa_check_desc(d);
+  if (st0 != PA_OK) return st0;
   const Plan p = plan_decode(d);
+  const int32_t st = prepare(q, k_pool, v_pool, bt, lens, scale, out, d, p, true, ws, ws_bytes,
+                             &a, &grid);
+  if (st != PA_OK || grid == 0) return st;
   bind_workspace(&a, ws, kMaxGrid, 2 * kMaxGrid, p.G);
   if (p.v.launch(a, grid, prefix_lds(a.S), static_cast<hipStream_t>(stream)) != hipSuccess)
     return PA_ERR_LAUNCH;
@@ -440,10 +447,18 @@ int32_t paged_attn_decode_noalloc(const void* q, const void* k_pool, const void*
                                   const pa_desc* d, void* stream) {
   Args a;
   int grid = 0;
-  const int32_t st = prepare(q, k_pool, v_pool, bt, lens, scale, out, d, false, nullptr, 0, &a,
-                             &grid);
+  const int32_t st0 = pa_check_desc(d);
+  if (st0 != PA_OK) return st0;
+  // A column-split group whose partials would overflow the static scratch
+  // runs as virtual groups of 16 heads instead.
+  Plan p = plan_decode(d);
+  if (p.G > 16) {
+    const int g = plan_grid(p, d->num_seqs);
+    if (g > 0 && ws_layout_bytes(g, 2 * g, p.G) > kScratchBytes) p = plan_decode(d, 16);
+  }
+  const int32_t st = prepare(q, k_pool, v_pool, bt, lens, scale, out, d, p, false, nullptr, 0,
+                             &a, &grid);
   if (st != PA_OK || grid == 0) return st;
-  const Plan p = plan_decode(d);
   const int G = p.G;
   if (ws_layout_bytes(grid, 2 * grid, G) > kScratchBytes) return PA_ERR_SCRATCH;
   void* ws = scratch_ptr();
@@ -526,8 +541,9 @@ int32_t paged_attn_decode_shared(const void* q, const void* k_pool, const void* 
     return paged_attn_decode(q, k_pool, v_pool, bt, lens, scale, out, d, ws, ws_bytes, stream);
   Args a;
   int grid = 0;
-  const int32_t st = prepare(q, k_pool, v_pool, bt, lens, scale, out, d, true, ws, ws_bytes, &a,
-                             &grid);
+  // the shared kernel's groups are held directly (split 1), as in the plain plan
+  const int32_t st = prepare(q, k_pool, v_pool, bt, lens, scale, out, d, plan_decode(d), true, ws,
+                             ws_bytes, &a, &grid);
   if (st != PA_OK || grid == 0) return st;
   grid = pa_decode_shared_grid(d, num_groups);
   if (grid <= 0) return PA_ERR_UNSUPPORTED;  // LDS of this batch and its groups does not fit

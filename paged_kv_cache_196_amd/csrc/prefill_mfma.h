@@ -21,7 +21,7 @@
 // token 0 up to its largest position; every loaded sub-tile serves all of
 // its column tiles:
 //   S^T[16 tok][16 cols] = K[16][128] . Q^T[128][16]   4 x mfma 16x16x32
-//   O^T[128][16 cols]   += V^T[128][16] . P^T[16][16]  8 dim tiles x 2 x mfma 16x16x16
+//   O^T[128][16 cols]   += V^T[128][16] . P^T[16][16]  8 dim tiles x mfma 16x16x32 (hi + lo P)
 // (operand layouts and the hi + lo split of P as in the decode engine), with
 // a running max and sum per column.  The waves of one (b, KV head) read the
 // same K/V tiles, through L2 (cached load policy).  Waves with later rows
@@ -150,8 +150,7 @@ __global__ __launch_bounds__(kAuxThreads) void prefill_kernel(PrefillArgs a) {
       }
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
-        acc[t][x] = M::mma_pv(v[x], phi, acc[t][x]);
-        acc[t][x] = M::mma_pv(v[x], plo, acc[t][x]);
+        acc[t][x] = M::mma_pv2(v[x], phi, plo, acc[t][x]);
       }
     }
   }

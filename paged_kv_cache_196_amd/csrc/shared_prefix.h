@@ -287,8 +287,7 @@ __device__ inline void item_piece(const Args& a, Smem& sm, const SharedInfo& si,
     }
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
-      acc[x] = M::mma_pv(tl.v[x], phi, acc[x]);
-      acc[x] = M::mma_pv(tl.v[x], plo, acc[x]);
+      acc[x] = M::mma_pv2(tl.v[x], phi, plo, acc[x]);
     }
   };
   // every pass refills each tile register after its compute (an empty

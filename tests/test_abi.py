@@ -113,8 +113,8 @@ def test_mfma_with_fp32_is_unsupported(lib):
 
 def test_every_query_group_is_planned(lib):
     """Any number of query heads per KV head is accepted: a group the
-    kernels hold directly (1-16 heads on the matrix cores; 1, 2, 4 on the
-    vector ALU for 16-bit types, 1 for fp32) runs as one, a larger or odd
+    kernels hold directly (1-16, 32 and 64 heads on the matrix cores; 1, 2,
+    4 on the vector ALU for 16-bit types, 1 for fp32) runs as one, a larger or odd
     one as virtual groups of the largest built size dividing it.  The
     workspace is sized by that kernel group, which pins the plan."""
     def ws(G, **kw):
@@ -122,12 +122,15 @@ def test_every_query_group_is_planned(lib):
         assert pa.pa_check_desc(d) == 0, (G, kw)
         return pa.pa_workspace_bytes(d)
     for kernel in (pa.PA_KERNEL_AUTO, pa.PA_KERNEL_MFMA, pa.PA_KERNEL_VALU):
-        for G in (1, 2, 3, 4, 5, 6, 8, 12, 16, 24, 32, 64):
+        for G in (1, 2, 3, 4, 5, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128):
             ws(G, kernel=kernel)
     per_head = ws(2) - ws(1)                       # one more head per kernel group
     assert per_head > 0 and ws(4) - ws(1) == 3 * per_head
     mf = pa.PA_KERNEL_MFMA
-    assert ws(64, kernel=mf) == ws(32, kernel=mf) == ws(16, kernel=mf) == ws(1) + 15 * per_head
+    assert ws(16, kernel=mf) == ws(1) + 15 * per_head
+    assert ws(32, kernel=mf) == ws(1) + 31 * per_head and ws(64, kernel=mf) == ws(1) + 63 * per_head
+    assert ws(128, kernel=mf) == ws(64, kernel=mf) and ws(96, kernel=mf) == ws(32, kernel=mf)
+    assert ws(48, kernel=mf) == ws(16, kernel=mf)
     assert ws(12, kernel=mf) == ws(4, kernel=mf) and ws(24, kernel=mf) == ws(8, kernel=mf)
     assert ws(3, kernel=mf) == ws(5, kernel=mf) == ws(1)
     va = pa.PA_KERNEL_VALU

@@ -6,8 +6,9 @@ spilled vector registers for any of them (scalar registers spilled into
 vector-register lanes are not memory traffic and are allowed).  The list of
 kernels is also pinned against the variants the C ABI dispatches to: the
 vector-ALU decode is built for 1, 2 and 4 heads per group (16-bit types)
-and 1 (fp32) only, the sizes that fit without spilling; larger groups run
-as virtual groups of those."""
+and 1 (fp32) only, the sizes that fit without spilling; the matrix-core
+decode for 1-16 heads and for 32 and 64 (column-split groups); other
+groups run as virtual groups of those."""
 import re
 
 import pytest
@@ -42,7 +43,7 @@ def test_decode_variants_built(usage):
     want = set()
     for B in (16, 32):
         for t in ("F16", "BF16"):
-            want |= {(t, B, G, True) for G in (1, 2, 4, 8, 16)}
+            want |= {(t, B, G, True) for G in (1, 2, 4, 8, 16, 32, 64)}
             want |= {(t, B, G, False) for G in (1, 2, 4)}
         want.add(("F32", B, 1, False))
     assert set(dec) == want

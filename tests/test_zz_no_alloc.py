@@ -81,6 +81,21 @@ def test_no_alloc_group16_then_fp32_vector_alu(O):
         assert max_err(b, ref) <= TOL[dtype], w.name
 
 
+def test_no_alloc_mqa_groups_run_as_virtual_groups(O):
+    """MQA groups (64, then 32 query heads on one KV head): the
+    column-split kernel's partials would overflow the static scratch, so
+    the allocation-free entry runs them as virtual groups of 16 heads.  Its
+    output matches the workspace entry's (column-split kernel) to the
+    oracle bar, and each is within the bar of the oracle."""
+    for Hq, batch, max_len in ((64, 10, 4000), (32, 4, 2000)):
+        w = workload.make_mqa(Hq, seed=40 + Hq, batch=batch, max_len=max_len)
+        _log(f"[no_alloc] {w.name} S={w.num_seqs}")
+        ref = O.run_workload(w)
+        a, b = _run_both(Uploaded(w), pa.PA_KERNEL_AUTO)
+        assert max_err(a, ref) <= TOL["bf16"] and max_err(b, ref) <= TOL["bf16"], Hq
+        assert float((a - b).abs().max()) <= TOL["bf16"], Hq
+
+
 def test_no_alloc_bf16_output_and_empty_batch():
     w = workload.build(name="noalloc-out16", dtype="bf16", seq_lens=[0, 37, 700, 16], num_q_heads=8,
                        num_kv_heads=2, head_dim=128, block_size=32, seed=9)
