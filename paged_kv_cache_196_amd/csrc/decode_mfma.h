@@ -75,6 +75,24 @@ struct MfmaEngine {
       return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
 
+  // One 32-deep product c += A . B (A: 16 rows x 32, B: 32 x 16 columns,
+  // each lane holding its 8 K elements as 16-byte words).
+  static __device__ __forceinline__ f32x4 mma_32(const uint4& a, const uint4& b, f32x4 c) {
+    if constexpr (T::kCode == BF16::kCode)
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(Op8, a),
+                                                     __builtin_bit_cast(Op8, b), c, 0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(Op8, a),
+                                                    __builtin_bit_cast(Op8, b), c, 0, 0, 0);
+  }
+
+  // Two floats rounded to the input type and packed (first in the low half).
+  static __device__ __forceinline__ uint32_t pack2(float x, float y) {
+    typedef Elem pair __attribute__((ext_vector_type(2)));
+    const pair v = {(Elem)x, (Elem)y};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+
   // c += V^T . (P_hi + P_lo)^T for one 16-dim tile in a single 32-deep
   // product: the lane's 8 K elements are its 4 tokens twice, paired with
   // the hi probabilities in the first four and the lo ones in the last four

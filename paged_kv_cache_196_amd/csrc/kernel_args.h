@@ -52,6 +52,11 @@ struct PrefillArgs {
   int32_t Hp, kv_split, kv_shift;           // virtual KV heads, as in the decode arguments
 };
 
-constexpr int kPrefillTiles = 3;  // 16-column tiles per wave: they share every K/V load (3: two waves per SIMD)
+constexpr int kPrefillTiles = 2;  // 16-column tiles per wave: they share every K/V sub-tile read
+// Four waves per prefill workgroup and two workgroups per CU: the waves
+// sharing a SIMD belong to different workgroups, whose per-step barriers
+// are independent, so one's softmax overlaps the other's matrix products.
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillThreads = 64 * kPrefillWaves;
 
 }  // namespace pa

@@ -811,11 +811,13 @@ int32_t paged_attn_prefill(const void* q, const void* k_pool, const void* v_pool
   if (!q || !k_pool || !v_pool || !bt || !lens || !q_start || !out) return PA_ERR_NULL;
   if (((uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool | (uintptr_t)out) & 15u) return PA_ERR_ALIGN;
   if (!device_info().ok) return PA_ERR_DEVICE;
-  const int rows_per_wave = kSub / pp.G * kPrefillTiles;
-  const int64_t tiles = (max_q_len + rows_per_wave - 1) / rows_per_wave;
+  // row blocks of one workgroup: kPrefillWaves waves of kPrefillTiles column tiles
+  const int rows_per_block = kPrefillWaves * kPrefillTiles * (kSub / pp.G);
+  const int64_t tiles = (max_q_len + rows_per_block - 1) / rows_per_block;
   const int64_t hkv = (int64_t)d->num_kv_heads * pp.split;  // virtual KV heads
-  const int64_t items = tiles * hkv * d->num_seqs;
-  if (items >= ((int64_t)1 << 31) - kAuxWaves) return PA_ERR_UNSUPPORTED;
+  const int64_t pairs = hkv * d->num_seqs;
+  const int64_t blocks = 8 * ((pairs + 7) / 8) * tiles;  // XCD-major order (prefill_kernel)
+  if (blocks >= ((int64_t)1 << 31)) return PA_ERR_UNSUPPORTED;
   PrefillArgs a;
   a.q = q;
   a.kp = k_pool;
@@ -834,8 +836,7 @@ int32_t paged_attn_prefill(const void* q, const void* k_pool, const void* v_pool
   a.mbs = d->max_blocks_per_seq;
   a.tiles = (int32_t)tiles;
   a.out_f32 = d->out_dtype == PA_F32 ? 1 : 0;
-  const dim3 grid((unsigned)((items + kAuxWaves - 1) / kAuxWaves));
-  pp.fn(a, grid, static_cast<hipStream_t>(stream));
+  pp.fn(a, dim3((unsigned)blocks), static_cast<hipStream_t>(stream));
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -9,7 +9,7 @@ namespace pa {
 
 template <class T, int B, int G>
 void launch_prefill(const PrefillArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_kernel<T, B, G>), grid, dim3(kAuxThreads), 0, s, a);
+  hipLaunchKernelGGL((prefill_kernel<T, B, G>), grid, dim3(kPrefillThreads), 0, s, a);
 }
 
 template <class T, int B>

@@ -14,18 +14,21 @@
 // position p = L_b - n_b + i and attends tokens 0 .. p.  n_b = L_b is a whole
 // prompt, 1 < n_b < L_b a chunk of one (chunked prefill).
 //
-// Work item: one wave per (sequence b, KV head, kPrefillTiles column tiles).
-// A column tile holds R = 16 / G consecutive query rows times the G query
-// heads of the KV head: 16 MFMA columns, column c = (row c / G, head c % G),
-// each with its own causal limit.  The wave walks 16-token sub-tiles from
-// token 0 up to its largest position; every loaded sub-tile serves all of
-// its column tiles:
+// Work item: one workgroup of kWaves waves per (sequence b, KV head, block
+// of rows); wave w takes kPrefillTiles column tiles of the block.  A column
+// tile holds R = 16 / G consecutive query rows times the G query heads of
+// the KV head: 16 MFMA columns, column c = (row c / G, head c % G), each
+// with its own causal limit.  The workgroup walks 16-token K/V sub-tiles
+// from token 0 up to its largest position; each sub-tile is read from
+// memory once per workgroup (one 16-byte load per thread, issued
+// kPrefillDepth sub-tiles ahead), staged in a double-buffered LDS tile and
+// read from there by every wave that still has rows attending it:
 //   S^T[16 tok][16 cols] = K[16][128] . Q^T[128][16]   4 x mfma 16x16x32
 //   O^T[128][16 cols]   += V^T[128][16] . P^T[16][16]  8 dim tiles x mfma 16x16x32 (hi + lo P)
 // (operand layouts and the hi + lo split of P as in the decode engine), with
-// a running max and sum per column.  The waves of one (b, KV head) read the
-// same K/V tiles, through L2 (cached load policy).  Waves with later rows
-// (longer) are issued first, across the whole batch.
+// a running max and sum per column.  Workgroups run longest rows first
+// across the batch, and the blocks of one (sequence, KV head) go to one XCD
+// (workgroup i runs on XCD i mod 8), so they share its L2.
 #pragma once
 
 #include "decode_mfma.h"
@@ -35,30 +38,81 @@
 namespace pa {
 
 
-// Grid: ceil(tiles * S * Hkv / kAuxWaves) workgroups of kAuxThreads; `tiles`
-// counts groups of kPrefillTiles column tiles.  Items run (column group,
-// sequence, KV head) with the column group slowest and reversed, so the
-// longest rows of the whole batch are issued first and the shortest last.
+constexpr int kPrefillStepSub = 4;           // 16-token sub-tiles per step (one softmax update)
+constexpr int kPrefillKRow = kD * 2 + 16;     // LDS bytes per K row (padded: rows 4 banks apart)
+constexpr int kPrefillKBytes = kSub * kPrefillKRow;
+// one sub-tile: K rows, then the V^T group as 8-byte entries (4 tokens of
+// one dim) in the order [dim / 16][token quarter][dim % 16], so the 16
+// lanes of one LDS read cycle (one token quarter, 16 dims) read 128
+// contiguous bytes
+constexpr int kPrefillStage = kPrefillKBytes + kSub * kD * 2;
+static_assert(kPrefillThreads * 16 == kSub * kD * 2, "one K and one V chunk per thread per sub-tile");
+
+// Reference-max slack of the prefill's lazy rescaling (log2 units).
+constexpr float kPrefillSlack = 8.f;
+static_assert(kPrefillStepSub % 2 == 0, "weighted values take sub-tiles in pairs");
+
+// Zero the V^T entries of tokens past `nv` (tokens 4 grp .. of this lane,
+// nv = valid tokens among them) in the 8 dim tiles.
+__device__ __forceinline__ void v_tail_mask(uint2 (&v)[8], int nv) {
+  const uint32_t lo_mask = (nv >= 1 ? 0x0000ffffu : 0u) | (nv >= 2 ? 0xffff0000u : 0u);
+  const uint32_t hi_mask = (nv >= 3 ? 0x0000ffffu : 0u) | (nv >= 4 ? 0xffff0000u : 0u);
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    v[x].x &= lo_mask;
+    v[x].y &= hi_mask;
+  }
+}
+
+// Rows of one workgroup's block for group size G.
+template <int G>
+constexpr int prefill_rows_per_block() {
+  return kPrefillWaves * kPrefillTiles * (kSub / G);
+}
+
+// Grid: 8 * ceil(S * Hkv / 8) * tiles workgroups of kPrefillThreads, `tiles` the
+// row blocks of the longest query set.  Workgroup i runs on XCD x = i % 8
+// and takes the (sequence, KV head) pairs x, x + 8, ... (pair = b * Hkv +
+// kvh) with its row block slowest and reversed, so each XCD works the
+// longest rows of its pairs first.
+//
+// The keys go by steps of kPrefillStepSub sub-tiles (64 tokens): the step's
+// scores of every column tile first (independent 4-deep products per
+// sub-tile), one softmax update per column tile for the whole step, then
+// the weighted values (8-deep chains per dim tile across the step), so the
+// matrix cores see long runs of independent products between the
+// reductions.
 template <class T, int B, int G>
-__global__ __launch_bounds__(kAuxThreads) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a) {
   using M = MfmaEngine<T, B, G>;
   using Op4 = typename M::Op4;
   using Elem = typename M::Elem;
   constexpr int NT = kPrefillTiles;
+  constexpr int KB = kPrefillStepSub;
   constexpr int R = kSub / G;  // query rows per column tile
+  constexpr int kRowsBlock = prefill_rows_per_block<G>();
   constexpr int kTileBytes = B * kD * 2;
+  constexpr int kStep = KB * kSub;  // tokens per step
+  __shared__ __align__(16) unsigned char stage[2][KB][kPrefillStage];
+
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
-  const int item = uniform(blockIdx.x * kAuxWaves + (threadIdx.x >> 6));
-  if (item >= a.tiles * a.S * a.Hkv) return;
-  const int ct0 = (a.tiles - 1 - item / (a.S * a.Hkv)) * NT;  // longest rows of the whole batch first
-  const int b = (item / a.Hkv) % a.S;
-  const int kvh = item % a.Hkv;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int P = a.S * a.Hkv;
+  const int xcd = blockIdx.x % 8, k = blockIdx.x / 8;
+  const int px = (P - xcd + 7) / 8;  // pairs of this XCD
+  if (k >= px * a.tiles) return;
+  const int rb = a.tiles - 1 - k / px;  // longest rows first
+  const int pair = xcd + 8 * (k % px);
+  const int b = pair / a.Hkv, kvh = pair % a.Hkv;
   const int q0 = as_constant(a.qs)[b];
   const int n = as_constant(a.qs)[b + 1] - q0;
   const int L = as_constant(a.lens)[b];
-  if (n <= 0 || n > L || ct0 * R >= n) return;
+  if (n <= 0 || n > L || rb * kRowsBlock >= n) return;  // uniform over the workgroup
   const int head = kvh * G + col % G;
-  const int last = L - n + min(n, (ct0 + NT) * R) - 1;  // largest position among the wave's rows
+  const int ct0 = (rb * kPrefillWaves + wave) * NT;  // this wave's first column tile
+  // largest position among the wave's rows (-1: none) and the workgroup's
+  const int last = ct0 * R < n ? L - n + min(n, (ct0 + NT) * R) - 1 : -1;
+  const int last_blk = L - n + min(n, (rb + 1) * kRowsBlock) - 1;
 
   int row[NT], pos[NT];
   uint4 qop[NT][4];  // query operand of tile t: column col, dims 32x + 8grp .. +8
@@ -85,75 +139,173 @@ __global__ __launch_bounds__(kAuxThreads) void prefill_kernel(PrefillArgs a) {
     lsum[t] = 0.f;
   }
 
+  // This thread's 2 x 16 bytes of every sub-tile: K chunk c (token c / 16,
+  // dims 8 (c % 16) ..) and V^T chunk c (dim c / 2, tokens 8 (c % 2) .. + 8,
+  // i.e. token quarters 2 (c % 2) and 2 (c % 2) + 1), c = threadIdx.x, and
+  // where they go in the LDS stage.
+  const int c16 = threadIdx.x;
+  const int vdim = c16 / 2, vq = 2 * (c16 % 2);
+  const int k_off = c16 / 16 * kPrefillKRow + c16 % 16 * 16;
+  const int v_off = kPrefillKBytes + (vdim / 16 * 64 + vq * 16 + vdim % 16) * 8;
   const const_i32_ptr row_bt = as_constant(a.bt + (int64_t)b * a.mbs);
-  const int koff = (col * kD + 8 * grp) * 2;
-  const int voff = (col * kSub + 4 * grp) * 2;
-  const int nsub = last / kSub + 1;
-  for (int j = 0; j < nsub; ++j) {
-    const int tok0 = j * kSub;
-    const int phys = row_bt[tok0 / B];
-    const int64_t tile = ((int64_t)phys * a.Hp + pool_head(a, kvh)) * kTileBytes;
-    const auto rk = tile_rsrc(a.kp, tile, kTileBytes);
-    const auto rv = tile_rsrc(a.vp, tile, kTileBytes);
-    const int soff = (tok0 % B) * kD * 2;
-    uint4 k[4];
-    uint2 v[8];
+  const int kvp = pool_head(a, kvh);
+  const int last_sub = last_blk / kSub;
+  const int nstep = last_blk / kStep + 1;
+  // Every load is issued, so the wait before the LDS stores is the same on
+  // every path: past the last sub-tile the resource has zero bytes (nothing
+  // is read, zeros come back) and the table entry is clamped to a live one.
+  uint4 gk[KB], gv[KB];  // step j + 1 while step j is computed
+  auto gload = [&](int j) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x) k[x] = tile_load16<kCachedPolicy>(rk, koff + 64 * x, soff);
-#pragma unroll
-    for (int x = 0; x < 8; ++x) v[x] = tile_load8<kCachedPolicy>(rv, voff + 32 * x * kSub, soff);
-    const int valid = last - tok0 + 1;  // tokens of this sub-tile that any column attends
-    if (valid < kSub) {
-      // Slots past the wave's last position may lie past the sequence end
-      // and hold anything (NaN included): zero them so 0 * slot stays 0.
-      const int nv = valid - 4 * grp;
-      const uint32_t lo_mask = (nv >= 1 ? 0x0000ffffu : 0u) | (nv >= 2 ? 0xffff0000u : 0u);
-      const uint32_t hi_mask = (nv >= 3 ? 0x0000ffffu : 0u) | (nv >= 4 ? 0xffff0000u : 0u);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        v[x].x &= lo_mask;
-        v[x].y &= hi_mask;
-      }
+    for (int u = 0; u < KB; ++u) {
+      const int sub = j * KB + u;
+      const bool live = sub <= last_sub;
+      const int tok0 = (live ? sub : last_sub) * kSub;
+      const int phys = uniform(row_bt[tok0 / B]);
+      const int64_t tile = ((int64_t)phys * a.Hp + kvp) * kTileBytes;
+      const int bytes = uniform(live ? kTileBytes : 0);
+      const int soff = (tok0 % B) * kD * 2;
+      gk[u] = tile_load16<kCachedPolicy>(tile_rsrc(a.kp, tile, bytes), c16 * 16, soff);
+      gv[u] = tile_load16<kCachedPolicy>(tile_rsrc(a.vp, tile, bytes), c16 * 16, soff);
     }
+  };
+  auto stage_store = [&](int buf) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < KB; ++u) {
+      unsigned char* dst = &stage[buf][u][0];
+      *reinterpret_cast<uint4*>(dst + k_off) = gk[u];
+      *reinterpret_cast<uint2*>(dst + v_off) = make_uint2(gv[u].x, gv[u].y);
+      *reinterpret_cast<uint2*>(dst + v_off + 16 * 8) = make_uint2(gv[u].z, gv[u].w);  // next quarter
+    }
+  };
+  gload(0);
+  stage_store(0);
+  gload(1);
+  __syncthreads();
+
+  // Step j is in LDS buffer j & 1 and step j + 1 in flight in gk / gv.
+  for (int j = 0; j < nstep; ++j) {
+    {
+      const int ts = j * kStep;
+      if (ts <= last) {
+        f32x4 s[NT][KB];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) s = M::mma_qk(k[x], qop[t][x], s);
-      float xr[4];
+        for (int u = 0; u < KB; ++u) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        xr[r] = (tok0 + 4 * grp + r <= pos[t]) ? s[r] * a.scale_log2 : -INFINITY;
-      float bm = fmaxf(fmaxf(xr[0], xr[1]), fmaxf(xr[2], xr[3]));
-      bm = max_xor16(bm);
-      bm = max_xor32(bm);
-      // Token 0 is in sub-tile 0 and every column attends it, so m is
-      // finite from the first sub-tile on.
-      const float mn = fmaxf(m[t], bm);
-      if (wave_any(mn > m[t])) {
-        // some column's max grew: rescale (alpha = 1 where it did not)
-        const float alpha = fast_exp2(m[t] - mn);
-        lsum[t] *= alpha;
+          for (int t = 0; t < NT; ++t) s[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (ts + u * kSub <= last) {
+            const unsigned char* su = &stage[j & 1][u][0];
+            uint4 kr[4];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) acc[t][x] *= alpha;
-        m[t] = mn;
+            for (int x = 0; x < 4; ++x)
+              kr[x] = *reinterpret_cast<const uint4*>(su + col * kPrefillKRow + (32 * x + 8 * grp) * 2);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+              for (int x = 0; x < 4; ++x) s[t][u] = M::mma_qk(kr[x], qop[t][x], s[t][u]);
+          }
+        }
+        // A step wholly at or below the wave's first row needs no causal
+        // mask (every live column attends all its tokens; padding columns
+        // are never stored).
+        const bool full = ts + kStep - 1 <= L - n + ct0 * R;
+        // Probabilities as the B operands of the weighted-value products:
+        // for sub-tile pair h (sub-tiles 2h, 2h + 1) the hi halves of both
+        // (4 tokens each, packed) and, separately, the lo halves.
+        uint4 bh[NT][KB / 2], bl[NT][KB / 2];
+        // Softmax update of each column tile for the step (scores in base-2
+        // units, x = s * scale * log2 e; p = 2^(x - m), exactly 1 where x is
+        // the max).
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          float xr[KB][4];
+          float bm = -INFINITY;
+#pragma unroll
+          for (int u = 0; u < KB; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              xr[u][r] = s[t][u][r] * a.scale_log2;
+              if (!full && ts + u * kSub + 4 * grp + r > pos[t]) xr[u][r] = -INFINITY;
+              bm = fmaxf(bm, xr[u][r]);
+            }
+          bm = max_xor16(bm);
+          bm = max_xor32(bm);
+          // Lazy rescaling: the reference max moves only when some column's
+          // scores exceed it by more than 2^kPrefillSlack, so most steps
+          // skip the rescale; the probabilities then stay below
+          // 2^kPrefillSlack, and the result o / l does not depend on the
+          // reference.  Token 0 is in step 0 and every column attends it,
+          // so m is finite from the first step on.
+          if (wave_any(bm > m[t] + kPrefillSlack)) {
+            const float mn = fmaxf(m[t], bm);
+            const float alpha = fast_exp2(m[t] - mn);
+            lsum[t] *= alpha;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) acc[t][x] *= alpha;
+            m[t] = mn;
+          }
+          float ps = 0.f;
+          uint32_t hw[KB][2], lw[KB][2];
+#pragma unroll
+          for (int u = 0; u < KB; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; r += 2) {
+              const float p0 = fast_exp2(xr[u][r] - m[t]);
+              const float p1 = fast_exp2(xr[u][r + 1] - m[t]);
+              ps += p0 + p1;
+              hw[u][r / 2] = M::pack2(p0, p1);
+              float h0, h1;
+              unpack2<T>(hw[u][r / 2], h0, h1);
+              lw[u][r / 2] = M::pack2(p0 - h0, p1 - h1);
+            }
+          lsum[t] += ps;
+#pragma unroll
+          for (int h = 0; h < KB / 2; ++h) {
+            bh[t][h] = make_uint4(hw[2 * h][0], hw[2 * h][1], hw[2 * h + 1][0], hw[2 * h + 1][1]);
+            bl[t][h] = make_uint4(lw[2 * h][0], lw[2 * h][1], lw[2 * h + 1][0], lw[2 * h + 1][1]);
+          }
+        }
+        // Weighted values, two sub-tiles per 32-deep product: A = this
+        // lane's 4 tokens of sub-tile 2h and of 2h + 1 (one dim), against
+        // the hi probabilities, then against the lo ones.
+#pragma unroll
+        for (int h = 0; h < KB / 2; ++h) {
+          const int tok0 = ts + 2 * h * kSub, tok1 = tok0 + kSub;
+          if (tok0 > last) continue;
+          const unsigned char* s0 = &stage[j & 1][2 * h][0] + kPrefillKBytes;
+          const unsigned char* s1 = &stage[j & 1][2 * h + 1][0] + kPrefillKBytes;
+          uint2 v0[8], v1[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const int e = (x * 64 + grp * 16 + col) * 8;
+            v0[x] = *reinterpret_cast<const uint2*>(s0 + e);
+            v1[x] = tok1 <= last ? *reinterpret_cast<const uint2*>(s1 + e) : make_uint2(0, 0);
+          }
+          // Slots past the wave's last position may lie past the sequence
+          // end and hold anything (NaN included): zero them so 0 * slot
+          // stays 0.
+          if (last - tok0 + 1 < kSub) v_tail_mask(v0, last - tok0 + 1 - 4 * grp);
+          if (tok1 <= last && last - tok1 + 1 < kSub) v_tail_mask(v1, last - tok1 + 1 - 4 * grp);
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const uint4 va = make_uint4(v0[x].x, v0[x].y, v1[x].x, v1[x].y);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              acc[t][x] = M::mma_32(va, bh[t][h], acc[t][x]);
+              acc[t][x] = M::mma_32(va, bl[t][h], acc[t][x]);
+            }
+          }
+        }
       }
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(xr[r] - m[t]);
-      lsum[t] += (p[0] + p[1]) + (p[2] + p[3]);
-      Op4 phi, plo;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        phi[r] = (Elem)p[r];
-        plo[r] = (Elem)(p[r] - (float)phi[r]);
-      }
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        acc[t][x] = M::mma_pv2(v[x], phi, plo, acc[t][x]);
-      }
+      // step j + 1 to the other buffer (last read before the previous
+      // barrier), then step j + 2 starts loading: it has one step of
+      // compute to arrive
+      if (j + 1 < nstep) stage_store((j + 1) & 1);
+      gload(j + 2);
+      __syncthreads();
     }
   }
+  if (last < 0) return;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     float l = sum_xor16(lsum[t]);
