@@ -47,21 +47,23 @@ def test_dtype_sizes():
     assert [pa.pa_dtype_size(d) for d in (pa.PA_F32, pa.PA_F16, pa.PA_BF16, 7)] == [4, 2, 2, 0]
 
 
-def test_block_rounding_matches_the_sizing_example():
-    fx = json.load(open(os.path.join(GOLDEN, "sizing_examples.json")))
-    r = fx["block_rounding"]
-    slots = [pa.pa_blocks_for_len(L, r["block_size"]) * r["block_size"] for L in r["lengths"]]
-    assert slots == r["rounded_slots"]
-    assert sum(slots) == r["paged_slots_total"]
-    assert sum(r["lengths"]) == r["used_slots"]
-    assert sum(slots) - sum(r["lengths"]) == r["unused_slots"]
-    reserved = len(r["lengths"]) * r["reserved_per_request"]
-    assert reserved == r["reserved_slots_total"]
-    mib = 2 ** 20
-    assert reserved * r["kv_bytes_per_token"] / mib == r["reserved_mib"]
-    assert sum(slots) * r["kv_bytes_per_token"] / mib == r["paged_mib"]
-    assert sum(r["lengths"]) * r["kv_bytes_per_token"] / mib == r["used_mib"]
-    u = fx["utilisation_200"]
+def test_blocks_for_len_gives_the_printed_paged_slots():
+    """pa_blocks_for_len against the printed paged-storage example of
+    "FlashAttention vs PagedAttention" (section on attention intermediates
+    and paged cache storage): requests of 19, 45 and 70 tokens in 16-token
+    pages hold 32, 48 and 80 slots, 160 in all, 26 of them empty.  Its MiB
+    lines are slot counts times one per-slot size, so they pin the same
+    counts as ratios: paged / fixed 20 / 48 MiB = 160 / 384 slots and used /
+    paged 16.75 / 20 MiB = 134 / 160 slots."""
+    ex = json.load(open(os.path.join(GOLDEN, "sizing_examples.json")))["printed_paged_slots"]
+    page = ex["page_tokens"]
+    held = [pa.pa_blocks_for_len(n, page) * page for n in ex["request_tokens"]]
+    assert held == ex["slots_per_request"]
+    in_use = sum(ex["request_tokens"])
+    assert sum(held) == ex["slots_held"] and sum(held) - in_use == ex["slots_empty"]
+    assert sum(held) * ex["mib_fixed"] == ex["slots_fixed"] * ex["mib_paged"]
+    assert in_use * ex["mib_paged"] == sum(held) * ex["mib_used"]
+    u = json.load(open(os.path.join(GOLDEN, "sizing_examples.json")))["utilisation_200"]
     n = pa.pa_blocks_for_len(u["length"], u["block_size"])
     assert n == u["blocks"] and n * u["block_size"] == u["slots"]
     assert round(100 * u["length"] / (n * u["block_size"]), 1) == u["utilisation_percent"]

@@ -4,8 +4,10 @@ bf16 inputs, fp32 accumulation).
 
 Rows are each sequence's newest n_b tokens, row i at position L - n_b + i,
 attending tokens 0 .. that position.  Small cases compare every output with
-the oracle's prefill; the full-size GQA prompt batch compares sampled rows
-with the oracle's decode at each row's position (a pinned equivalence)."""
+the oracle's prefill; the full-size GQA prompt batch checks that every row
+is written, compares every row of one prompt with the oracle's prefill and
+sampled rows of the others with the oracle's decode at each row's position
+(a pinned equivalence)."""
 import sys
 
 import numpy as np
@@ -103,13 +105,33 @@ def test_prefill_first_row_is_value_row_and_single_row_is_decode(O):
     assert torch.max(torch.abs(pre - dec)).item() <= 1e-4
 
 
-def test_prefill_gqa_prompt_batch_full_size_sampled(O):
+def test_prefill_gqa_prompt_batch_full_size(O):
     """The benchmarked prefill workload (8 whole prompts of 2048 tokens, GQA
-    32/8, bf16, B = 16): sampled rows against the oracle's decode at each
-    row's position."""
+    32/8, bf16, B = 16), output buffer filled with NaN first: every element
+    must come back finite (every row written), every row of one whole
+    prompt must match the oracle's prefill, and sampled rows of the others
+    the oracle's decode at each row's position (a pinned equivalence)."""
     w, q, qs = workload.prefill_workload()
-    got = _run(w, q, qs).double().cpu().numpy()
-    assert np.all(np.isfinite(got))
+    qd = device_tensor(q, w.dtype)
+    out = torch.full(qd.shape, float("nan"), dtype=torch.float32, device=qd.device)
+    pa.prefill(qd, device_tensor(w.k_pool, w.dtype), device_tensor(w.v_pool, w.dtype),
+               torch.from_numpy(w.block_tables).cuda(), torch.from_numpy(w.seq_lens).cuda(),
+               torch.from_numpy(qs).cuda(), float(w.scale), out=out)
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy()
+    assert np.all(np.isfinite(got)), "rows left unwritten"
+    # every row of prompt 3 (its own sequence, the others' lengths zeroed out)
+    b = 3
+    lens1 = np.zeros_like(w.seq_lens)
+    lens1[b] = w.seq_lens[b]
+    qs1 = np.zeros_like(qs)
+    qs1[b + 1:] = qs[b + 1] - qs[b]
+    ref_b = O.paged_prefill(np.ascontiguousarray(q[qs[b]:qs[b + 1]]), w.k_pool, w.v_pool,
+                            w.block_tables, lens1, qs1, np.float64(np.float32(w.scale)),
+                            num_kv_heads=w.num_kv_heads, block_size=w.block_size, dtype=w.dtype)
+    whole = float(np.max(np.abs(got[qs[b]:qs[b + 1]] - ref_b)))
+    _log(f"[prefill] full size: every row of prompt {b} max_abs_err={whole:.3e}")
+    assert whole <= TOL["bf16"]
     rng = np.random.default_rng(7)
     worst = 0.0
     for b in range(w.num_seqs):
