@@ -219,15 +219,22 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           float xr[KB][4];
+#pragma unroll
+          for (int u = 0; u < KB; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) xr[u][r] = s[t][u][r] * a.scale_log2;
+          if (!full) {  // uniform: only steps crossing the diagonal pay for the mask
+#pragma unroll
+            for (int u = 0; u < KB; ++u)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (ts + u * kSub + 4 * grp + r > pos[t]) xr[u][r] = -INFINITY;
+          }
           float bm = -INFINITY;
 #pragma unroll
           for (int u = 0; u < KB; ++u)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              xr[u][r] = s[t][u][r] * a.scale_log2;
-              if (!full && ts + u * kSub + 4 * grp + r > pos[t]) xr[u][r] = -INFINITY;
-              bm = fmaxf(bm, xr[u][r]);
-            }
+            for (int r = 0; r < 4; ++r) bm = fmaxf(bm, xr[u][r]);
           bm = max_xor16(bm);
           bm = max_xor32(bm);
           // Lazy rescaling: the reference max moves only when some column's
