@@ -64,6 +64,29 @@ __device__ __forceinline__ void v_tail_mask(uint2 (&v)[8], int nv) {
   }
 }
 
+// Probabilities p0, p1 as hi and lo pairs in the input type, p ~= hi + lo.
+// bf16: hi is p with its low 16 bits cut off (the upper halves of both, one
+// byte permute), lo the exact remainder rounded to bf16; p <= 2^8 here and
+// |lo| < 2^-7 p, so the pair keeps about 16 bits.  f16: hi rounded to
+// nearest, lo the rounded remainder.
+template <class T>
+__device__ __forceinline__ void split_pair(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+  typedef typename std::conditional<T::kCode == BF16::kCode, __bf16, _Float16>::type E;
+  typedef E pair __attribute__((ext_vector_type(2)));
+  if constexpr (T::kCode == BF16::kCode) {
+    const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
+    hi = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+    const pair r = {(E)(p0 - __uint_as_float(b0 & 0xffff0000u)),
+                    (E)(p1 - __uint_as_float(b1 & 0xffff0000u))};
+    lo = __builtin_bit_cast(uint32_t, r);
+  } else {
+    const pair h = {(E)p0, (E)p1};
+    hi = __builtin_bit_cast(uint32_t, h);
+    const pair r = {(E)(p0 - (float)h.x), (E)(p1 - (float)h.y)};
+    lo = __builtin_bit_cast(uint32_t, r);
+  }
+}
+
 // Rows of one workgroup's block for group size G.
 template <int G>
 constexpr int prefill_rows_per_block() {
@@ -147,7 +170,6 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   const int vdim = c16 / 2, vq = 2 * (c16 % 2);
   const int k_off = c16 / 16 * kPrefillKRow + c16 % 16 * 16;
   const int v_off = kPrefillKBytes + (vdim / 16 * 64 + vq * 16 + vdim % 16) * 8;
-  const const_i32_ptr row_bt = as_constant(a.bt + (int64_t)b * a.mbs);
   const int kvp = pool_head(a, kvh);
   const int last_sub = last_blk / kSub;
   const int nstep = last_blk / kStep + 1;
@@ -155,16 +177,30 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   // every path: past the last sub-tile the resource has zero bytes (nothing
   // is read, zeros come back) and the table entry is clamped to a live one.
   uint4 gk[KB], gv[KB];  // step j + 1 while step j is computed
+  // Table entries of the step a load call fetches are read by the call
+  // before it, as vector loads: they retire in order with the K/V loads
+  // that the LDS stores wait for anyway, so no barrier or load waits on a
+  // table read (a scalar read would be waited for at the next barrier).
+  const __amdgpu_buffer_rsrc_t tab_rsrc = tile_rsrc(a.bt, (int64_t)b * a.mbs * 4, a.mbs * 4);
+  uint32_t tab[KB];
+  auto gtab = [&](int j) {
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+      tab[u] = __builtin_amdgcn_raw_buffer_load_b32(tab_rsrc, 0, min(j * KB + u, last_sub) * kSub / B * 4,
+                                                    kCachedPolicy);
+  };
   auto gload = [&](int j) {
+    int phys[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) phys[u] = uniform((int)tab[u]);
+    gtab(j + 1);
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int sub = j * KB + u;
       const bool live = sub <= last_sub;
-      const int tok0 = (live ? sub : last_sub) * kSub;
-      const int phys = uniform(row_bt[tok0 / B]);
-      const int64_t tile = ((int64_t)phys * a.Hp + kvp) * kTileBytes;
+      const int64_t tile = ((int64_t)phys[u] * a.Hp + kvp) * kTileBytes;
       const int bytes = uniform(live ? kTileBytes : 0);
-      const int soff = (tok0 % B) * kD * 2;
+      const int soff = ((live ? sub : last_sub) * kSub % B) * kD * 2;
       gk[u] = tile_load16<kCachedPolicy>(tile_rsrc(a.kp, tile, bytes), c16 * 16, soff);
       gv[u] = tile_load16<kCachedPolicy>(tile_rsrc(a.vp, tile, bytes), c16 * 16, soff);
     }
@@ -178,6 +214,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
       *reinterpret_cast<uint2*>(dst + v_off + 16 * 8) = make_uint2(gv[u].z, gv[u].w);  // next quarter
     }
   };
+  gtab(0);
   gload(0);
   stage_store(0);
   gload(1);
@@ -188,21 +225,22 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     {
       const int ts = j * kStep;
       if (ts <= last) {
+        // Every sub-tile of the step is scored, also those past the wave's
+        // last position (zeros or stale tokens in LDS; the causal mask
+        // removes them), so the products need no branches or zero fills.
         f32x4 s[NT][KB];
 #pragma unroll
         for (int u = 0; u < KB; ++u) {
+          const unsigned char* su = &stage[j & 1][u][0];
+          uint4 kr[4];
 #pragma unroll
-          for (int t = 0; t < NT; ++t) s[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (ts + u * kSub <= last) {
-            const unsigned char* su = &stage[j & 1][u][0];
-            uint4 kr[4];
+          for (int x = 0; x < 4; ++x)
+            kr[x] = *reinterpret_cast<const uint4*>(su + col * kPrefillKRow + (32 * x + 8 * grp) * 2);
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
-              kr[x] = *reinterpret_cast<const uint4*>(su + col * kPrefillKRow + (32 * x + 8 * grp) * 2);
+          for (int t = 0; t < NT; ++t) {
+            s[t][u] = M::mma_qk(kr[0], qop[t][0], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-#pragma unroll
-              for (int x = 0; x < 4; ++x) s[t][u] = M::mma_qk(kr[x], qop[t][x], s[t][u]);
+            for (int x = 1; x < 4; ++x) s[t][u] = M::mma_qk(kr[x], qop[t][x], s[t][u]);
           }
         }
         // A step wholly at or below the wave's first row needs no causal
@@ -224,11 +262,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
 #pragma unroll
             for (int r = 0; r < 4; ++r) xr[u][r] = s[t][u][r] * a.scale_log2;
           if (!full) {  // uniform: only steps crossing the diagonal pay for the mask
+            const int d = pos[t] - ts - 4 * grp;  // token ts + 4 grp + i is masked when i > d
 #pragma unroll
             for (int u = 0; u < KB; ++u)
 #pragma unroll
               for (int r = 0; r < 4; ++r)
-                if (ts + u * kSub + 4 * grp + r > pos[t]) xr[u][r] = -INFINITY;
+                if (u * kSub + r > d) xr[u][r] = -INFINITY;
           }
           float bm = -INFINITY;
 #pragma unroll
@@ -260,10 +299,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
               const float p0 = fast_exp2(xr[u][r] - m[t]);
               const float p1 = fast_exp2(xr[u][r + 1] - m[t]);
               ps += p0 + p1;
-              hw[u][r / 2] = M::pack2(p0, p1);
-              float h0, h1;
-              unpack2<T>(hw[u][r / 2], h0, h1);
-              lw[u][r / 2] = M::pack2(p0 - h0, p1 - h1);
+              split_pair<T>(p0, p1, hw[u][r / 2], lw[u][r / 2]);
             }
           lsum[t] += ps;
 #pragma unroll
@@ -286,13 +322,13 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
           for (int x = 0; x < 8; ++x) {
             const int e = (x * 64 + grp * 16 + col) * 8;
             v0[x] = *reinterpret_cast<const uint2*>(s0 + e);
-            v1[x] = tok1 <= last ? *reinterpret_cast<const uint2*>(s1 + e) : make_uint2(0, 0);
+            v1[x] = *reinterpret_cast<const uint2*>(s1 + e);
           }
           // Slots past the wave's last position may lie past the sequence
-          // end and hold anything (NaN included): zero them so 0 * slot
-          // stays 0.
+          // end and hold anything (NaN included; sub-tile 2h + 1 may lie
+          // wholly past it): zero them so 0 * slot stays 0.
           if (last - tok0 + 1 < kSub) v_tail_mask(v0, last - tok0 + 1 - 4 * grp);
-          if (tok1 <= last && last - tok1 + 1 < kSub) v_tail_mask(v1, last - tok1 + 1 - 4 * grp);
+          if (last - tok1 + 1 < kSub) v_tail_mask(v1, last - tok1 + 1 - 4 * grp);
 #pragma unroll
           for (int x = 0; x < 8; ++x) {
             const uint4 va = make_uint4(v0[x].x, v0[x].y, v1[x].x, v1[x].y);
