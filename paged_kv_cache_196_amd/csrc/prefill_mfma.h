@@ -35,6 +35,8 @@
 #include "kernel_args.h"
 #include "pa_device.h"
 
+#include <type_traits>
+
 namespace pa {
 
 
@@ -221,133 +223,152 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   __syncthreads();
 
   // Step j is in LDS buffer j & 1 and step j + 1 in flight in gk / gv.
-  for (int j = 0; j < nstep; ++j) {
-    {
-      const int ts = j * kStep;
-      if (ts <= last) {
-        // Every sub-tile of the step is scored, also those past the wave's
-        // last position (zeros or stale tokens in LDS; the causal mask
-        // removes them), so the products need no branches or zero fills.
-        f32x4 s[NT][KB];
+  // Steps wholly at or below the wave's first row need no causal mask
+  // (every live column attends all their tokens; padding columns are never
+  // stored) and run without any mask code or branch; the steps from the
+  // diagonal on run with it.  The rescale decision is taken once per step
+  // for both column tiles, so the exponentials, the splits and the
+  // weighted-value products of a step form one straight run in which one
+  // tile's products overlap the other tile's vector work.
+  auto step = [&](const int j, auto masked) {
+    constexpr bool kMasked = decltype(masked)::value;
+    const int ts = j * kStep;
+    if (!kMasked || ts <= last) {
+      // Every sub-tile of the step is scored, also those past the wave's
+      // last position (zeros or stale tokens in LDS; the causal mask
+      // removes them), so the products need no branches or zero fills.
+      f32x4 s[NT][KB];
 #pragma unroll
-        for (int u = 0; u < KB; ++u) {
-          const unsigned char* su = &stage[j & 1][u][0];
-          uint4 kr[4];
+      for (int u = 0; u < KB; ++u) {
+        const unsigned char* su = &stage[j & 1][u][0];
+        uint4 kr[4];
 #pragma unroll
-          for (int x = 0; x < 4; ++x)
-            kr[x] = *reinterpret_cast<const uint4*>(su + col * kPrefillKRow + (32 * x + 8 * grp) * 2);
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            s[t][u] = M::mma_qk(kr[0], qop[t][0], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-            for (int x = 1; x < 4; ++x) s[t][u] = M::mma_qk(kr[x], qop[t][x], s[t][u]);
-          }
-        }
-        // A step wholly at or below the wave's first row needs no causal
-        // mask (every live column attends all its tokens; padding columns
-        // are never stored).
-        const bool full = ts + kStep - 1 <= L - n + ct0 * R;
-        // Probabilities as the B operands of the weighted-value products:
-        // for sub-tile pair h (sub-tiles 2h, 2h + 1) the hi halves of both
-        // (4 tokens each, packed) and, separately, the lo halves.
-        uint4 bh[NT][KB / 2], bl[NT][KB / 2];
-        // Softmax update of each column tile for the step (scores in base-2
-        // units, x = s * scale * log2 e; p = 2^(x - m), exactly 1 where x is
-        // the max).
+        for (int x = 0; x < 4; ++x)
+          kr[x] = *reinterpret_cast<const uint4*>(su + col * kPrefillKRow + (32 * x + 8 * grp) * 2);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          float xr[KB][4];
+          s[t][u] = M::mma_qk(kr[0], qop[t][0], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-          for (int u = 0; u < KB; ++u)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) xr[u][r] = s[t][u][r] * a.scale_log2;
-          if (!full) {  // uniform: only steps crossing the diagonal pay for the mask
-            const int d = pos[t] - ts - 4 * grp;  // token ts + 4 grp + i is masked when i > d
-#pragma unroll
-            for (int u = 0; u < KB; ++u)
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (u * kSub + r > d) xr[u][r] = -INFINITY;
-          }
-          float bm = -INFINITY;
-#pragma unroll
-          for (int u = 0; u < KB; ++u)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) bm = fmaxf(bm, xr[u][r]);
-          bm = max_xor16(bm);
-          bm = max_xor32(bm);
-          // Lazy rescaling: the reference max moves only when some column's
-          // scores exceed it by more than 2^kPrefillSlack, so most steps
-          // skip the rescale; the probabilities then stay below
-          // 2^kPrefillSlack, and the result o / l does not depend on the
-          // reference.  Token 0 is in step 0 and every column attends it,
-          // so m is finite from the first step on.
-          if (wave_any(bm > m[t] + kPrefillSlack)) {
-            const float mn = fmaxf(m[t], bm);
-            const float alpha = fast_exp2(m[t] - mn);
-            lsum[t] *= alpha;
-#pragma unroll
-            for (int x = 0; x < 8; ++x) acc[t][x] *= alpha;
-            m[t] = mn;
-          }
-          float ps = 0.f;
-          uint32_t hw[KB][2], lw[KB][2];
-#pragma unroll
-          for (int u = 0; u < KB; ++u)
-#pragma unroll
-            for (int r = 0; r < 4; r += 2) {
-              const float p0 = fast_exp2(xr[u][r] - m[t]);
-              const float p1 = fast_exp2(xr[u][r + 1] - m[t]);
-              ps += p0 + p1;
-              split_pair<T>(p0, p1, hw[u][r / 2], lw[u][r / 2]);
-            }
-          lsum[t] += ps;
-#pragma unroll
-          for (int h = 0; h < KB / 2; ++h) {
-            bh[t][h] = make_uint4(hw[2 * h][0], hw[2 * h][1], hw[2 * h + 1][0], hw[2 * h + 1][1]);
-            bl[t][h] = make_uint4(lw[2 * h][0], lw[2 * h][1], lw[2 * h + 1][0], lw[2 * h + 1][1]);
-          }
+          for (int x = 1; x < 4; ++x) s[t][u] = M::mma_qk(kr[x], qop[t][x], s[t][u]);
         }
-        // Weighted values, two sub-tiles per 32-deep product: A = this
-        // lane's 4 tokens of sub-tile 2h and of 2h + 1 (one dim), against
-        // the hi probabilities, then against the lo ones.
+      }
+      // Scores in base-2 units, x = s * scale * log2 e; p = 2^(x - m),
+      // exactly 1 where x is the max.
+      float xr[NT][KB][4], bm[NT];
+      bool up = false;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int u = 0; u < KB; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) xr[t][u][r] = s[t][u][r] * a.scale_log2;
+        if constexpr (kMasked) {
+          const int d = pos[t] - ts - 4 * grp;  // token ts + 4 grp + i is masked when i > d
+#pragma unroll
+          for (int u = 0; u < KB; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (u * kSub + r > d) xr[t][u][r] = -INFINITY;
+        }
+        bm[t] = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < KB; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) bm[t] = fmaxf(bm[t], xr[t][u][r]);
+        bm[t] = max_xor16(bm[t]);
+        bm[t] = max_xor32(bm[t]);
+        up = up || bm[t] > m[t] + kPrefillSlack;
+      }
+      // Lazy rescaling: the reference max moves only when some column's
+      // scores exceed it by more than 2^kPrefillSlack, so most steps skip
+      // the rescale; the probabilities then stay below 2^kPrefillSlack, and
+      // the result o / l does not depend on the reference.  Token 0 is in
+      // step 0 and every column attends it, so m is finite from the first
+      // step on (a tile whose columns did not move gets alpha = 1).
+      if (wave_any(up)) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const float mn = fmaxf(m[t], bm[t]);
+          const float alpha = fast_exp2(m[t] - mn);
+          lsum[t] *= alpha;
+#pragma unroll
+          for (int x = 0; x < 8; ++x) acc[t][x] *= alpha;
+          m[t] = mn;
+        }
+      }
+      // Probabilities as the B operands of the weighted-value products: for
+      // sub-tile pair h (sub-tiles 2h, 2h + 1) the hi halves of both (4
+      // tokens each, packed) and, separately, the lo halves.
+      uint4 bh[NT][KB / 2], bl[NT][KB / 2];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        float ps = 0.f;
+        uint32_t hw[KB][2], lw[KB][2];
+#pragma unroll
+        for (int u = 0; u < KB; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; r += 2) {
+            const float p0 = fast_exp2(xr[t][u][r] - m[t]);
+            const float p1 = fast_exp2(xr[t][u][r + 1] - m[t]);
+            ps += p0 + p1;
+            split_pair<T>(p0, p1, hw[u][r / 2], lw[u][r / 2]);
+          }
+        lsum[t] += ps;
 #pragma unroll
         for (int h = 0; h < KB / 2; ++h) {
-          const int tok0 = ts + 2 * h * kSub, tok1 = tok0 + kSub;
-          if (tok0 > last) continue;
-          const unsigned char* s0 = &stage[j & 1][2 * h][0] + kPrefillKBytes;
-          const unsigned char* s1 = &stage[j & 1][2 * h + 1][0] + kPrefillKBytes;
-          uint2 v0[8], v1[8];
+          bh[t][h] = make_uint4(hw[2 * h][0], hw[2 * h][1], hw[2 * h + 1][0], hw[2 * h + 1][1]);
+          bl[t][h] = make_uint4(lw[2 * h][0], lw[2 * h][1], lw[2 * h + 1][0], lw[2 * h + 1][1]);
+        }
+      }
+      // Weighted values, two sub-tiles per 32-deep product: A = this lane's
+      // 4 tokens of sub-tile 2h and of 2h + 1 (one dim), against the hi
+      // probabilities, then against the lo ones.
 #pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const int e = (x * 64 + grp * 16 + col) * 8;
-            v0[x] = *reinterpret_cast<const uint2*>(s0 + e);
-            v1[x] = *reinterpret_cast<const uint2*>(s1 + e);
-          }
+      for (int h = 0; h < KB / 2; ++h) {
+        const int tok0 = ts + 2 * h * kSub, tok1 = tok0 + kSub;
+        if constexpr (kMasked) {
+          if (tok0 > last) continue;
+        }
+        const unsigned char* s0 = &stage[j & 1][2 * h][0] + kPrefillKBytes;
+        const unsigned char* s1 = &stage[j & 1][2 * h + 1][0] + kPrefillKBytes;
+        uint2 v0[8], v1[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int e = (x * 64 + grp * 16 + col) * 8;
+          v0[x] = *reinterpret_cast<const uint2*>(s0 + e);
+          v1[x] = *reinterpret_cast<const uint2*>(s1 + e);
+        }
+        if constexpr (kMasked) {
           // Slots past the wave's last position may lie past the sequence
           // end and hold anything (NaN included; sub-tile 2h + 1 may lie
           // wholly past it): zero them so 0 * slot stays 0.
           if (last - tok0 + 1 < kSub) v_tail_mask(v0, last - tok0 + 1 - 4 * grp);
           if (last - tok1 + 1 < kSub) v_tail_mask(v1, last - tok1 + 1 - 4 * grp);
+        }
 #pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const uint4 va = make_uint4(v0[x].x, v0[x].y, v1[x].x, v1[x].y);
+        for (int x = 0; x < 8; ++x) {
+          const uint4 va = make_uint4(v0[x].x, v0[x].y, v1[x].x, v1[x].y);
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-              acc[t][x] = M::mma_32(va, bh[t][h], acc[t][x]);
-              acc[t][x] = M::mma_32(va, bl[t][h], acc[t][x]);
-            }
+          for (int t = 0; t < NT; ++t) {
+            acc[t][x] = M::mma_32(va, bh[t][h], acc[t][x]);
+            acc[t][x] = M::mma_32(va, bl[t][h], acc[t][x]);
           }
         }
       }
-      // step j + 1 to the other buffer (last read before the previous
-      // barrier), then step j + 2 starts loading: it has one step of
-      // compute to arrive
-      if (j + 1 < nstep) stage_store((j + 1) & 1);
-      gload(j + 2);
-      __syncthreads();
     }
-  }
+    // step j + 1 to the other buffer (last read before the previous
+    // barrier), then step j + 2 starts loading: it has one step of compute
+    // to arrive
+    if (j + 1 < nstep) stage_store((j + 1) & 1);
+    gload(j + 2);
+    __syncthreads();
+  };
+  // The first step crossing the wave's first row (0 for a wave without
+  // rows: every step then only stages and waits).
+  const int jd = last < 0 ? 0 : min(nstep, (L - n + ct0 * R + 1) / kStep);
+  int j = 0;
+  for (; j < jd; ++j) step(j, std::false_type{});
+  for (; j < nstep; ++j) step(j, std::true_type{});
   if (last < 0) return;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
