@@ -709,8 +709,8 @@ __device__ inline void fold_split(const Args& a, Smem& sm, const Piece& pc,
 // then counted in on the pair's counter a.pcnt[pair]; the workgroup whose
 // count-in completes the pair folds it.  Count-ins are batched: a
 // workgroup lists the contributions it published (sm.dpair) and counts
-// them in together (flush_members) after its prefix items, when the list
-// is full and at the end of its chunk, so no wave waits for a count-in in
+// them in together (flush_members) when the list is full, at the end of
+// its chunk and after its prefix items, so no wave waits for a count-in in
 // the middle of the stream.  Publication and reading follow the counter
 // protocol above (count_in: acquire-release at agent scope after every
 // wave's stores completed and a barrier; partials read after a barrier

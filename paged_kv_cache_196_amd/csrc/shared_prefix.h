@@ -25,8 +25,15 @@
 // Schedule.  Two unit spaces, each cut into nwg equal chunks: the items'
 // blocks (sub-group-major, then KV head, then block) and the private
 // blocks (sequence-major as in the ordinary decode, without the shared
-// blocks).  Workgroup k first runs its chunk of item units, counts their
-// contributions in, then streams its chunk of private units.
+// blocks).  Workgroup k streams its chunk of private units first and runs
+// its chunk of item units last (after its chunk-end folds).  An item's
+// fixed costs (staging the members' queries, merging the waves,
+// publishing, folding) leave the memory system idle; run last, they fall
+// where workgroups finish their streams at different times, while others
+// still stream (measured on the serving batch: items first 267 us per
+// call, items last on half the workgroups 264, on all 262; items placed
+// at staggered points inside the streams 290).  Contributions count in on
+// their pair's counter in any order.
 #pragma once
 
 #include "decode_mfma.h"
@@ -66,12 +73,12 @@ __device__ inline void block_scan(int n, F count, int* out, int* wsum) {
 }
 
 // Virtual units charged per (sequence, KV head) in the private unit space.
-// On the serving batch a workgroup's time after its prefix items measured
-// linear in its chunk's 16-token blocks (~0.3 us each) and pieces (~2 us
-// each: the merge across the waves, the publication and the fold at the
-// chunk end); charges of 7, 8, 10 and 13 blocks per piece measured 268,
-// 265, 266 and 269 us per call.
-constexpr int kPieceUnits = 8;
+// On the serving batch a workgroup's stream time measured linear in its
+// chunk's 16-token blocks (~0.3 us each) and pieces (~2 us each: the merge
+// across the waves, the publication and the fold at the chunk end); with
+// the items last, charges of 4, 5, 6, 7, 8 and 10 blocks per piece
+// measured 285, 264, 259.5, 260.3, 261.7 and 267 us per call.
+constexpr int kPieceUnits = 6;
 
 // Builds the shared-prefix schedule in dynamic LDS (SharedLayout, scalars
 // in sm.ssc).  A group of M >= 2 members with shared > 0 blocks is cut into
@@ -156,9 +163,8 @@ __device__ inline void shared_prologue(const Args& a, Smem& sm, int* wsum) {
 }
 
 // Sub-tiles in flight per wave in the item phase.  Two, as in the ordinary
-// engine, measured as fast as three (the most that fit the registers): at
-// the start of the kernel every workgroup fetches its items at once, and
-// the chip's bandwidth bounds them.
+// engine; three (the most that fit the registers) measured 1.5 us slower
+// per call on the serving batch.
 constexpr int kItemTiles = 2;
 
 // One piece of an item: blocks [j0, j1) of sub-group sg's shared blocks,
@@ -316,9 +322,33 @@ __device__ inline void item_piece(const Args& a, Smem& sm, const SharedInfo& si,
     for (int x = 0; x < 8; ++x)
       *reinterpret_cast<f32x4*>(&sm.o[wave][col][16 * x + 4 * grp]) = acc[x];
   }
+  // A whole item whose member has every private contribution counted in
+  // already is that pair's last contribution: the workgroup folds the pair
+  // from the merged item part without publishing it or counting in (the
+  // counter goes back to zero; nobody else touches it in this call).  The
+  // fold takes the contributions in the same order and arithmetic as
+  // fold_members, so the result does not depend on who folds.  Member
+  // flags in sm.dlast, layouts in sm.dlay (both free between count-ins).
+  if (whole && threadIdx.x < nm) {
+    const int b = b0 + threadIdx.x, L = si.lens[b];
+    int fast = 0;
+    if (L > 0 && blocks_of(L, B) != si.shb[b]) {
+      const int pair = b * a.Hkv + kvh;
+      const MemberLayout m = member_layout(a, si, pair);
+      if (counted(a.pcnt + pair) == m.nfr + m.npp - 1) {
+        fast = 1;
+        reset_count(a.pcnt + pair);
+        acquire_counted();
+        sm.dlay[threadIdx.x] = m;
+      }
+    }
+    sm.dlast[threadIdx.x] = fast;
+  }
   __syncthreads();
   constexpr int kOut = kWideCols * kD / kThreads;
-#pragma unroll
+  // not unrolled: the fold's loads of eight outputs at once would not fit
+  // the registers
+#pragma unroll 1
   for (int r = 0; r < kOut; ++r) {
     const int idx = threadIdx.x + r * kThreads;
     const int cc = idx / kD, d = idx % kD, cl = cc % 16, tile = cc / 16;
@@ -339,6 +369,38 @@ __device__ inline void item_piece(const Args& a, Smem& sm, const SharedInfo& si,
     if (whole) {
       if (blocks_of(L, B) == si.shb[b]) {
         store_out<T>(a.out, ((int64_t)b * a.Hq + kvh * G + g) * kD + d, o / l, a.out_f32);
+      } else if (sm.dlast[mi]) {
+        const MemberLayout& m = sm.dlay[mi];
+        const int E = m.nfr + m.npp;
+        float fm = -INFINITY, fl = 0.f, fo = 0.f;
+        for (int i0 = 0; i0 < E; i0 += 2) {
+          float vo[2], vm[2], vl[2];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            vo[j] = 0.f;
+            vm[j] = -INFINITY;
+            vl[j] = 0.f;
+            const int i = i0 + j;
+            if (i == 0) {  // the item part (the pair's first contribution)
+              vo[j] = o;
+              vm[j] = Mx;
+              vl[j] = l;
+            } else if (i < E) {
+              const float* po;
+              const float* pml;
+              member_contrib<G>(a, m, i, po, pml);
+              vo[j] = ld_agent(po + g * kD + d);
+              vm[j] = ld_agent(pml + g * 2);
+              vl[j] = ld_agent(pml + g * 2 + 1);
+            }
+          }
+          const float Mn = fmaxf(fm, fmaxf(vm[0], vm[1]));
+          const float f0 = rescale(fm, Mn), f1 = rescale(vm[0], Mn), f2 = rescale(vm[1], Mn);
+          fl = fl * f0 + f1 * vl[0] + f2 * vl[1];
+          fo = fo * f0 + f1 * vo[0] + f2 * vo[1];
+          fm = Mn;
+        }
+        store_out<T>(a.out, ((int64_t)b * a.Hq + kvh * G + g) * kD + d, fo / fl, a.out_f32);
       } else {
         st_agent(a.pair_o + ((int64_t)(2 * pair) * G + g) * kD + d, o);
         if (d == 0) {
@@ -355,11 +417,11 @@ __device__ inline void item_piece(const Args& a, Smem& sm, const SharedInfo& si,
     }
   }
   // list the members' contributions for the count-in (a whole item's
-  // member without private blocks is already final)
+  // member without private blocks, or folded above, is already final)
   if (threadIdx.x < 64) {
     const int b = b0 + lane;
     bool add = lane < nm && si.lens[b] > 0;
-    if (add && whole) add = blocks_of(si.lens[b], B) != si.shb[b];
+    if (add && whole) add = blocks_of(si.lens[b], B) != si.shb[b] && !sm.dlast[lane];
     const uint64_t am = __builtin_amdgcn_ballot_w64(add);
     const int n0 = sm.dn;
     if (add) {
@@ -393,9 +455,10 @@ __device__ inline void run_items(const Args& a, Smem& sm, int chunk) {
   if (uniform(sm.dn) > 0) flush_members<T, G, kMemberFoldU>(a, sm);
 }
 
-// The shared-prefix decode: prologue, this workgroup's item units, then
-// its private units with the ordinary streaming loop (member pieces publish
-// instead of writing out), the chunk-end folds and the last count-in.
+// The shared-prefix decode: prologue, this workgroup's private units with
+// the ordinary streaming loop (member pieces publish instead of writing
+// out), the chunk-end folds and count-in, then its item units and their
+// count-in.
 template <class T, int B, int G>
 __device__ inline void run_decode_shared(const Args& a) {
   using Engine = MfmaEngine<T, B, G, true>;
@@ -411,7 +474,6 @@ __device__ inline void run_decode_shared(const Args& a) {
   shared_prologue<B, G>(a, sm, wsum);
   const int chunk = chunk_of_wg(blockIdx.x, a.nwg);
   zero_empty_sequences<T>(a, chunk, shared_layout(a.S, a.ngroups).lens);
-  run_items<T, B, G>(a, sm, chunk);
   const SharedInfo si = shared_info(a, sm);
   const int W = si.cum[a.S] * a.Hkv;
   const int c = si.cP;
@@ -431,6 +493,9 @@ __device__ inline void run_decode_shared(const Args& a) {
     if (uniform(sm.dn) > Smem::kDefers - Smem::kBatch) flush_members<T, G, 1>(a, sm);
   }
   finish_chunk<T, G>(a, sm);
+  // after the chunk-end folds: an item's merge reuses the LDS that holds
+  // the own partial of a late split
+  run_items<T, B, G>(a, sm, chunk);
 }
 
 }  // namespace pa
