@@ -39,6 +39,8 @@
 #include "decode_mfma.h"
 #include "pa_device.h"
 
+#include <type_traits>
+
 namespace pa {
 
 // Exclusive prefix sum of count(i), i < n, into out[0..n] (out[n] = total),
@@ -346,10 +348,15 @@ __device__ inline void item_piece(const Args& a, Smem& sm, const SharedInfo& si,
   }
   __syncthreads();
   constexpr int kOut = kWideCols * kD / kThreads;
-  // not unrolled: the fold's loads of eight outputs at once would not fit
-  // the registers
-#pragma unroll 1
+  // item part of each of this thread's outputs that a fast member folds
+  // below (pf = member + 1; 0: none)
+  float po[kOut], pm[kOut], pl[kOut];
+  int pf[kOut];
+#pragma unroll
   for (int r = 0; r < kOut; ++r) {
+    pf[r] = 0;
+    po[r] = pl[r] = 0.f;
+    pm[r] = -INFINITY;
     const int idx = threadIdx.x + r * kThreads;
     const int cc = idx / kD, d = idx % kD, cl = cc % 16, tile = cc / 16;
     const int mi = cc / G, g = cc % G;
@@ -370,37 +377,10 @@ __device__ inline void item_piece(const Args& a, Smem& sm, const SharedInfo& si,
       if (blocks_of(L, B) == si.shb[b]) {
         store_out<T>(a.out, ((int64_t)b * a.Hq + kvh * G + g) * kD + d, o / l, a.out_f32);
       } else if (sm.dlast[mi]) {
-        const MemberLayout& m = sm.dlay[mi];
-        const int E = m.nfr + m.npp;
-        float fm = -INFINITY, fl = 0.f, fo = 0.f;
-        for (int i0 = 0; i0 < E; i0 += 2) {
-          float vo[2], vm[2], vl[2];
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            vo[j] = 0.f;
-            vm[j] = -INFINITY;
-            vl[j] = 0.f;
-            const int i = i0 + j;
-            if (i == 0) {  // the item part (the pair's first contribution)
-              vo[j] = o;
-              vm[j] = Mx;
-              vl[j] = l;
-            } else if (i < E) {
-              const float* po;
-              const float* pml;
-              member_contrib<G>(a, m, i, po, pml);
-              vo[j] = ld_agent(po + g * kD + d);
-              vm[j] = ld_agent(pml + g * 2);
-              vl[j] = ld_agent(pml + g * 2 + 1);
-            }
-          }
-          const float Mn = fmaxf(fm, fmaxf(vm[0], vm[1]));
-          const float f0 = rescale(fm, Mn), f1 = rescale(vm[0], Mn), f2 = rescale(vm[1], Mn);
-          fl = fl * f0 + f1 * vl[0] + f2 * vl[1];
-          fo = fo * f0 + f1 * vo[0] + f2 * vo[1];
-          fm = Mn;
-        }
-        store_out<T>(a.out, ((int64_t)b * a.Hq + kvh * G + g) * kD + d, fo / fl, a.out_f32);
+        pf[r] = mi + 1;
+        po[r] = o;
+        pm[r] = Mx;
+        pl[r] = l;
       } else {
         st_agent(a.pair_o + ((int64_t)(2 * pair) * G + g) * kD + d, o);
         if (d == 0) {
@@ -416,6 +396,74 @@ __device__ inline void item_piece(const Args& a, Smem& sm, const SharedInfo& si,
       }
     }
   }
+  // The fast members' folds: contributions two at a time (the item part
+  // first), in the order and arithmetic of fold_members, for half of this
+  // thread's outputs at a time with all their loads in flight together
+  // (the whole set at once does not fit the registers).
+  auto fold_fast = [&](auto half) {
+    constexpr int kU = kOut / 2, r0 = decltype(half)::value * kU;
+    int emax = 0;
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (pf[r0 + u]) emax = max(emax, sm.dlay[pf[r0 + u] - 1].nfr + sm.dlay[pf[r0 + u] - 1].npp);
+    if (emax == 0) return;
+    float fm[kU], fl[kU], fo[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      fm[u] = -INFINITY;
+      fl[u] = fo[u] = 0.f;
+    }
+    for (int i0 = 0; i0 < emax; i0 += 2) {
+      float vo[kU][2], vm[kU][2], vl[kU][2];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int r = r0 + u, idx = threadIdx.x + r * kThreads;
+        const int g = (idx / kD) % G, d = idx % kD;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          vo[u][j] = 0.f;
+          vm[u][j] = -INFINITY;
+          vl[u][j] = 0.f;
+          if (!pf[r]) continue;
+          const MemberLayout& m = sm.dlay[pf[r] - 1];
+          const int i = i0 + j;
+          if (i == 0) {
+            vo[u][j] = po[r];
+            vm[u][j] = pm[r];
+            vl[u][j] = pl[r];
+          } else if (i < m.nfr + m.npp) {
+            const float* co;
+            const float* cml;
+            member_contrib<G>(a, m, i, co, cml);
+            vo[u][j] = ld_agent(co + g * kD + d);
+            vm[u][j] = ld_agent(cml + g * 2);
+            vl[u][j] = ld_agent(cml + g * 2 + 1);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const float Mn = fmaxf(fm[u], fmaxf(vm[u][0], vm[u][1]));
+        const float f0 = rescale(fm[u], Mn), f1 = rescale(vm[u][0], Mn), f2 = rescale(vm[u][1], Mn);
+        fl[u] = fl[u] * f0 + f1 * vl[u][0] + f2 * vl[u][1];
+        fo[u] = fo[u] * f0 + f1 * vo[u][0] + f2 * vo[u][1];
+        fm[u] = Mn;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int r = r0 + u;
+      if (!pf[r]) continue;
+      const int idx = threadIdx.x + r * kThreads;
+      const int cc = idx / kD, d = idx % kD, g = cc % G;
+      const int b = b0 + pf[r] - 1;
+      store_out<T>(a.out, ((int64_t)b * a.Hq + kvh * G + g) * kD + d, fo[u] / fl[u], a.out_f32);
+    }
+  };
+  static_assert(kOut % 2 == 0, "outputs fold in two halves");
+  fold_fast(std::integral_constant<int, 0>{});
+  __builtin_amdgcn_sched_barrier(0);
+  fold_fast(std::integral_constant<int, 1>{});
   // list the members' contributions for the count-in (a whole item's
   // member without private blocks, or folded above, is already final)
   if (threadIdx.x < 64) {
