@@ -43,26 +43,34 @@ namespace pa {
 constexpr int kPrefillStepSub = 4;           // 16-token sub-tiles per step (one softmax update)
 constexpr int kPrefillKRow = kD * 2 + 16;     // LDS bytes per K row (padded: rows 4 banks apart)
 constexpr int kPrefillKBytes = kSub * kPrefillKRow;
-// one sub-tile: K rows, then the V^T group as 8-byte entries (4 tokens of
-// one dim) in the order [dim / 16][token quarter][dim % 16], so the 16
-// lanes of one LDS read cycle (one token quarter, 16 dims) read 128
-// contiguous bytes
-constexpr int kPrefillStage = kPrefillKBytes + kSub * kD * 2;
+// A pair of sub-tiles (2h, 2h + 1) in LDS: the K rows of both, then their
+// V^T as 16-byte entries in the order [dim / 16][token quarter][dim % 16],
+// entry = 4 tokens of one dim from sub-tile 2h, then the same 4 tokens'
+// places in 2h + 1: exactly the A operand of one 32-deep weighted-value
+// product, so a lane reads it with one 16-byte load, and the 16 lanes of
+// one LDS cycle (one token quarter, 16 dims) read 256 contiguous bytes.
+constexpr int kPrefillVPair = 2 * kSub * kD * 2;
+constexpr int kPrefillPair = 2 * kPrefillKBytes + kPrefillVPair;
 static_assert(kPrefillThreads * 16 == kSub * kD * 2, "one K and one V chunk per thread per sub-tile");
 
 // Reference-max slack of the prefill's lazy rescaling (log2 units).
 constexpr float kPrefillSlack = 8.f;
 static_assert(kPrefillStepSub % 2 == 0, "weighted values take sub-tiles in pairs");
 
-// Zero the V^T entries of tokens past `nv` (tokens 4 grp .. of this lane,
-// nv = valid tokens among them) in the 8 dim tiles.
-__device__ __forceinline__ void v_tail_mask(uint2 (&v)[8], int nv) {
-  const uint32_t lo_mask = (nv >= 1 ? 0x0000ffffu : 0u) | (nv >= 2 ? 0xffff0000u : 0u);
-  const uint32_t hi_mask = (nv >= 3 ? 0x0000ffffu : 0u) | (nv >= 4 ? 0xffff0000u : 0u);
+// Zero the V^T entries of tokens past the valid ones in the 8 dim tiles
+// of a pair entry: nv0 / nv1 = valid tokens among this lane's 4 of
+// sub-tile 2h (halves x, y) / of 2h + 1 (halves z, w).
+__device__ __forceinline__ void v_tail_mask(uint4 (&v)[8], int nv0, int nv1) {
+  const uint32_t m0 = (nv0 >= 1 ? 0x0000ffffu : 0u) | (nv0 >= 2 ? 0xffff0000u : 0u);
+  const uint32_t m1 = (nv0 >= 3 ? 0x0000ffffu : 0u) | (nv0 >= 4 ? 0xffff0000u : 0u);
+  const uint32_t m2 = (nv1 >= 1 ? 0x0000ffffu : 0u) | (nv1 >= 2 ? 0xffff0000u : 0u);
+  const uint32_t m3 = (nv1 >= 3 ? 0x0000ffffu : 0u) | (nv1 >= 4 ? 0xffff0000u : 0u);
 #pragma unroll
   for (int x = 0; x < 8; ++x) {
-    v[x].x &= lo_mask;
-    v[x].y &= hi_mask;
+    v[x].x &= m0;
+    v[x].y &= m1;
+    v[x].z &= m2;
+    v[x].w &= m3;
   }
 }
 
@@ -118,7 +126,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   constexpr int kRowsBlock = prefill_rows_per_block<G>();
   constexpr int kTileBytes = B * kD * 2;
   constexpr int kStep = KB * kSub;  // tokens per step
-  __shared__ __align__(16) unsigned char stage[2][KB][kPrefillStage];
+  __shared__ __align__(16) unsigned char stage[2][KB / 2][kPrefillPair];
 
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
   const int wave = uniform(threadIdx.x >> 6);
@@ -165,13 +173,15 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   }
 
   // This thread's 2 x 16 bytes of every sub-tile: K chunk c (token c / 16,
-  // dims 8 (c % 16) ..) and V^T chunk c (dim c / 2, tokens 8 (c % 2) .. + 8,
-  // i.e. token quarters 2 (c % 2) and 2 (c % 2) + 1), c = threadIdx.x, and
-  // where they go in the LDS stage.
+  // dims 8 (c % 16) ..), c = threadIdx.x, and the V^T chunk of dim vdim,
+  // tokens 8 vh .. + 8 (token quarters 2 vh and 2 vh + 1), with 16
+  // consecutive lanes on 16 consecutive dims of one quarter (their LDS
+  // stores hit distinct banks); where they go in the pair's stage.
   const int c16 = threadIdx.x;
-  const int vdim = c16 / 2, vq = 2 * (c16 % 2);
+  const int vdim = c16 % 16 + 16 * (c16 / 32), vh = (c16 / 16) % 2;
+  const int v_src = (vdim * 2 + vh) * 16;
   const int k_off = c16 / 16 * kPrefillKRow + c16 % 16 * 16;
-  const int v_off = kPrefillKBytes + (vdim / 16 * 64 + vq * 16 + vdim % 16) * 8;
+  const int v_off = 2 * kPrefillKBytes + (vdim / 16 * 64 + 2 * vh * 16 + vdim % 16) * 16;
   const int kvp = pool_head(a, kvh);
   const int last_sub = last_blk / kSub;
   const int nstep = last_blk / kStep + 1;
@@ -204,16 +214,17 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
       const int bytes = uniform(live ? kTileBytes : 0);
       const int soff = ((live ? sub : last_sub) * kSub % B) * kD * 2;
       gk[u] = tile_load16<kCachedPolicy>(tile_rsrc(a.kp, tile, bytes), c16 * 16, soff);
-      gv[u] = tile_load16<kCachedPolicy>(tile_rsrc(a.vp, tile, bytes), c16 * 16, soff);
+      gv[u] = tile_load16<kCachedPolicy>(tile_rsrc(a.vp, tile, bytes), v_src, soff);
     }
   };
   auto stage_store = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
-      unsigned char* dst = &stage[buf][u][0];
-      *reinterpret_cast<uint4*>(dst + k_off) = gk[u];
-      *reinterpret_cast<uint2*>(dst + v_off) = make_uint2(gv[u].x, gv[u].y);
-      *reinterpret_cast<uint2*>(dst + v_off + 16 * 8) = make_uint2(gv[u].z, gv[u].w);  // next quarter
+      unsigned char* dst = &stage[buf][u / 2][0];
+      *reinterpret_cast<uint4*>(dst + (u % 2) * kPrefillKBytes + k_off) = gk[u];
+      *reinterpret_cast<uint2*>(dst + v_off + (u % 2) * 8) = make_uint2(gv[u].x, gv[u].y);
+      // the next token quarter
+      *reinterpret_cast<uint2*>(dst + v_off + 16 * 16 + (u % 2) * 8) = make_uint2(gv[u].z, gv[u].w);
     }
   };
   gtab(0);
@@ -240,7 +251,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
       f32x4 s[NT][KB];
 #pragma unroll
       for (int u = 0; u < KB; ++u) {
-        const unsigned char* su = &stage[j & 1][u][0];
+        const unsigned char* su = &stage[j & 1][u / 2][0] + (u % 2) * kPrefillKBytes;
         uint4 kr[4];
 #pragma unroll
         for (int x = 0; x < 4; ++x)
@@ -321,37 +332,30 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
         }
       }
       // Weighted values, two sub-tiles per 32-deep product: A = this lane's
-      // 4 tokens of sub-tile 2h and of 2h + 1 (one dim), against the hi
-      // probabilities, then against the lo ones.
+      // 4 tokens of sub-tile 2h and of 2h + 1 (one dim, one 16-byte LDS
+      // entry), against the hi probabilities, then against the lo ones.
 #pragma unroll
       for (int h = 0; h < KB / 2; ++h) {
         const int tok0 = ts + 2 * h * kSub, tok1 = tok0 + kSub;
         if constexpr (kMasked) {
           if (tok0 > last) continue;
         }
-        const unsigned char* s0 = &stage[j & 1][2 * h][0] + kPrefillKBytes;
-        const unsigned char* s1 = &stage[j & 1][2 * h + 1][0] + kPrefillKBytes;
-        uint2 v0[8], v1[8];
+        const unsigned char* sv = &stage[j & 1][h][0] + 2 * kPrefillKBytes;
+        uint4 va[8];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const int e = (x * 64 + grp * 16 + col) * 8;
-          v0[x] = *reinterpret_cast<const uint2*>(s0 + e);
-          v1[x] = *reinterpret_cast<const uint2*>(s1 + e);
-        }
+        for (int x = 0; x < 8; ++x) va[x] = *reinterpret_cast<const uint4*>(sv + (x * 64 + grp * 16 + col) * 16);
         if constexpr (kMasked) {
           // Slots past the wave's last position may lie past the sequence
           // end and hold anything (NaN included; sub-tile 2h + 1 may lie
           // wholly past it): zero them so 0 * slot stays 0.
-          if (last - tok0 + 1 < kSub) v_tail_mask(v0, last - tok0 + 1 - 4 * grp);
-          if (last - tok1 + 1 < kSub) v_tail_mask(v1, last - tok1 + 1 - 4 * grp);
+          if (last - tok1 + 1 < kSub) v_tail_mask(va, last - tok0 + 1 - 4 * grp, last - tok1 + 1 - 4 * grp);
         }
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
-          const uint4 va = make_uint4(v0[x].x, v0[x].y, v1[x].x, v1[x].y);
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
-            acc[t][x] = M::mma_32(va, bh[t][h], acc[t][x]);
-            acc[t][x] = M::mma_32(va, bl[t][h], acc[t][x]);
+            acc[t][x] = M::mma_32(va[x], bh[t][h], acc[t][x]);
+            acc[t][x] = M::mma_32(va[x], bl[t][h], acc[t][x]);
           }
         }
       }
