@@ -74,6 +74,54 @@ __device__ inline void block_scan(int n, F count, int* out, int* wsum) {
   __syncthreads();
 }
 
+// Exclusive prefix sums of count1(i), i < n1, into out1[0..n1] and of
+// count2(i), i < n2, into out2[0..n2], in one set of passes (the two take
+// the barriers of one).  All threads call; wsum holds 2 * kWaves ints of
+// LDS.
+template <class F1, class F2>
+__device__ inline void block_scan2(int n1, F1 count1, int* out1, int n2, F2 count2, int* out2,
+                                   int* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int c1 = 0, c2 = 0;
+  for (int base = 0; base < max(n1, n2); base += kThreads) {
+    const int i = base + tid;
+    int x = i < n1 ? count1(i) : 0, y = i < n2 ? count2(i) : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int u = __shfl_up(x, off), v = __shfl_up(y, off);
+      if (lane >= off) {
+        x += u;
+        y += v;
+      }
+    }
+    if (lane == 63) {
+      wsum[wave] = x;
+      wsum[kWaves + wave] = y;
+    }
+    __syncthreads();
+    int b1 = c1, t1 = c1, b2 = c2, t2 = c2;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      if (w < wave) {
+        b1 += wsum[w];
+        b2 += wsum[kWaves + w];
+      }
+      t1 += wsum[w];
+      t2 += wsum[kWaves + w];
+    }
+    if (i < n1) out1[i + 1] = b1 + x;
+    if (i < n2) out2[i + 1] = b2 + y;
+    c1 = t1;
+    c2 = t2;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    out1[0] = 0;
+    out2[0] = 0;
+  }
+  __syncthreads();
+}
+
 // Virtual units charged per (sequence, KV head) in the private unit space.
 // On the serving batch a workgroup's stream time measured linear in its
 // chunk's 16-token blocks (~0.3 us each) and pieces (~2 us each: the merge
@@ -88,7 +136,7 @@ constexpr int kPieceUnits = 6;
 // Group bounds are clamped to [0, S], so malformed groups cannot address
 // outside the arrays (their results are undefined; pa_validate_shared_host
 // rejects them).  The lengths and the group arrays are read from global
-// memory in one pass.  All threads call.
+// memory in one pass.  All threads call; wsum holds 2 * kWaves ints.
 template <int B, int G, class Smem>
 __device__ inline void shared_prologue(const Args& a, Smem& sm, int* wsum) {
   constexpr int kMmax = kWideCols / G;
@@ -126,12 +174,18 @@ __device__ inline void shared_prologue(const Args& a, Smem& sm, int* wsum) {
     for (int i = 0; i < n; ++i) {
       const int s = l.gbase[g] + i;
       if (s >= S) break;  // only overlapping (invalid) groups get here
-      const int f = st + (i * M) / n, e = st + ((i + 1) * M) / n;
+      const int f = st + (i * M) / n, e = st + ((i + 1) * M) / n;  // e - f <= kMmax
       int lmax = 0, ref = f;
-      for (int b = f; b < e; ++b) {
-        const int L = l.lens[b];
-        const int lim = min(L, shtok);
-        if (L > 0) {
+      // the members' lengths first, all reads in flight at once
+      int Ls[kMmax];
+#pragma unroll
+      for (int k = 0; k < kMmax; ++k) Ls[k] = f + k < e ? l.lens[f + k] : 0;
+#pragma unroll
+      for (int k = 0; k < kMmax; ++k) {
+        const int b = f + k;
+        if (b >= e) break;
+        const int lim = min(Ls[k], shtok);
+        if (Ls[k] > 0) {
           l.shb[b] = blocks_of(lim, B);
           l.seq_sg[b] = s;
         }
@@ -148,11 +202,10 @@ __device__ inline void shared_prologue(const Args& a, Smem& sm, int* wsum) {
   }
   __syncthreads();
   const int nsg = min(l.gbase[ng], S);
-  block_scan(S, [&](int b) {
+  block_scan2(S, [&](int b) {
     const int np = blocks_of(l.lens[b], B) - l.shb[b];
     return np > 0 ? np + kPieceUnits : 0;
-  }, l.cum, wsum);
-  block_scan(nsg, [&](int s) { return blocks_of(l.sg_len[s], B); }, l.icum, wsum);
+  }, l.cum, nsg, [&](int s) { return blocks_of(l.sg_len[s], B); }, l.icum, wsum);
   if (threadIdx.x == 0) {
     sm.ssc.nsg = nsg;
     sm.ssc.B = B;
@@ -511,7 +564,7 @@ template <class T, int B, int G>
 __device__ inline void run_decode_shared(const Args& a) {
   using Engine = MfmaEngine<T, B, G, true>;
   using Smem = typename Engine::Smem;
-  __shared__ int wsum[kWaves];
+  __shared__ int wsum[2 * kWaves];
   __shared__ Smem sm;
   if (threadIdx.x == 0) {
     sm.fold_late = 0;
