@@ -18,17 +18,19 @@
 // of rows); wave w takes kPrefillTiles column tiles of the block.  A column
 // tile holds R = 16 / G consecutive query rows times the G query heads of
 // the KV head: 16 MFMA columns, column c = (row c / G, head c % G), each
-// with its own causal limit.  The workgroup walks 16-token K/V sub-tiles
-// from token 0 up to its largest position; each sub-tile is read from
-// memory once per workgroup (one 16-byte load per thread, issued
-// kPrefillDepth sub-tiles ahead), staged in a double-buffered LDS tile and
-// read from there by every wave that still has rows attending it:
-//   S^T[16 tok][16 cols] = K[16][128] . Q^T[128][16]   4 x mfma 16x16x32
-//   O^T[128][16 cols]   += V^T[128][16] . P^T[16][16]  8 dim tiles x mfma 16x16x32 (hi + lo P)
-// (operand layouts and the hi + lo split of P as in the decode engine), with
-// a running max and sum per column.  Workgroups run longest rows first
-// across the batch, and the blocks of one (sequence, KV head) go to one XCD
-// (workgroup i runs on XCD i mod 8), so they share its L2.
+// with its own causal limit.  The workgroup walks the keys in 64-token
+// steps of four 16-token K/V sub-tiles from token 0 up to its largest
+// position; each sub-tile is read from memory once per workgroup (one
+// 16-byte K and one V load per thread, one step ahead), staged in a
+// double-buffered LDS stage and read from there by every wave that still
+// has rows attending it:
+//   S^T[16 tok][16 cols] = K[16][128] . Q^T[128][16]        4 x mfma 16x16x32 per sub-tile
+//   O^T[128][16 cols]   += V^T[128][32] . P^T[32][16]        8 dim tiles x mfma 16x16x32 per
+//                                                            sub-tile pair (bf16: hi, then lo P)
+// (operand layouts as in the decode engine), with a running max and sum per
+// column.  Workgroups run longest rows first across the batch, and the
+// blocks of one (sequence, KV head) go to one XCD (workgroup i runs on XCD
+// i mod 8), so they share its L2.
 #pragma once
 
 #include "decode_mfma.h"
@@ -74,27 +76,28 @@ __device__ __forceinline__ void v_tail_mask(uint4 (&v)[8], int nv0, int nv1) {
   }
 }
 
-// Probabilities p0, p1 as hi and lo pairs in the input type, p ~= hi + lo.
-// bf16: hi is p with its low 16 bits cut off (the upper halves of both, one
-// byte permute), lo the exact remainder rounded to bf16; p <= 2^8 here and
-// |lo| < 2^-7 p, so the pair keeps about 16 bits.  f16: hi rounded to
-// nearest, lo the rounded remainder.
+// Whether the weighted values take P as hi + lo (two products per pair of
+// sub-tiles) or as P rounded to the input type alone.  bf16 keeps 8 bits:
+// alone, the worst error in a CPU simulation of 2048-token causal prompts
+// (N(0,1) data, K scaled up to 2x) reached 2.4-3.9e-3, over the 2e-3 bar,
+// even with the sum taken over the rounded P.  fp16 keeps 11 bits: alone,
+// with the sum over the same rounded P, the worst was 7.2e-4.
 template <class T>
-__device__ __forceinline__ void split_pair(float p0, float p1, uint32_t& hi, uint32_t& lo) {
-  typedef typename std::conditional<T::kCode == BF16::kCode, __bf16, _Float16>::type E;
-  typedef E pair __attribute__((ext_vector_type(2)));
-  if constexpr (T::kCode == BF16::kCode) {
-    const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
-    hi = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
-    const pair r = {(E)(p0 - __uint_as_float(b0 & 0xffff0000u)),
-                    (E)(p1 - __uint_as_float(b1 & 0xffff0000u))};
-    lo = __builtin_bit_cast(uint32_t, r);
-  } else {
-    const pair h = {(E)p0, (E)p1};
-    hi = __builtin_bit_cast(uint32_t, h);
-    const pair r = {(E)(p0 - (float)h.x), (E)(p1 - (float)h.y)};
-    lo = __builtin_bit_cast(uint32_t, r);
-  }
+constexpr bool prefill_p_split() {
+  return T::kCode == BF16::kCode;
+}
+
+// bf16: probabilities p0, p1 as hi and lo pairs, p ~= hi + lo: hi is p with
+// its low 16 bits cut off (the upper halves of both, one byte permute), lo
+// the exact remainder rounded to bf16; p <= 2^8 here and |lo| < 2^-7 p, so
+// the pair keeps about 16 bits.
+__device__ __forceinline__ void split_pair_bf16(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+  typedef __bf16 pair __attribute__((ext_vector_type(2)));
+  const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
+  hi = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+  const pair r = {(__bf16)(p0 - __uint_as_float(b0 & 0xffff0000u)),
+                  (__bf16)(p1 - __uint_as_float(b1 & 0xffff0000u))};
+  lo = __builtin_bit_cast(uint32_t, r);
 }
 
 // Rows of one workgroup's block for group size G.
@@ -126,6 +129,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   constexpr int kRowsBlock = prefill_rows_per_block<G>();
   constexpr int kTileBytes = B * kD * 2;
   constexpr int kStep = KB * kSub;  // tokens per step
+  constexpr bool kSplit = prefill_p_split<T>();
+  typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
   __shared__ __align__(16) unsigned char stage[2][KB / 2][kPrefillPair];
 
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
@@ -321,19 +326,28 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
           for (int r = 0; r < 4; r += 2) {
             const float p0 = fast_exp2(xr[t][u][r] - m[t]);
             const float p1 = fast_exp2(xr[t][u][r + 1] - m[t]);
-            ps += p0 + p1;
-            split_pair<T>(p0, p1, hw[u][r / 2], lw[u][r / 2]);
+            if constexpr (kSplit) {
+              ps += p0 + p1;
+              split_pair_bf16(p0, p1, hw[u][r / 2], lw[u][r / 2]);
+            } else {
+              // P rounded once; the sum is over the same rounded values
+              const half2_t h = {(_Float16)p0, (_Float16)p1};
+              hw[u][r / 2] = __builtin_bit_cast(uint32_t, h);
+              ps = __builtin_amdgcn_fdot2(h, half2_t{(_Float16)1.f, (_Float16)1.f}, ps, false);
+            }
           }
         lsum[t] += ps;
 #pragma unroll
         for (int h = 0; h < KB / 2; ++h) {
           bh[t][h] = make_uint4(hw[2 * h][0], hw[2 * h][1], hw[2 * h + 1][0], hw[2 * h + 1][1]);
-          bl[t][h] = make_uint4(lw[2 * h][0], lw[2 * h][1], lw[2 * h + 1][0], lw[2 * h + 1][1]);
+          if constexpr (kSplit)
+            bl[t][h] = make_uint4(lw[2 * h][0], lw[2 * h][1], lw[2 * h + 1][0], lw[2 * h + 1][1]);
         }
       }
       // Weighted values, two sub-tiles per 32-deep product: A = this lane's
       // 4 tokens of sub-tile 2h and of 2h + 1 (one dim, one 16-byte LDS
-      // entry), against the hi probabilities, then against the lo ones.
+      // entry), against the hi probabilities, then (bf16) against the lo
+      // ones.
 #pragma unroll
       for (int h = 0; h < KB / 2; ++h) {
         const int tok0 = ts + 2 * h * kSub, tok1 = tok0 + kSub;
@@ -355,7 +369,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
             acc[t][x] = M::mma_32(va[x], bh[t][h], acc[t][x]);
-            acc[t][x] = M::mma_32(va[x], bl[t][h], acc[t][x]);
+            if constexpr (kSplit) acc[t][x] = M::mma_32(va[x], bl[t][h], acc[t][x]);
           }
         }
       }

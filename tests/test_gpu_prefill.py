@@ -105,6 +105,16 @@ def test_prefill_first_row_is_value_row_and_single_row_is_decode(O):
     assert torch.max(torch.abs(pre - dec)).item() <= 1e-4
 
 
+def test_prefill_f16_whole_prompt_every_row(O):
+    """fp16 inputs take P rounded to fp16 alone in the weighted values (the
+    row sums over the same rounded values): one whole 2048-token GQA 32/8
+    prompt, every row against the oracle's prefill at the same bar."""
+    w, q, qs = workload.prefill_workload(seed=11, num_prompts=1, dtype="f16")
+    err = max_err(_run(w, q, qs), _oracle(O, w, q, qs))
+    _log(f"[prefill] f16 2048-token prompt max_abs_err={err:.3e}")
+    assert err <= TOL["f16"]
+
+
 def test_prefill_gqa_prompt_batch_full_size(O):
     """The benchmarked prefill workload (8 whole prompts of 2048 tokens, GQA
     32/8, bf16, B = 16), output buffer filled with NaN first: every element

@@ -378,12 +378,15 @@ def prefill_queries(w: Workload, q_lens, seed: int):
 PREFILL_NAME = "prefill GQA 32/8 heads, 8 whole prompts x 2048 tokens, bf16, B=16"
 
 
-def prefill_workload(seed: int = 6, num_prompts: int = 8, prompt_len: int = 2048):
+def prefill_workload(seed: int = 6, num_prompts: int = 8, prompt_len: int = 2048,
+                     dtype: str = "bf16"):
     """Prompt prefill over the paged cache with the GQA batch's head shapes:
     num_prompts whole prompts of prompt_len tokens, their K/V already in
     shuffled physical blocks, every token a query row.  Returns
     (w, q storage [num_prompts * prompt_len][32][128], q_start)."""
-    w = build(name=PREFILL_NAME, dtype="bf16", seq_lens=[prompt_len] * num_prompts,
+    name = PREFILL_NAME if (num_prompts, prompt_len, dtype) == (8, 2048, "bf16") else \
+        f"prefill GQA 32/8 heads, {num_prompts} whole prompts x {prompt_len} tokens, {dtype}, B=16"
+    w = build(name=name, dtype=dtype, seq_lens=[prompt_len] * num_prompts,
               num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, seed=seed)
     q, q_start = prefill_queries(w, [prompt_len] * num_prompts, seed)
     return w, q, q_start
