@@ -445,14 +445,16 @@ def eviction_scores(w, kp, vp, dev, flush, stream, with_cpu: bool) -> dict:
     return res
 
 
-def prefill_timing(dev, flush, stream, with_cpu: bool) -> dict:
+def prefill_timing(dev, flush, stream, with_cpu: bool, dtype: str = "bf16") -> dict:
     """Causal paged prefill (paged_attn_prefill) of 8 whole prompts of 2048
     tokens with the GQA batch's head shapes (32 query / 8 KV heads, D 128,
-    bf16, B 16, shuffled blocks), bf16 output.  Algorithmic flops: 4 * D per
-    (query row, query head, attended key): 2 D for q.k and 2 D for the
-    weighted value sum; row i of a whole prompt attends i + 1 keys.  Timed
-    with HIP events; the oracle is timed on a bounded sample (the last 32
-    rows of the first prompt)."""
+    B 16, shuffled blocks), inputs and output in `dtype` (bf16: the
+    benchmarked prefill; f16: the same prompts in fp16, whose weighted values
+    take P in fp16 alone).  Algorithmic flops: 4 * D per (query row, query
+    head, attended key): 2 D for q.k and 2 D for the weighted value sum; row
+    i of a whole prompt attends i + 1 keys.  Timed with HIP events; the
+    oracle is timed on a bounded sample (the last 32 rows of the first
+    prompt).  The matrix peak is the same for both types."""
     import numpy as np
     import torch
 
@@ -460,7 +462,8 @@ def prefill_timing(dev, flush, stream, with_cpu: bool) -> dict:
     import workload
     from workload import to_device as device_tensor
 
-    w, q, qs = workload.prefill_workload()
+    w, q, qs = workload.prefill_workload(dtype=dtype)
+    out_type = torch.bfloat16 if dtype == "bf16" else torch.float16
     n = np.diff(qs).astype(np.int64)
     L = w.seq_lens.astype(np.int64)
     keys = int(sum(((Lb - nb + 1) + Lb) * nb // 2 for Lb, nb in zip(L, n)))  # sum of (p + 1)
@@ -468,11 +471,11 @@ def prefill_timing(dev, flush, stream, with_cpu: bool) -> dict:
     args = [device_tensor(q, w.dtype), device_tensor(w.k_pool, w.dtype),
             device_tensor(w.v_pool, w.dtype), torch.from_numpy(w.block_tables).to(dev),
             torch.from_numpy(w.seq_lens).to(dev), torch.from_numpy(qs).to(dev)]
-    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(q.shape, dtype=out_type, device=dev)
     max_q = int(n.max())
     mean, med = _time_events(
         lambda: pa.prefill(*args, float(w.scale), max_q_len=max_q, out=out,
-                           out_dtype=torch.bfloat16, stream=stream, check_rows=False),
+                           out_dtype=out_type, stream=stream, check_rows=False),
         flush, stream, 10)
     tflops = flops / (mean * 1e-3) / 1e12
     res = {
@@ -860,6 +863,7 @@ def main() -> int:
         del kp, vp
     if not args.no_prefill:
         result["prefill"] = prefill_timing(dev, flush, stream, with_cpu=not args.no_cpu_baseline)
+        result["prefill_f16"] = prefill_timing(dev, flush, stream, with_cpu=False, dtype="f16")
     print(json.dumps(result), flush=True)
     return 0
 
