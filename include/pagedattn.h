@@ -303,9 +303,13 @@ int32_t pa_validate_shared_host(const pa_desc* desc, const int32_t* block_tables
  * max_q_len >= every n_b (launch size; rows beyond it are not computed).
  * Pools, block_tables, seq_lens, scale, dtype, out_dtype: as for
  * paged_attn_decode.  No workspace.  Matrix cores only: fp16 / bf16 with
- * kernel AUTO or MFMA, else PA_ERR_UNSUPPORTED.  Data-dependent
- * preconditions are checked by pa_validate_prefill_host, not on the device;
- * a sequence with n_b > seq_lens[b] is skipped by the kernel. */
+ * kernel AUTO or MFMA, else PA_ERR_UNSUPPORTED.  Accuracy as for the
+ * decode (fp32 accumulation, max |out - exact| <= 2e-3 for 16-bit inputs):
+ * bf16 probabilities enter the weighted values as two bf16 halves (about
+ * 16 bits), fp16 probabilities rounded once to fp16 with the row sums over
+ * the same rounded values.  Data-dependent preconditions are checked by
+ * pa_validate_prefill_host, not on the device; a sequence with
+ * n_b > seq_lens[b] is skipped by the kernel. */
 int32_t paged_attn_prefill(const void* q, const void* k_pool, const void* v_pool,
                            const int32_t* block_tables, const int32_t* seq_lens,
                            const int32_t* q_start, int32_t max_q_len, float scale, void* out,
