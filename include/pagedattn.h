@@ -168,7 +168,10 @@ int32_t pa_validate_host(const pa_desc* desc, const int32_t* block_tables_host,
 /* Checks a descriptor alone (what every launching entry point checks). */
 int32_t pa_check_desc(const pa_desc* desc);
 
-/* Paged decode attention: one kernel launch on `stream`.  All pointers are
+/* Paged decode attention: one kernel launch on `stream` per 8192
+ * sequences (the launch keeps its batch's length prefix in LDS; a larger
+ * batch runs as consecutive launches over sequences 0-8191, 8192-16383,
+ * ..., each with the same workspace).  All pointers are
  * device pointers in the layouts above; `scale` multiplies q.k
  * (1/sqrt(head_dim) for standard attention).  workspace: device buffer of
  * at least pa_workspace_bytes(desc) bytes, zeroed before its first use.
@@ -195,8 +198,8 @@ int32_t paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
  * the layouts above; results are those of paged_attn_decode (same kernels,
  * same fold order).
  *
- * Two launches on `stream`: a small kernel that zeroes the split counters,
- * then the decode kernel.  Every call on one GPU shares that GPU's array,
+ * Two launches on `stream` per 8192 sequences: a small kernel that zeroes
+ * the split counters, then the decode kernel.  Every call on one GPU shares that GPU's array,
  * which keeps the last call's contents: calls that overlap on one GPU (on
  * different streams, or from different host threads without ordering)
  * race and may produce wrong results; order them on one stream.
@@ -213,7 +216,8 @@ int32_t paged_attn_decode_noalloc(const void* q, const void* k_pool, const void*
 
 /* Number of decode workgroups a launch uses for this descriptor on the
  * current device (the split-K granularity: CUs x resident workgroups per
- * CU), or -1 on error or when the workgroup's LDS does not fit a CU. */
+ * CU; of each launch, for a batch of more than 8192 sequences), or -1 on
+ * error or when the workgroup's LDS does not fit a CU. */
 int32_t pa_decode_grid(const pa_desc* desc);
 
 /* ------------------------------------------------------------------
@@ -244,13 +248,14 @@ int32_t pa_decode_grid(const pa_desc* desc);
  * than two members or no shared block run as ordinary sequences.
  *
  * Built for fp16 / bf16 on the matrix-core kernel with G = Hq/Hkv in
- * {1, 2, 4, 8}; for every other descriptor (and for num_groups == 0) the
- * call runs paged_attn_decode with the same workspace, so results are
- * always defined.
+ * {1, 2, 4, 8} and batches of at most 8192 sequences; for every other
+ * descriptor (and for num_groups == 0) the call runs paged_attn_decode
+ * with the same workspace, so results are always defined.
  *
  * workspace: at least pa_shared_workspace_bytes(desc) bytes, zero-filled
  * before its first use; every call leaves it zeroed again.  One launch on
- * `stream`.  Errors as for paged_attn_decode, plus PA_ERR_SHAPE for
+ * `stream` (paged_attn_decode's launches when it runs that).  Errors as
+ * for paged_attn_decode, plus PA_ERR_SHAPE for
  * num_groups < 0 and PA_ERR_NULL for missing group arrays; PA_ERR_UNSUPPORTED
  * when the schedule of this batch and its groups does not fit the
  * workgroup's LDS (about 36 bytes per sequence and 4 per group besides the
@@ -264,8 +269,8 @@ int32_t paged_attn_decode_shared(const void* q, const void* k_pool, const void* 
 
 /* Workspace bytes of paged_attn_decode_shared (the ordinary decode's
  * workspace, then per-(sequence, KV head) arrival counters and partials,
- * and partials of shared parts cut by chunk boundaries); 0 on a bad
- * descriptor. */
+ * and partials of shared parts cut by chunk boundaries; the ordinary
+ * decode's alone for more than 8192 sequences); 0 on a bad descriptor. */
 size_t pa_shared_workspace_bytes(const pa_desc* desc);
 
 /* Workgroups of a paged_attn_decode_shared launch for this descriptor and

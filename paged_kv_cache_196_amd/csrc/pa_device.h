@@ -18,7 +18,7 @@ constexpr int kSub = 16;         // tokens per sub-tile (unit of the streaming l
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxGrid = 2048;   // upper bound on decode workgroups (sizes the workspace)
 constexpr int kWideCols = 32;    // MFMA columns of a prefix item: members x query heads
-constexpr int kMaxSeqs = 8192;   // sequences per call (LDS prefix array)
+constexpr int kMaxSeqs = 8192;   // sequences per decode launch (LDS prefix array); larger batches run in slices
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

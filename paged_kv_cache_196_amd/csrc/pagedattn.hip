@@ -174,6 +174,10 @@ SharedWs shared_ws_layout(const pa_desc* d) {
   // the leading part also serves the plain decode these calls fall back to
   const int g_plain = plan_decode(d).G;
   size_t off = al(ws_layout_bytes(kMaxGrid, 2 * kMaxGrid, std::max((int)G, g_plain)));
+  if (d->num_seqs > kMaxSeqs) {  // runs as the ordinary decode: the leading part alone
+    w.pcnt = w.pair_o = w.pair_ml = w.wide_o = w.wide_ml = w.total = off;
+    return w;
+  }
   w.pcnt = off;
   off = al(off + sizeof(int) * pairs);
   w.pair_o = off;
@@ -262,6 +266,29 @@ PrefillPlan plan_prefill(const pa_desc* d) {
 
 using namespace pa;
 
+// A decode launch keeps its batch's length prefix in LDS, so it takes at
+// most kMaxSeqs sequences: a larger batch runs as consecutive launches of
+// at most kMaxSeqs sequences on the caller's stream.  Sequences are
+// independent, and every launch leaves the workspace's counters at zero
+// for the next.  call(slice descriptor, first sequence) launches one.
+template <class F>
+static int32_t decode_in_slices(const void* q, const int32_t* bt, const int32_t* lens, void* out,
+                                const pa_desc* d, F call) {
+  if (!q || !bt || !lens || !out) return PA_ERR_NULL;
+  pa_desc ds = *d;
+  for (int32_t s0 = 0; s0 < d->num_seqs; s0 += kMaxSeqs) {
+    ds.num_seqs = std::min(kMaxSeqs, d->num_seqs - s0);
+    const int32_t st = call(&ds, s0);
+    if (st != PA_OK) return st;
+  }
+  return PA_OK;
+}
+
+// Byte offset of sequence s0's rows in q (input type) or out (output type).
+static int64_t rows_bytes(const pa_desc* d, int64_t s0, int32_t dtype) {
+  return s0 * d->num_q_heads * d->head_dim * (int64_t)pa_dtype_size(dtype);
+}
+
 extern "C" {
 
 const char* pa_status_str(int32_t s) {
@@ -311,11 +338,10 @@ int32_t pa_check_desc(const pa_desc* d) {
   if (d->block_size != 16 && d->block_size != 32) return PA_ERR_UNSUPPORTED;
   if (d->kernel < PA_KERNEL_AUTO || d->kernel > PA_KERNEL_MFMA) return PA_ERR_UNSUPPORTED;
   if (d->kernel == PA_KERNEL_MFMA && d->dtype == PA_F32) return PA_ERR_UNSUPPORTED;
-  if (d->num_seqs > kMaxSeqs) return PA_ERR_UNSUPPORTED;
   const Plan p = plan_decode(d);
   if (!p.v.launch) return PA_ERR_UNSUPPORTED;
-  // flat unit indices are int32
-  if ((int64_t)d->num_seqs * d->max_blocks_per_seq * p.hkv >= ((int64_t)1 << 31))
+  // flat unit indices of one decode launch (at most kMaxSeqs sequences) are int32
+  if ((int64_t)std::min(d->num_seqs, kMaxSeqs) * d->max_blocks_per_seq * p.hkv >= ((int64_t)1 << 31))
     return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
@@ -376,7 +402,7 @@ static int plan_grid(const Plan& p, int S) {
 
 int32_t pa_decode_grid(const pa_desc* d) {
   if (pa_check_desc(d) != PA_OK) return -1;
-  return plan_grid(plan_decode(d), d->num_seqs);
+  return plan_grid(plan_decode(d), std::min(d->num_seqs, kMaxSeqs));
 }
 
 // Checks the call (a caller workspace too when check_ws) and fills every
@@ -432,6 +458,13 @@ int32_t paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
   int grid = 0;
   const int32_t st0 = pa_check_desc(d);
   if (st0 != PA_OK) return st0;
+  if (d->num_seqs > kMaxSeqs)
+    return decode_in_slices(q, bt, lens, out, d, [&](const pa_desc* ds, int64_t s0) {
+      return paged_attn_decode(static_cast<const char*>(q) + rows_bytes(d, s0, d->dtype), k_pool,
+                               v_pool, bt + s0 * d->max_blocks_per_seq, lens + s0, scale,
+                               static_cast<char*>(out) + rows_bytes(d, s0, d->out_dtype), ds, ws,
+                               ws_bytes, stream);
+    });
   const Plan p = plan_decode(d);
   const int32_t st = prepare(q, k_pool, v_pool, bt, lens, scale, out, d, p, true, ws, ws_bytes,
                              &a, &grid);
@@ -449,6 +482,13 @@ int32_t paged_attn_decode_noalloc(const void* q, const void* k_pool, const void*
   int grid = 0;
   const int32_t st0 = pa_check_desc(d);
   if (st0 != PA_OK) return st0;
+  if (d->num_seqs > kMaxSeqs)
+    return decode_in_slices(q, bt, lens, out, d, [&](const pa_desc* ds, int64_t s0) {
+      return paged_attn_decode_noalloc(static_cast<const char*>(q) + rows_bytes(d, s0, d->dtype),
+                                       k_pool, v_pool, bt + s0 * d->max_blocks_per_seq, lens + s0,
+                                       scale, static_cast<char*>(out) + rows_bytes(d, s0, d->out_dtype),
+                                       ds, stream);
+    });
   // A column-split group whose partials would overflow the static scratch
   // runs as virtual groups of 16 heads instead.
   Plan p = plan_decode(d);
@@ -514,6 +554,7 @@ int32_t pa_validate_shared_host(const pa_desc* d, const int32_t* bt, const int32
 
 int32_t pa_decode_shared_grid(const pa_desc* d, int32_t num_groups) {
   if (pa_check_desc(d) != PA_OK || num_groups < 0) return -1;
+  if (d->num_seqs > kMaxSeqs) return pa_decode_grid(d);  // runs as the ordinary decode
   const DeviceInfo info = device_info();
   if (!info.ok) return -1;
   const Variant v = pick_shared(d);
@@ -537,7 +578,10 @@ int32_t paged_attn_decode_shared(const void* q, const void* k_pool, const void* 
   if (d->num_seqs > 0 && (!ws || ws_bytes < shared_ws_layout(d).total || ((uintptr_t)ws & 15u)))
     return PA_ERR_WORKSPACE;
   const Variant v = pick_shared(d);
-  if (num_groups == 0 || !v.launch)  // no group to share, or not the matrix-core kernel
+  // no group to share, not the matrix-core kernel, or a batch whose
+  // schedule does not fit the workgroup's LDS (more than kMaxSeqs
+  // sequences: the ordinary decode, in slices)
+  if (num_groups == 0 || !v.launch || d->num_seqs > kMaxSeqs)
     return paged_attn_decode(q, k_pool, v_pool, bt, lens, scale, out, d, ws, ws_bytes, stream);
   Args a;
   int grid = 0;

@@ -91,11 +91,22 @@ def _desc(**kw):
     ("num_q_heads", 0, 2), ("num_kv_heads", 3, 2), ("num_seqs", -1, 2), ("block_size", 0, 2),
     ("num_blocks", 0, 2), ("max_blocks_per_seq", 0, 2), ("dtype", 5, 3), ("out_dtype", pa.PA_F16, 3),
     ("head_dim", 64, 4), ("block_size", 8, 4), ("block_size", 48, 4), ("kernel", 9, 4),
-    ("max_blocks_per_seq", 1 << 26, 4), ("num_seqs", 9000, 4), ("cached_prefix_blocks", -1, 2),
+    ("max_blocks_per_seq", 1 << 26, 4), ("cached_prefix_blocks", -1, 2),
 ])
 def test_descriptor_errors(lib, field, value, code):
     assert pa.pa_check_desc(_desc()) == 0
     assert pa.pa_check_desc(_desc(**{field: value})) == code
+
+
+def test_batches_beyond_one_launch_are_accepted(lib):
+    """A batch of more than 8192 sequences is valid (the decode runs it as
+    launches of at most 8192); the int32 flat-unit bound applies to one
+    launch's sequences."""
+    assert pa.pa_check_desc(_desc(num_seqs=9000)) == 0
+    assert pa.pa_check_desc(_desc(num_seqs=1 << 20, max_blocks_per_seq=4096)) == 0
+    # 8192 sequences x 32768 blocks x 8 KV heads = 2^31 units in one launch
+    assert pa.pa_check_desc(_desc(num_seqs=9000, max_blocks_per_seq=1 << 15)) == 4
+    assert pa.pa_check_desc(_desc(num_seqs=8191, max_blocks_per_seq=1 << 15)) == 0
 
 
 def test_descriptor_fields_match_the_header():

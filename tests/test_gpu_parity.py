@@ -9,7 +9,8 @@ import torch
 
 import oracle
 import workload
-from tests.gpu_util import TOL, Uploaded, kernels_for, max_err
+import paged_kv_cache_196_amd as pa
+from tests.gpu_util import TOL, Uploaded, desc_of, kernels_for, max_err, run_shared
 
 pytestmark = pytest.mark.gpu
 
@@ -126,8 +127,8 @@ def test_all_sequences_empty():
 
 @pytest.mark.parametrize("kern", ["mfma", "valu"])
 def test_max_batch_many_pieces_per_chunk(O, kern):
-    """The largest batch the library takes (8192 sequences: the length
-    prefix in LDS at capacity) with lengths 0..100, one in ten empty: the
+    """The largest batch one decode launch takes (8192 sequences: the
+    length prefix in LDS at capacity) with lengths 0..100, one in ten empty: the
     length scan runs 32 passes with carries, empty sequences sit between the
     pieces, and every chunk meets ~57 (sequence, KV head) pairs, so its
     pieces are listed and streamed in more than one batch."""
@@ -141,6 +142,37 @@ def test_max_batch_many_pieces_per_chunk(O, kern):
     err = max_err(Uploaded(w).run(kern), ref)
     _log(f"[parity] max batch kernel={kern} max_abs_err={err:.3e}")
     assert err <= TOL["bf16"], err
+
+
+def test_batch_beyond_one_launch(O):
+    """More sequences than one decode launch takes (8192: the length prefix
+    in LDS): 17,000 sequences of 0..40 tokens run as three launches (8192,
+    8192, 616), each on its own rows of q, the table, the lengths and out.
+    Groups of four share two leading blocks, so the shared-prefix entry
+    takes the ordinary decode's slices too, and the allocation-free entry
+    slices the same way: all three give the same bits, within the bar of
+    the oracle."""
+    S = 17000
+    rng = np.random.default_rng(S)
+    lens = rng.integers(0, 41, size=S)
+    lens[rng.random(S) < 0.1] = 0
+    w = workload.build(name="beyond-one-launch", dtype="bf16", seq_lens=lens, num_q_heads=8,
+                       num_kv_heads=2, head_dim=128, block_size=16, seed=78, prefix_group=4,
+                       prefix_blocks=2)
+    _log(f"[parity] {S} sequences in slices")
+    ref = O.run_workload(w)
+    up = Uploaded(w)
+    plain = up.run("auto")
+    err = max_err(plain, ref)
+    _log(f"[parity] {S} sequences max_abs_err={err:.3e}")
+    assert err <= TOL["bf16"], err
+    assert torch.equal(run_shared(up), plain)
+    desc = desc_of(up)
+    no_alloc = torch.full(up.q.shape, float("nan"), dtype=torch.float32, device=up.q.device)
+    pa.paged_attn_decode_noalloc(up.q, up.k, up.v, up.bt, up.lens, float(w.scale), no_alloc, desc,
+                                 torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(no_alloc, plain)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
