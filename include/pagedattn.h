@@ -310,9 +310,13 @@ int32_t pa_validate_shared_host(const pa_desc* desc, const int32_t* block_tables
  * paged_attn_decode.  No workspace.  Matrix cores only: fp16 / bf16 with
  * kernel AUTO or MFMA, else PA_ERR_UNSUPPORTED.  Accuracy as for the
  * decode (fp32 accumulation, max |out - exact| <= 2e-3 for 16-bit inputs):
- * bf16 probabilities enter the weighted values as two bf16 halves (about
- * 16 bits), fp16 probabilities rounded once to fp16 with the row sums over
- * the same rounded values.  Data-dependent preconditions are checked by
+ * the probabilities enter the weighted values rounded once to fp16, with
+ * the row sums over the same rounded values.  bf16 V is converted to fp16
+ * as it is staged (exact for magnitudes in [2^-17, 2^16); smaller ones
+ * move by less than 2^-24); a workgroup that meets a V value of magnitude
+ * 2^16 or more (or an infinity) reruns its rows with V in bf16 and the
+ * probabilities as two bf16 halves (about 16 bits).  Data-dependent
+ * preconditions are checked by
  * pa_validate_prefill_host, not on the device; a sequence with
  * n_b > seq_lens[b] is skipped by the kernel. */
 int32_t paged_attn_prefill(const void* q, const void* k_pool, const void* v_pool,

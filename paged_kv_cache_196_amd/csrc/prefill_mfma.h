@@ -26,7 +26,8 @@
 // has rows attending it:
 //   S^T[16 tok][16 cols] = K[16][128] . Q^T[128][16]        4 x mfma 16x16x32 per sub-tile
 //   O^T[128][16 cols]   += V^T[128][32] . P^T[32][16]        8 dim tiles x mfma 16x16x32 per
-//                                                            sub-tile pair (bf16: hi, then lo P)
+//                                                            sub-tile pair (fp16 V and P; see
+//                                                            the weighted-value modes below)
 // (operand layouts as in the decode engine), with a running max and sum per
 // column.  Workgroups run longest rows first across the batch, and the
 // blocks of one (sequence, KV head) go to one XCD (workgroup i runs on XCD
@@ -76,15 +77,30 @@ __device__ __forceinline__ void v_tail_mask(uint4 (&v)[8], int nv0, int nv1) {
   }
 }
 
-// Whether the weighted values take P as hi + lo (two products per pair of
-// sub-tiles) or as P rounded to the input type alone.  bf16 keeps 8 bits:
-// alone, the worst error in a CPU simulation of 2048-token causal prompts
-// (N(0,1) data, K scaled up to 2x) reached 2.4-3.9e-3, over the 2e-3 bar,
-// even with the sum taken over the rounded P.  fp16 keeps 11 bits: alone,
-// with the sum over the same rounded P, the worst was 7.2e-4.
-template <class T>
-constexpr bool prefill_p_split() {
-  return T::kCode == BF16::kCode;
+// How the weighted values take V and P.  P rounded to bf16 alone (8 bits)
+// is not enough: the worst error in a CPU simulation of 2048-token causal
+// prompts (N(0,1) data, K scaled up to 2x) reached 2.4-3.9e-3, over the
+// 2e-3 bar, even with the sum taken over the rounded P.  P rounded to fp16
+// alone (11 bits), with the sum over the same rounded values, gave 7.2e-4
+// on fp16 data and 7.4e-4 on bf16 data.  So:
+//  kPvF16   fp16 inputs: V as stored, P rounded to fp16, one product per
+//           pair of sub-tiles;
+//  kPvConv  bf16 inputs: V converted to fp16 as it is staged (exact for
+//           every bf16 value of magnitude in [2^-17, 2^16); smaller ones
+//           move by less than 2^-24), then as kPvF16.  A workgroup that
+//           stages a V value of magnitude 2^16 or more (beyond fp16) reruns
+//           with kPvSplit;
+//  kPvSplit bf16: V as stored, P as hi + lo (two products per pair).
+constexpr int kPvF16 = 0, kPvConv = 1, kPvSplit = 2;
+constexpr float kPvConvLimit = 65536.f;  // smallest bf16 magnitude fp16 cannot hold
+
+// Two bf16 values (low half first) as two fp16 values, and the larger
+// magnitude folded into vmax (NaN ignored).  Round toward zero: every value
+// the conversion must keep is representable, so the mode does not matter.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, float& vmax) {
+  const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
+  vmax = fmaxf(fmaxf(vmax, fabsf(lo)), fabsf(hi));
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 
 // bf16: probabilities p0, p1 as hi and lo pairs, p ~= hi + lo: hi is p with
@@ -129,7 +145,6 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   constexpr int kRowsBlock = prefill_rows_per_block<G>();
   constexpr int kTileBytes = B * kD * 2;
   constexpr int kStep = KB * kSub;  // tokens per step
-  constexpr bool kSplit = prefill_p_split<T>();
   typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
   __shared__ __align__(16) unsigned char stage[2][KB / 2][kPrefillPair];
 
@@ -169,13 +184,6 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
 
   f32x4 acc[NT][8];
   float m[NT], lsum[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-#pragma unroll
-    for (int x = 0; x < 8; ++x) acc[t][x] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m[t] = -INFINITY;
-    lsum[t] = 0.f;
-  }
 
   // This thread's 2 x 16 bytes of every sub-tile: K chunk c (token c / 16,
   // dims 8 (c % 16) ..), c = threadIdx.x, and the V^T chunk of dim vdim,
@@ -222,171 +230,212 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
       gv[u] = tile_load16<kCachedPolicy>(tile_rsrc(a.vp, tile, bytes), v_src, soff);
     }
   };
-  auto stage_store = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      unsigned char* dst = &stage[buf][u / 2][0];
-      *reinterpret_cast<uint4*>(dst + (u % 2) * kPrefillKBytes + k_off) = gk[u];
-      *reinterpret_cast<uint2*>(dst + v_off + (u % 2) * 8) = make_uint2(gv[u].x, gv[u].y);
-      // the next token quarter
-      *reinterpret_cast<uint2*>(dst + v_off + 16 * 16 + (u % 2) * 8) = make_uint2(gv[u].z, gv[u].w);
-    }
-  };
-  gtab(0);
-  gload(0);
-  stage_store(0);
-  gload(1);
-  __syncthreads();
+  __shared__ int v_overflow;  // kPvConv: some staged V value is beyond fp16
 
-  // Step j is in LDS buffer j & 1 and step j + 1 in flight in gk / gv.
-  // Steps wholly at or below the wave's first row need no causal mask
-  // (every live column attends all their tokens; padding columns are never
-  // stored) and run without any mask code or branch; the steps from the
-  // diagonal on run with it.  The rescale decision is taken once per step
-  // for both column tiles, so the exponentials, the splits and the
-  // weighted-value products of a step form one straight run in which one
-  // tile's products overlap the other tile's vector work.
-  auto step = [&](const int j, auto masked) {
-    constexpr bool kMasked = decltype(masked)::value;
-    const int ts = j * kStep;
-    if (!kMasked || ts <= last) {
-      // Every sub-tile of the step is scored, also those past the wave's
-      // last position (zeros or stale tokens in LDS; the causal mask
-      // removes them), so the products need no branches or zero fills.
-      f32x4 s[NT][KB];
+  // One pass over the keys with the weighted values in mode kMode; for
+  // kPvConv, whether the workgroup staged a V value fp16 cannot hold (the
+  // pass is then void and reruns with kPvSplit).
+  auto run = [&](auto mode) -> bool {
+    constexpr int kMode = decltype(mode)::value;
+    constexpr bool kSplit = kMode == kPvSplit;
+    using MP = MfmaEngine<typename std::conditional<kSplit, T, F16>::type, B, G>;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int x = 0; x < 8; ++x) acc[t][x] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m[t] = -INFINITY;
+      lsum[t] = 0.f;
+    }
+    float vmax = 0.f;
+    auto stage_store = [&](int buf) {
 #pragma unroll
       for (int u = 0; u < KB; ++u) {
-        const unsigned char* su = &stage[j & 1][u / 2][0] + (u % 2) * kPrefillKBytes;
-        uint4 kr[4];
+        unsigned char* dst = &stage[buf][u / 2][0];
+        uint4 v = gv[u];
+        if constexpr (kMode == kPvConv) {
+          v.x = bf16x2_to_f16x2(v.x, vmax);
+          v.y = bf16x2_to_f16x2(v.y, vmax);
+          v.z = bf16x2_to_f16x2(v.z, vmax);
+          v.w = bf16x2_to_f16x2(v.w, vmax);
+        }
+        *reinterpret_cast<uint4*>(dst + (u % 2) * kPrefillKBytes + k_off) = gk[u];
+        *reinterpret_cast<uint2*>(dst + v_off + (u % 2) * 8) = make_uint2(v.x, v.y);
+        // the next token quarter
+        *reinterpret_cast<uint2*>(dst + v_off + 16 * 16 + (u % 2) * 8) = make_uint2(v.z, v.w);
+      }
+    };
+
+    // Step j is in LDS buffer j & 1 and step j + 1 in flight in gk / gv.
+    // Steps wholly at or below the wave's first row need no causal mask
+    // (every live column attends all their tokens; padding columns are never
+    // stored) and run without any mask code or branch; the steps from the
+    // diagonal on run with it.  The rescale decision is taken once per step
+    // for both column tiles, so the exponentials, the splits and the
+    // weighted-value products of a step form one straight run in which one
+    // tile's products overlap the other tile's vector work.
+    auto step = [&](const int j, auto masked) {
+      constexpr bool kMasked = decltype(masked)::value;
+      const int ts = j * kStep;
+      if (!kMasked || ts <= last) {
+        // Every sub-tile of the step is scored, also those past the wave's
+        // last position (zeros or stale tokens in LDS; the causal mask
+        // removes them), so the products need no branches or zero fills.
+        f32x4 s[NT][KB];
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-          kr[x] = *reinterpret_cast<const uint4*>(su + col * kPrefillKRow + (32 * x + 8 * grp) * 2);
+        for (int u = 0; u < KB; ++u) {
+          const unsigned char* su = &stage[j & 1][u / 2][0] + (u % 2) * kPrefillKBytes;
+          uint4 kr[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            kr[x] = *reinterpret_cast<const uint4*>(su + col * kPrefillKRow + (32 * x + 8 * grp) * 2);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            s[t][u] = M::mma_qk(kr[0], qop[t][0], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int x = 1; x < 4; ++x) s[t][u] = M::mma_qk(kr[x], qop[t][x], s[t][u]);
+          }
+        }
+        // Scores in base-2 units, x = s * scale * log2 e; p = 2^(x - m),
+        // exactly 1 where x is the max.
+        float xr[NT][KB][4], bm[NT];
+        bool up = false;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          s[t][u] = M::mma_qk(kr[0], qop[t][0], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-          for (int x = 1; x < 4; ++x) s[t][u] = M::mma_qk(kr[x], qop[t][x], s[t][u]);
-        }
-      }
-      // Scores in base-2 units, x = s * scale * log2 e; p = 2^(x - m),
-      // exactly 1 where x is the max.
-      float xr[NT][KB][4], bm[NT];
-      bool up = false;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int u = 0; u < KB; ++u)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) xr[t][u][r] = s[t][u][r] * a.scale_log2;
-        if constexpr (kMasked) {
-          const int d = pos[t] - ts - 4 * grp;  // token ts + 4 grp + i is masked when i > d
 #pragma unroll
           for (int u = 0; u < KB; ++u)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (u * kSub + r > d) xr[t][u][r] = -INFINITY;
-        }
-        bm[t] = -INFINITY;
+            for (int r = 0; r < 4; ++r) xr[t][u][r] = s[t][u][r] * a.scale_log2;
+          if constexpr (kMasked) {
+            const int d = pos[t] - ts - 4 * grp;  // token ts + 4 grp + i is masked when i > d
 #pragma unroll
-        for (int u = 0; u < KB; ++u)
+            for (int u = 0; u < KB; ++u)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) bm[t] = fmaxf(bm[t], xr[t][u][r]);
-        bm[t] = max_xor16(bm[t]);
-        bm[t] = max_xor32(bm[t]);
-        up = up || bm[t] > m[t] + kPrefillSlack;
-      }
-      // Lazy rescaling: the reference max moves only when some column's
-      // scores exceed it by more than 2^kPrefillSlack, so most steps skip
-      // the rescale; the probabilities then stay below 2^kPrefillSlack, and
-      // the result o / l does not depend on the reference.  Token 0 is in
-      // step 0 and every column attends it, so m is finite from the first
-      // step on (a tile whose columns did not move gets alpha = 1).
-      if (wave_any(up)) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const float mn = fmaxf(m[t], bm[t]);
-          const float alpha = fast_exp2(m[t] - mn);
-          lsum[t] *= alpha;
-#pragma unroll
-          for (int x = 0; x < 8; ++x) acc[t][x] *= alpha;
-          m[t] = mn;
-        }
-      }
-      // Probabilities as the B operands of the weighted-value products: for
-      // sub-tile pair h (sub-tiles 2h, 2h + 1) the hi halves of both (4
-      // tokens each, packed) and, separately, the lo halves.
-      uint4 bh[NT][KB / 2], bl[NT][KB / 2];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        float ps = 0.f;
-        uint32_t hw[KB][2], lw[KB][2];
-#pragma unroll
-        for (int u = 0; u < KB; ++u)
-#pragma unroll
-          for (int r = 0; r < 4; r += 2) {
-            const float p0 = fast_exp2(xr[t][u][r] - m[t]);
-            const float p1 = fast_exp2(xr[t][u][r + 1] - m[t]);
-            if constexpr (kSplit) {
-              ps += p0 + p1;
-              split_pair_bf16(p0, p1, hw[u][r / 2], lw[u][r / 2]);
-            } else {
-              // P rounded once; the sum is over the same rounded values
-              const half2_t h = {(_Float16)p0, (_Float16)p1};
-              hw[u][r / 2] = __builtin_bit_cast(uint32_t, h);
-              ps = __builtin_amdgcn_fdot2(h, half2_t{(_Float16)1.f, (_Float16)1.f}, ps, false);
-            }
+              for (int r = 0; r < 4; ++r)
+                if (u * kSub + r > d) xr[t][u][r] = -INFINITY;
           }
-        lsum[t] += ps;
+          bm[t] = -INFINITY;
 #pragma unroll
-        for (int h = 0; h < KB / 2; ++h) {
-          bh[t][h] = make_uint4(hw[2 * h][0], hw[2 * h][1], hw[2 * h + 1][0], hw[2 * h + 1][1]);
-          if constexpr (kSplit)
-            bl[t][h] = make_uint4(lw[2 * h][0], lw[2 * h][1], lw[2 * h + 1][0], lw[2 * h + 1][1]);
+          for (int u = 0; u < KB; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bm[t] = fmaxf(bm[t], xr[t][u][r]);
+          bm[t] = max_xor16(bm[t]);
+          bm[t] = max_xor32(bm[t]);
+          up = up || bm[t] > m[t] + kPrefillSlack;
         }
-      }
-      // Weighted values, two sub-tiles per 32-deep product: A = this lane's
-      // 4 tokens of sub-tile 2h and of 2h + 1 (one dim, one 16-byte LDS
-      // entry), against the hi probabilities, then (bf16) against the lo
-      // ones.
-#pragma unroll
-      for (int h = 0; h < KB / 2; ++h) {
-        const int tok0 = ts + 2 * h * kSub, tok1 = tok0 + kSub;
-        if constexpr (kMasked) {
-          if (tok0 > last) continue;
-        }
-        const unsigned char* sv = &stage[j & 1][h][0] + 2 * kPrefillKBytes;
-        uint4 va[8];
-#pragma unroll
-        for (int x = 0; x < 8; ++x) va[x] = *reinterpret_cast<const uint4*>(sv + (x * 64 + grp * 16 + col) * 16);
-        if constexpr (kMasked) {
-          // Slots past the wave's last position may lie past the sequence
-          // end and hold anything (NaN included; sub-tile 2h + 1 may lie
-          // wholly past it): zero them so 0 * slot stays 0.
-          if (last - tok1 + 1 < kSub) v_tail_mask(va, last - tok0 + 1 - 4 * grp, last - tok1 + 1 - 4 * grp);
-        }
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
+        // Lazy rescaling: the reference max moves only when some column's
+        // scores exceed it by more than 2^kPrefillSlack, so most steps skip
+        // the rescale; the probabilities then stay below 2^kPrefillSlack, and
+        // the result o / l does not depend on the reference.  Token 0 is in
+        // step 0 and every column attends it, so m is finite from the first
+        // step on (a tile whose columns did not move gets alpha = 1).
+        if (wave_any(up)) {
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
-            acc[t][x] = M::mma_32(va[x], bh[t][h], acc[t][x]);
-            if constexpr (kSplit) acc[t][x] = M::mma_32(va[x], bl[t][h], acc[t][x]);
+            const float mn = fmaxf(m[t], bm[t]);
+            const float alpha = fast_exp2(m[t] - mn);
+            lsum[t] *= alpha;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) acc[t][x] *= alpha;
+            m[t] = mn;
+          }
+        }
+        // Probabilities as the B operands of the weighted-value products:
+        // for sub-tile pair h (sub-tiles 2h, 2h + 1) the values of both (4
+        // tokens each, packed): fp16, or (kPvSplit) the bf16 hi halves and,
+        // separately, the lo halves.
+        uint4 bh[NT][KB / 2], bl[NT][KB / 2];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          float ps = 0.f;
+          uint32_t hw[KB][2], lw[KB][2];
+#pragma unroll
+          for (int u = 0; u < KB; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; r += 2) {
+              const float p0 = fast_exp2(xr[t][u][r] - m[t]);
+              const float p1 = fast_exp2(xr[t][u][r + 1] - m[t]);
+              if constexpr (kSplit) {
+                ps += p0 + p1;
+                split_pair_bf16(p0, p1, hw[u][r / 2], lw[u][r / 2]);
+              } else {
+                // P rounded once; the sum is over the same rounded values
+                const half2_t h = {(_Float16)p0, (_Float16)p1};
+                hw[u][r / 2] = __builtin_bit_cast(uint32_t, h);
+                ps = __builtin_amdgcn_fdot2(h, half2_t{(_Float16)1.f, (_Float16)1.f}, ps, false);
+              }
+            }
+          lsum[t] += ps;
+#pragma unroll
+          for (int h = 0; h < KB / 2; ++h) {
+            bh[t][h] = make_uint4(hw[2 * h][0], hw[2 * h][1], hw[2 * h + 1][0], hw[2 * h + 1][1]);
+            if constexpr (kSplit)
+              bl[t][h] = make_uint4(lw[2 * h][0], lw[2 * h][1], lw[2 * h + 1][0], lw[2 * h + 1][1]);
+          }
+        }
+        // Weighted values, two sub-tiles per 32-deep product: A = this
+        // lane's 4 tokens of sub-tile 2h and of 2h + 1 (one dim, one 16-byte
+        // LDS entry), against the probabilities (kPvSplit: the hi ones, then
+        // the lo ones).
+#pragma unroll
+        for (int h = 0; h < KB / 2; ++h) {
+          const int tok0 = ts + 2 * h * kSub, tok1 = tok0 + kSub;
+          if constexpr (kMasked) {
+            if (tok0 > last) continue;
+          }
+          const unsigned char* sv = &stage[j & 1][h][0] + 2 * kPrefillKBytes;
+          uint4 va[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) va[x] = *reinterpret_cast<const uint4*>(sv + (x * 64 + grp * 16 + col) * 16);
+          if constexpr (kMasked) {
+            // Slots past the wave's last position may lie past the sequence
+            // end and hold anything (NaN included; sub-tile 2h + 1 may lie
+            // wholly past it): zero them so 0 * slot stays 0.
+            if (last - tok1 + 1 < kSub) v_tail_mask(va, last - tok0 + 1 - 4 * grp, last - tok1 + 1 - 4 * grp);
+          }
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              acc[t][x] = MP::mma_32(va[x], bh[t][h], acc[t][x]);
+              if constexpr (kSplit) acc[t][x] = MP::mma_32(va[x], bl[t][h], acc[t][x]);
+            }
           }
         }
       }
-    }
-    // step j + 1 to the other buffer (last read before the previous
-    // barrier), then step j + 2 starts loading: it has one step of compute
-    // to arrive
-    if (j + 1 < nstep) stage_store((j + 1) & 1);
-    gload(j + 2);
+      // step j + 1 to the other buffer (last read before the previous
+      // barrier), then step j + 2 starts loading: it has one step of compute
+      // to arrive
+      if (j + 1 < nstep) stage_store((j + 1) & 1);
+      gload(j + 2);
+      __syncthreads();
+    };
+
+    if (kMode == kPvConv && threadIdx.x == 0) v_overflow = 0;
+    gtab(0);
+    gload(0);
+    stage_store(0);
+    gload(1);
     __syncthreads();
+    // The first step crossing the wave's first row (0 for a wave without
+    // rows: every step then only stages and waits).
+    const int jd = last < 0 ? 0 : min(nstep, (L - n + ct0 * R + 1) / kStep);
+    int j = 0;
+    for (; j < jd; ++j) step(j, std::false_type{});
+    for (; j < nstep; ++j) step(j, std::true_type{});
+    if constexpr (kMode != kPvConv) {
+      return false;
+    } else {
+      // every thread is past its last stage read (the step's barrier)
+      if (vmax >= kPvConvLimit) v_overflow = 1;
+      __syncthreads();
+      return v_overflow != 0;
+    }
   };
-  // The first step crossing the wave's first row (0 for a wave without
-  // rows: every step then only stages and waits).
-  const int jd = last < 0 ? 0 : min(nstep, (L - n + ct0 * R + 1) / kStep);
-  int j = 0;
-  for (; j < jd; ++j) step(j, std::false_type{});
-  for (; j < nstep; ++j) step(j, std::true_type{});
+  if constexpr (T::kCode == BF16::kCode) {
+    if (run(std::integral_constant<int, kPvConv>{})) run(std::integral_constant<int, kPvSplit>{});
+  } else {
+    run(std::integral_constant<int, kPvF16>{});
+  }
   if (last < 0) return;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {

@@ -115,6 +115,38 @@ def test_prefill_f16_whole_prompt_every_row(O):
     assert err <= TOL["f16"]
 
 
+def test_prefill_bf16_values_beyond_fp16_rerun_with_split_probabilities(O):
+    """bf16 inputs stage V as fp16 (exact below 2^16 in magnitude) and take
+    P rounded to fp16; a workgroup that stages a V value fp16 cannot hold
+    reruns with V in bf16 and P as hi + lo.  One token of sequence 1 on KV
+    head 0 gets V = 2^17 in every dim: the row blocks of that sequence and
+    head that reach it rerun (their rows attend a value 2^17, so their
+    bound grows with |out|: the hi + lo probabilities keep ~16 bits), every
+    other workgroup stays on the fp16 path at the usual bar."""
+    lens = [300, 1000, 700]
+    w = workload.build(name="prefill-bigv", dtype="bf16", seq_lens=lens, num_q_heads=8,
+                       num_kv_heads=2, head_dim=128, block_size=16, seed=31)
+    tok = 600
+    blk = int(w.block_tables[1, tok // 16])
+    big = np.float32(2.0 ** 17)
+    # V pool [NB][Hkv][B/16][D][16] holds bf16 bits: the upper half of the fp32 bits
+    w.v_pool[blk, 0, 0, :, tok % 16] = np.uint16(big.view(np.uint32) >> 16)
+    q, qs = workload.prefill_queries(w, lens, seed=32)
+    ref = _oracle(O, w, q, qs)
+    got = _run(w, q, qs).double().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - ref)
+    # rows of sequence 1 at positions >= tok on the query heads of KV head 0
+    G = w.group
+    hit = np.zeros(err.shape, bool)
+    hit[qs[1] + tok: qs[2], :G, :] = True
+    _log(f"[prefill] big V: max |ref| {np.abs(ref[hit]).max():.3e}, "
+         f"err there {err[hit].max():.3e}, elsewhere {err[~hit].max():.3e}")
+    assert np.abs(ref[hit]).max() > 1e3  # the big value dominates some rows
+    assert np.all(err[hit] <= 2e-3 + 1e-4 * np.abs(ref[hit]))
+    assert err[~hit].max() <= TOL["bf16"]
+
+
 def test_prefill_gqa_prompt_batch_full_size(O):
     """The benchmarked prefill workload (8 whole prompts of 2048 tokens, GQA
     32/8, bf16, B = 16), output buffer filled with NaN first: every element
