@@ -31,7 +31,8 @@
 // (operand layouts as in the decode engine), with a running max and sum per
 // column.  Workgroups run longest rows first across the batch, and the
 // blocks of one (sequence, KV head) go to one XCD (workgroup i runs on XCD
-// i mod 8), so they share its L2.
+// i mod 8), so they share its L2.  Finished tiles leave through LDS as
+// whole 16-byte chunks (prefill_store_tiles).
 #pragma once
 
 #include "decode_mfma.h"
@@ -116,6 +117,56 @@ __device__ __forceinline__ void split_pair_bf16(float p0, float p1, uint32_t& hi
   lo = __builtin_bit_cast(uint32_t, r);
 }
 
+// A wave's finished column tiles to out, through LDS: the scattered
+// per-lane elements (4 consecutive dims of one column per 16-byte chunk)
+// are written to the wave's LDS region `buf` as [column][dim] rows, then
+// read back as 16-byte chunks in output order, so every global store is a
+// whole 16-byte chunk and consecutive lanes write consecutive chunks (the
+// G heads of a row are contiguous).  buf: kPrefillOutBytes bytes, 16-byte
+// aligned, private to the wave; every wave of the workgroup calls this
+// (it holds workgroup barriers).  inv[t] = 1 / l of the lane's column.
+constexpr int kPrefillOutRow = kD * 4 + 16;  // fp32 row, padded: rows 4 banks apart
+constexpr int kPrefillOutBytes = kSub * kPrefillOutRow;
+
+template <class T, int G, int NT>
+__device__ __forceinline__ void prefill_store_tiles(const PrefillArgs& a, unsigned char* buf,
+                                                    const f32x4 (&acc)[NT][8], const float (&inv)[NT],
+                                                    int ct0, int n, int q0, int kvh) {
+  constexpr int R = kSub / G;
+  const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+  const int esz = a.out_f32 ? 4 : 2;
+  const int row_bytes = kD * esz;              // one column's output
+  const int stride = row_bytes + 16;           // its padded LDS row
+  const int cpc = row_bytes / 16;              // 16-byte chunks per column
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const f32x4 v = acc[t][x] * inv[t];
+      unsigned char* dst = buf + col * stride + (16 * x + 4 * grp) * esz;
+      if (a.out_f32) {
+        *reinterpret_cast<f32x4*>(dst) = v;
+      } else {
+        typedef typename std::conditional<T::kCode == BF16::kCode, __bf16, _Float16>::type E;
+        typedef E e4 __attribute__((ext_vector_type(4)));
+        const e4 h = {(E)v[0], (E)v[1], (E)v[2], (E)v[3]};
+        *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, h);
+      }
+    }
+    __syncthreads();
+    for (int id = lane; id < kSub * cpc; id += 64) {
+      const int c = id / cpc, k = id % cpc;
+      const int r = (ct0 + t) * R + c / G;
+      if (r < n) {
+        const uint4 v = *reinterpret_cast<const uint4*>(buf + c * stride + k * 16);
+        const int64_t o = ((int64_t)(q0 + r) * a.Hq + kvh * G + c % G) * row_bytes + k * 16;
+        *reinterpret_cast<uint4*>(static_cast<char*>(a.out) + o) = v;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // Rows of one workgroup's block for group size G.
 template <int G>
 constexpr int prefill_rows_per_block() {
@@ -125,8 +176,8 @@ constexpr int prefill_rows_per_block() {
 // Grid: 8 * ceil(S * Hkv / 8) * tiles workgroups of kPrefillThreads, `tiles` the
 // row blocks of the longest query set.  Workgroup i runs on XCD x = i % 8
 // and takes the (sequence, KV head) pairs x, x + 8, ... (pair = b * Hkv +
-// kvh) with its row block slowest and reversed, so each XCD works the
-// longest rows of its pairs first.
+// kvh) in two halves, within a half with its row block slowest and
+// reversed, so each XCD works the longest rows of half its pairs first.
 //
 // The keys go by steps of kPrefillStepSub sub-tiles (64 tokens): the step's
 // scores of every column tile first (independent 4-deep products per
@@ -154,8 +205,13 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   const int xcd = blockIdx.x % 8, k = blockIdx.x / 8;
   const int px = (P - xcd + 7) / 8;  // pairs of this XCD
   if (k >= px * a.tiles) return;
-  const int rb = a.tiles - 1 - k / px;  // longest rows first
-  const int pair = xcd + 8 * (k % px);
+  // The XCD's pairs in two halves, each with its row blocks longest
+  // first: the K/V its workgroups stream at a time is half as large, so
+  // more of it stays in the XCD's L2.
+  const int hp = (px + 1) / 2, h1 = k >= hp * a.tiles ? 1 : 0;
+  const int kk = h1 ? k - hp * a.tiles : k, pn = h1 ? px - hp : hp;
+  const int rb = a.tiles - 1 - kk / pn;
+  const int pair = xcd + 8 * (h1 * hp + kk % pn);
   const int b = pair / a.Hkv, kvh = pair % a.Hkv;
   const int q0 = as_constant(a.qs)[b];
   const int n = as_constant(a.qs)[b + 1] - q0;
@@ -182,6 +238,17 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     for (int x = 0; x < 4; ++x) qop[t][x] = live ? qsrc[4 * x] : make_uint4(0, 0, 0, 0);
   }
 
+  // Scores are scaled by c2 = |scale log2 e|; a negative scale flips the
+  // query's sign bits instead (the products then come out negated exactly).
+  const float c2 = fabsf(a.scale_log2);
+  if (a.scale_log2 < 0.f) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        qop[t][x].x ^= 0x80008000u; qop[t][x].y ^= 0x80008000u; qop[t][x].z ^= 0x80008000u; qop[t][x].w ^= 0x80008000u;
+      }
+  }
   f32x4 acc[NT][8];
   float m[NT], lsum[NT];
 
@@ -295,8 +362,13 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
             for (int x = 1; x < 4; ++x) s[t][u] = M::mma_qk(kr[x], qop[t][x], s[t][u]);
           }
         }
-        // Scores in base-2 units, x = s * scale * log2 e; p = 2^(x - m),
-        // exactly 1 where x is the max.
+        // Scores in base-2 units, x = s * c2; p = 2^(x - m).  Steps without
+        // the mask keep the raw scores: the max is taken on them and scaled
+        // once (c2 > 0, and rounding is monotonic, so this is the max of the
+        // scaled scores), and each exponent is one fused s * c2 - m, which
+        // leaves the largest p within 2^-24 |m| of 1 (1 exactly once rounded
+        // to fp16 while |m| < 2^12).  Masked steps and the hi + lo mode scale
+        // first, as the mask and the split need.
         float xr[NT][KB][4], bm[NT];
         bool up = false;
 #pragma unroll
@@ -304,7 +376,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
 #pragma unroll
           for (int u = 0; u < KB; ++u)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) xr[t][u][r] = s[t][u][r] * a.scale_log2;
+            for (int r = 0; r < 4; ++r) xr[t][u][r] = (kMasked || kSplit) ? s[t][u][r] * c2 : s[t][u][r];
           if constexpr (kMasked) {
             const int d = pos[t] - ts - 4 * grp;  // token ts + 4 grp + i is masked when i > d
 #pragma unroll
@@ -320,6 +392,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
             for (int r = 0; r < 4; ++r) bm[t] = fmaxf(bm[t], xr[t][u][r]);
           bm[t] = max_xor16(bm[t]);
           bm[t] = max_xor32(bm[t]);
+          if constexpr (!kMasked && !kSplit) bm[t] *= c2;
           up = up || bm[t] > m[t] + kPrefillSlack;
         }
         // Lazy rescaling: the reference max moves only when some column's
@@ -352,8 +425,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
           for (int u = 0; u < KB; ++u)
 #pragma unroll
             for (int r = 0; r < 4; r += 2) {
-              const float p0 = fast_exp2(xr[t][u][r] - m[t]);
-              const float p1 = fast_exp2(xr[t][u][r + 1] - m[t]);
+              const float p0 = (kMasked || kSplit) ? fast_exp2(xr[t][u][r] - m[t]) : fast_exp2(fmaf(xr[t][u][r], c2, -m[t]));
+              const float p1 = (kMasked || kSplit) ? fast_exp2(xr[t][u][r + 1] - m[t]) : fast_exp2(fmaf(xr[t][u][r + 1], c2, -m[t]));
               if constexpr (kSplit) {
                 ps += p0 + p1;
                 split_pair_bf16(p0, p1, hw[u][r / 2], lw[u][r / 2]);
@@ -436,21 +509,17 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   } else {
     run(std::integral_constant<int, kPvF16>{});
   }
-  if (last < 0) return;
+  // Every wave is past its last stage read (the last step's barrier): the
+  // stage now holds each wave's output tiles on their way out.  Waves
+  // without rows take part in the barriers and store nothing.
+  float inv[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    float l = sum_xor16(lsum[t]);
-    l = sum_xor32(l);
-    if (row[t] < n) {
-      const float inv = 1.f / l;
-      const int64_t base = ((int64_t)(q0 + row[t]) * a.Hq + head) * kD + 4 * grp;
-#pragma unroll
-      for (int x = 0; x < 8; ++x)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          store_out<T>(a.out, base + 16 * x + r, acc[t][x][r] * inv, a.out_f32);
-    }
+    const float l = sum_xor32(sum_xor16(lsum[t]));
+    inv[t] = last < 0 ? 0.f : 1.f / l;
   }
+  static_assert(kPrefillWaves * kPrefillOutBytes <= sizeof(stage), "output tiles fit the stage");
+  prefill_store_tiles<T, G, NT>(a, &stage[0][0][0] + wave * kPrefillOutBytes, acc, inv, ct0, n, q0, kvh);
 }
 
 }  // namespace pa
