@@ -32,19 +32,20 @@ def O():
     return oracle.load()
 
 
-def _run(w, q, qs, out_dtype=torch.float32, kernel=pa.PA_KERNEL_AUTO):
+def _run(w, q, qs, out_dtype=torch.float32, kernel=pa.PA_KERNEL_AUTO, scale=None):
     qd = device_tensor(q, w.dtype)
     out = pa.prefill(qd, device_tensor(w.k_pool, w.dtype), device_tensor(w.v_pool, w.dtype),
                      torch.from_numpy(w.block_tables).cuda(), torch.from_numpy(w.seq_lens).cuda(),
-                     torch.from_numpy(qs).cuda(), float(w.scale), out_dtype=out_dtype, kernel=kernel)
+                     torch.from_numpy(qs).cuda(), float(w.scale if scale is None else scale),
+                     out_dtype=out_dtype, kernel=kernel)
     torch.cuda.synchronize()
     return out
 
 
-def _oracle(O, w, q, qs):
+def _oracle(O, w, q, qs, scale=None):
     return O.paged_prefill(q, w.k_pool, w.v_pool, w.block_tables, w.seq_lens, qs,
-                           np.float64(np.float32(w.scale)), num_kv_heads=w.num_kv_heads,
-                           block_size=w.block_size, dtype=w.dtype)
+                           np.float64(np.float32(w.scale if scale is None else scale)),
+                           num_kv_heads=w.num_kv_heads, block_size=w.block_size, dtype=w.dtype)
 
 
 LENS = [1, 2, 15, 16, 17, 33, 64, 65, 129, 300, 511]
@@ -71,6 +72,23 @@ def test_prefill_ragged(O, dtype, B, G):
     err = max_err(_run(w, q, qs), ref)
     _log(f"[prefill] {dtype} B={B} G={G} max_abs_err={err:.3e}")
     assert err <= TOL[dtype], (dtype, B, G, err)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("scale", [-1.0 / np.sqrt(128.0), 0.0, 0.7])
+def test_prefill_scale_sign_and_zero(O, dtype, scale):
+    """Any scale: steps without the mask take the max on the raw scores and
+    scale it once, which needs a positive factor, so a negative scale runs
+    with the query's sign bits flipped (the products come out negated
+    exactly) and a zero scale gives uniform weights."""
+    lens = [130, 700, 64]
+    w = workload.build(name="prefill-scale", dtype=dtype, seq_lens=lens, num_q_heads=8,
+                       num_kv_heads=2, head_dim=128, block_size=16, seed=41)
+    q, qs = workload.prefill_queries(w, [130, 300, 64], seed=42)
+    ref = _oracle(O, w, q, qs, scale=scale)
+    err = max_err(_run(w, q, qs, scale=scale), ref)
+    _log(f"[prefill] {dtype} scale={scale:.4f} max_abs_err={err:.3e}")
+    assert err <= TOL[dtype], (dtype, scale, err)
 
 
 def test_prefill_output_in_input_type_and_forced_kernel(O):
