@@ -226,8 +226,9 @@ constexpr int kItemTiles = 2;
 // KV head kvh, all its members' query heads as up to kWideCols MFMA
 // columns (two 16-column tiles when they need more than 16).  Each wave
 // owns one column tile: with two tiles, waves 0-3 hold tile 0 and waves 4-7
-// tile 1, and the two halves walk the same 16-token sub-tiles in step (the
-// second read of a sub-tile is served by the cache, so HBM sees it once);
+// tile 1, and the two halves walk the same 16-token sub-tiles, kept within
+// two passes of each other by barriers (the second read of a sub-tile is
+// served by L2, so HBM sees it once);
 // with one tile all eight waves share the sub-tiles.  kItemTiles sub-tiles
 // are in flight per wave, and the wave partials of all columns merge in
 // LDS in one pass.  A whole item's member parts go to the
@@ -353,8 +354,16 @@ __device__ inline void item_piece(const Args& a, Smem& sm, const SharedInfo& si,
   };
   // every pass refills each tile register after its compute (an empty
   // load past the end), so the loads in flight are always in the order
-  // they are consumed
-  while (t < nsub) {
+  // they are consumed.  With two column tiles, waves w and w + 4 read the
+  // same sub-tiles: every wave runs the same number of passes and a
+  // barrier ends every second one (the merge below has its own), so the
+  // two reads of a sub-tile are issued within two passes of each other and
+  // the second finds it in L2.  Unsynchronised, about half of the shared
+  // bytes were fetched from HBM twice (34 MB per call on the serving
+  // batch); a barrier every pass removes all of it but costs more time
+  // than it saves.
+  const int passes = (nsub + kItemTiles * wpt - 1) / (kItemTiles * wpt);
+  for (int pass = 0; pass < passes; ++pass) {
 #pragma unroll
     for (int k = 0; k < kItemTiles; ++k) {
       const int tk = t + k * wpt;
@@ -362,6 +371,7 @@ __device__ inline void item_piece(const Args& a, Smem& sm, const SharedInfo& si,
       load(tk + kItemTiles * wpt, tl[k]);
     }
     t += kItemTiles * wpt;
+    if (nct == 2 && (pass & 1) && pass + 1 < passes) __syncthreads();
   }
 
   // wave partials -> LDS (wave w holds column tile w / wpt), then every
