@@ -1260,13 +1260,43 @@ __device__ inline void stream_batch(const Args& a, typename Engine::Smem& sm) {
   State st;
   Engine::reset(st);
   Query q;
-  // Finish pieces cur .. p-1 and start piece p (p <= npl).  The late
+  // Column groups (64 heads) read the same sub-tiles, each group dealing
+  // them over its own waves.  Left to drift, the second read of a sub-tile
+  // mostly missed L2 (FETCH_SIZE 1.9 x the K/V bytes; 1.02 x with these
+  // barriers), so the groups meet at a workgroup barrier at every
+  // kSyncSub-th position of the stream
+  // (positions number the batch's sub-tiles through its pieces, as dealt).
+  // A wave takes the barrier at position X before computing its first
+  // sub-tile at or past X, and the finish of piece p (its own barriers) at
+  // the position where piece p + 1 starts, ties going to the finish: every
+  // wave meets the same barriers in the same order, only at different
+  // sub-tiles of its own.
+  constexpr bool kSync = kColGroups<G> > 1;
+  constexpr int kSyncSub = 8 * kColWaves<G>;  // four passes of the group (2, 4, 8 measured 344, 333, 328 us, 16 335)
+  int cur_end = 0;                            // stream position where piece cur + 1 starts
+  int next_sync = kSyncSub;                   // position of the next barrier
+  int total = 0;                              // the batch's stream length
+  if constexpr (kSync) {
+    cur_end = uniform(sm.plist[0].nsub);
+    for (int p = 0; p < npl; ++p) total += uniform(sm.plist[p].nsub);
+  }
+  // Finish pieces cur .. p-1 and start piece p (p <= npl), taking the
+  // barriers up to position pos on the way (column groups).  The late
   // piece is the last of the chunk, so it is only ever finished after the
-  // streaming loop (enter(npl, true)); only there is its arrival count
-  // read, which keeps that load and its wait out of the loop.
-  auto enter = [&](int p, bool last) {
-    if (cur >= p) return;
-    do {
+  // streaming loop (enter(npl, total - 1, true)); only there is its arrival
+  // count read, which keeps that load and its wait out of the loop.
+  auto enter = [&](int p, int pos, bool last) {
+    const int cur0 = cur;
+    while (true) {
+      const bool fin = cur < p;
+      if constexpr (kSync) {
+        if (next_sync <= pos && (!fin || next_sync < cur_end)) {
+          __syncthreads();
+          next_sync += kSyncSub;
+          continue;
+        }
+      }
+      if (!fin) break;
       const Piece pc = uniform_piece(sm.plist[cur]);
       const int seen = last ? split_seen(a, pc) : -1;
       if constexpr (kTilesPerWave<G> > 1) {
@@ -1278,8 +1308,12 @@ __device__ inline void stream_batch(const Args& a, typename Engine::Smem& sm) {
         finish_piece<T, G>(a, sm, pc);
       }
       Engine::reset(st);
-    } while (++cur < p);
-    if (p < npl) Engine::load_query(sm, p, q);
+      ++cur;
+      if constexpr (kSync) {
+        if (cur < npl) cur_end += uniform(sm.plist[cur].nsub);
+      }
+    }
+    if (cur != cur0 && p < npl) Engine::load_query(sm, p, q);
   };
 
   if (c.p < npl) {
@@ -1311,6 +1345,8 @@ __device__ inline void stream_batch(const Args& a, typename Engine::Smem& sm) {
     // trips instead of three.
     const Cur c0 = c;
     int p0 = c.p, v0 = c.te - (c.tb + kSub * c.j);
+    int s0 = wave % kStride, s1 = s0 + kStride;  // stream positions of t0, t1
+    int snext = s1 + kStride;                    // of the next refill
     advance(c);
     if (c.p < npl) last = c;
     const Cur c1 = last;
@@ -1328,9 +1364,11 @@ __device__ inline void stream_batch(const Args& a, typename Engine::Smem& sm) {
     Engine::load_query(sm, 0, q);
     // Load the stream's next sub-tile into t and return its (piece, valid
     // tokens).
-    auto refill = [&](Tile& t, int& pn, int& vn) {
+    auto refill = [&](Tile& t, int& pn, int& vn, int& sn) {
       pn = c.p;
       vn = c.te - (c.tb + kSub * c.j);
+      sn = snext;
+      snext += kStride;
       load(last, ph, c.p < npl, t);
       advance(c);
       if (c.p < npl) last = c;
@@ -1341,29 +1379,32 @@ __device__ inline void stream_batch(const Args& a, typename Engine::Smem& sm) {
     // always t0's followed by t1's and the compiler's wait before each
     // compute covers exactly that tile.  The loop leaves only at the
     // bottom.
-    enter(p0, false);
+    enter(p0, s0, false);
     while (true) {
-      int n0, w0, n1, w1;
+      int n0, w0, n1, w1, m0, m1;
       Engine::compute(a, sm, q, st, t0, v0);
-      refill(t0, n0, w0);
+      refill(t0, n0, w0, m0);
       const bool more = p1 < npl;
       if (more) {
-        enter(p1, false);
+        enter(p1, s1, false);
         Engine::compute(a, sm, q, st, t1, v1);
       }
-      refill(t1, n1, w1);
+      refill(t1, n1, w1, m1);
       p0 = n0;
       v0 = w0;
+      s0 = m0;
       p1 = n1;
       v1 = w1;
+      s1 = m1;
       if (!more || p0 >= npl) break;
-      enter(p0, false);
+      enter(p0, s0, false);
     }
   } else {
     stage_queries<T, G>(a, sm, npl);
     __syncthreads();  // query groups staged
   }
-  enter(npl, true);
+  // the rest of the batch's pieces and barriers (those before its end)
+  enter(npl, total - 1, true);
 }
 
 // Lists the chunk's next batch of pieces (flat range [sm.next_f, e)) in
