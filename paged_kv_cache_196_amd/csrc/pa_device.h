@@ -347,7 +347,8 @@ constexpr int kFoldLoads = 64;  // workspace loads per thread in flight when fol
 // column tiles of 16 heads (32 heads), and the waves form G / 32 column
 // groups of kColWaves waves; a group takes its 32 heads and deals the
 // sub-tiles among its own waves.  Two groups (64 heads) read the same
-// sub-tiles at about the same time, so each is fetched from HBM once.
+// sub-tiles, kept within a few passes of each other by barriers in the
+// stream (stream_batch), so each is fetched from HBM once.
 // Merging goes through the 16-column wave arrays one column tile (round)
 // at a time.
 template <int G>
@@ -1264,15 +1265,16 @@ __device__ inline void stream_batch(const Args& a, typename Engine::Smem& sm) {
   // them over its own waves.  Left to drift, the second read of a sub-tile
   // mostly missed L2 (FETCH_SIZE 1.9 x the K/V bytes; 1.02 x with these
   // barriers), so the groups meet at a workgroup barrier at every
-  // kSyncSub-th position of the stream
-  // (positions number the batch's sub-tiles through its pieces, as dealt).
+  // kSyncSub-th position of the stream (positions number the batch's
+  // sub-tiles through its pieces, as dealt; a barrier every 1, 2, 4, 8
+  // passes measured 344, 333, 328 and 335 us on the 64-head batch).
   // A wave takes the barrier at position X before computing its first
   // sub-tile at or past X, and the finish of piece p (its own barriers) at
   // the position where piece p + 1 starts, ties going to the finish: every
   // wave meets the same barriers in the same order, only at different
   // sub-tiles of its own.
   constexpr bool kSync = kColGroups<G> > 1;
-  constexpr int kSyncSub = 8 * kColWaves<G>;  // four passes of the group (2, 4, 8 measured 344, 333, 328 us, 16 335)
+  constexpr int kSyncSub = 8 * kColWaves<G>;  // four passes of the group
   int cur_end = 0;                            // stream position where piece cur + 1 starts
   int next_sync = kSyncSub;                   // position of the next barrier
   int total = 0;                              // the batch's stream length
