@@ -123,6 +123,15 @@ def _mean_counter(rows, counter: str, name_part: str) -> float:
     return sum(vals) / len(vals)
 
 
+def make_workload(wid: str, seed=None):
+    """A workload by its bench name: a config number ("1".."5") or the
+    multi-query batch ("mqa32", "mqa64")."""
+    import workload as wl
+    if wid.startswith("mqa"):
+        return wl.make_mqa(int(wid[3:]), seed)
+    return wl.make(int(wid), seed)
+
+
 def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, workload_id, kernel,
                        shared: bool):
     """Turns four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE, each on
@@ -130,7 +139,7 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, wor
     launch, scaled by the copy's known bytes, and stores the entry for this
     (kernel, workload) in TRAFFIC_FILE."""
     import workload as wl
-    w = wl.make(workload_id)
+    w = make_workload(workload_id)
     kname = decode_kernel_name(w, kernel, shared)
     part = "decode_shared_kernel" if kname.startswith("decode_shared") else "decode_kernel"
     kib = 1024.0
@@ -719,7 +728,9 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", default="5", choices=["1", "2", "3", "4", "5", "mqa32", "mqa64"],
+                    help="the timed workload: a config number, or mqa32 / mqa64 (the multi-query "
+                         "batch; used for its counter runs)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--kernel", choices=["auto", "valu", "mfma"], default="auto")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
@@ -783,7 +794,7 @@ def main() -> int:
         import oracle
         O = oracle.load()
     shared = not args.no_prefix_groups
-    w = workload.make(args.workload, args.seed)
+    w = make_workload(args.workload, args.seed)
     head = decode_leg(w, args, dev, flush, stream, O, shared, args.steps, args.warmup)
     probe = None if args.no_read_probe else read_probe(flush, dev)
 
@@ -836,7 +847,7 @@ def main() -> int:
     for wid in others:
         if wid == str(args.workload):
             continue
-        wo = workload.make_mqa(int(wid[3:])) if wid.startswith("mqa") else workload.make(int(wid))
+        wo = make_workload(wid)
         leg = decode_leg(wo, args, dev, flush, stream, O, shared, args.steps, args.warmup)
         subs[wid] = {k: leg[k] for k in (
             "workload", "dtype", "ms_per_step", "kv_gbps", "hbm_frac", "tokens_per_s", "kv_bytes",
