@@ -106,6 +106,27 @@ def test_mqa_full_size(O, Hq):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("seed", [0, 1])
+def test_mqa64_many_short_pieces_between_group_barriers(O, seed):
+    """64 heads on one KV head: the two column groups meet at barriers every
+    few passes of the sub-tile stream, ordered with the piece finishes by
+    stream position.  Many short sequences (1-60 tokens, some empty) put
+    many piece finishes between and on those barriers, and a few long ones
+    put many barriers inside one piece, in batches of several sizes; every
+    output against the oracle."""
+    rng = np.random.default_rng(6400 + seed)
+    lens = rng.integers(0, 61, size=700)
+    lens[rng.random(700) < 0.05] = 0
+    lens[rng.choice(700, size=6, replace=False)] = rng.integers(2000, 6000, size=6)
+    w = workload.build(name=f"mqa64-short-{seed}", dtype="bf16", seq_lens=lens, num_q_heads=64,
+                       num_kv_heads=1, head_dim=128, block_size=16, seed=71 + seed)
+    _log(f"[parity] {w.name}: {w.num_seqs} sequences")
+    ref = O.run_workload(w)
+    err = max_err(Uploaded(w).run("mfma"), ref)
+    _log(f"[parity] {w.name} max_abs_err={err:.3e}")
+    assert err <= TOL["bf16"], err
+
+
 def test_single_sequence_single_token(O):
     w = workload.build(name="one", dtype="bf16", seq_lens=[1], num_q_heads=4, num_kv_heads=1,
                        head_dim=128, block_size=16, seed=5)
