@@ -183,15 +183,16 @@ __device__ inline void shared_prologue(const Args& a, Smem& sm, int* wsum) {
 #pragma unroll
       for (int k = 0; k < kMmax; ++k) {
         const int b = f + k;
-        if (b >= e) break;
-        const int lim = min(Ls[k], shtok);
-        if (Ls[k] > 0) {
-          l.shb[b] = blocks_of(lim, B);
-          l.seq_sg[b] = s;
-        }
-        if (lim > lmax) {
-          lmax = lim;
-          ref = b;
+        if (b < e) {  // a guard rather than a break, so the loop unrolls
+          const int lim = min(Ls[k], shtok);
+          if (Ls[k] > 0) {
+            l.shb[b] = blocks_of(lim, B);
+            l.seq_sg[b] = s;
+          }
+          if (lim > lmax) {
+            lmax = lim;
+            ref = b;
+          }
         }
       }
       l.sg_first[s] = f;
